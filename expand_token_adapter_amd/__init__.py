@@ -1,0 +1,246 @@
+"""Multi-LoRA batched adapter kernels for AMD MI355X (gfx950).
+
+Python binding of the C ABI (include/lora_batch.h).  Each function has the
+name of the C entry point it calls, takes torch tensors that live on the GPU,
+and only marshals pointers, sizes and the current HIP stream: every step of
+the computation runs in the HIP kernels of liblora_batch.so.  PyTorch supplies
+device memory and streams.
+
+    seg = lora_segments_build(ids, num_adapters)         # group rows by adapter
+    v = lora_shrink(x, table, seg)                       # v = A_a x    (fp32)
+    lora_expand_add(v, table, seg, y)                    # y += s_a B_a v
+    lora_backward(x_ft, dy, table, grads, seg_ft, dx)    # dX, dA, dB  (+=)
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence
+
+import torch
+
+from . import _abi
+from ._abi import LORA_BF16, LORA_F32, LORA_MAX_RANK, LoraError
+
+__all__ = [
+    "AdapterTable", "GradTable", "Segments", "LoraError",
+    "lora_segments_build", "lora_shrink", "lora_expand_add", "lora_backward",
+    "lora_abi_version", "lora_status_string",
+    "lora_segments_workspace_bytes", "lora_backward_workspace_bytes", "lora_segments_sched_elems",
+]
+
+_DTYPES = {torch.bfloat16: LORA_BF16, torch.float32: LORA_F32}
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DTYPES:
+        raise TypeError(f"element type must be bfloat16 or float32, got {t.dtype}")
+    return _DTYPES[t.dtype]
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _on_gpu(*ts: Optional[torch.Tensor]) -> None:
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+
+
+def _rows(t: torch.Tensor, name: str):
+    """(pointer, rows, cols, pitch) of a 2-D tensor whose rows are contiguous."""
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D with contiguous rows")
+    return t.data_ptr(), t.shape[0], t.shape[1], t.stride(0)
+
+
+def lora_abi_version() -> int:
+    return _abi.load().lora_abi_version()
+
+
+def lora_status_string(status: int) -> str:
+    return _abi.status_string(status)
+
+
+def lora_segments_workspace_bytes(T: int, num_adapters: int) -> int:
+    return _abi.load().lora_segments_workspace_bytes(T, num_adapters)
+
+
+def lora_backward_workspace_bytes(T_ft: int, r_max: int) -> int:
+    return _abi.load().lora_backward_workspace_bytes(T_ft, r_max)
+
+
+def lora_segments_sched_elems(T: int, num_adapters: int) -> int:
+    return _abi.load().lora_segments_sched_elems(T, num_adapters)
+
+
+class AdapterTable:
+    """Device-resident table of adapters (lora_adapter structs).
+
+    A[a]: [r_a, d_in] and B[a]: [d_out, r_a] tensors on the GPU (kept alive
+    by this object); scales[a] multiplies adapter a's delta.
+    """
+
+    def __init__(self, A: Sequence[torch.Tensor], B: Sequence[torch.Tensor], scales: Sequence[float]):
+        if not (len(A) == len(B) == len(scales)) or len(A) == 0:
+            raise ValueError("A, B and scales must have the same nonzero length")
+        self.A = list(A)
+        self.B = list(B)
+        self.scales = [float(s) for s in scales]
+        self.dtype = self.A[0].dtype
+        self.device = self.A[0].device
+        _on_gpu(*self.A, *self.B)
+        ranks = []
+        host = (_abi.LoraAdapter * len(A))()
+        for i, (a, b, s) in enumerate(zip(self.A, self.B, self.scales)):
+            if a.dtype != self.dtype or b.dtype != self.dtype or not a.is_contiguous() or not b.is_contiguous():
+                raise ValueError("adapter weights must share one dtype and be contiguous")
+            if a.dim() != 2 or b.dim() != 2 or b.shape[1] != a.shape[0]:
+                raise ValueError("A must be [r, d_in] and B [d_out, r]")
+            host[i] = _abi.LoraAdapter(a.data_ptr(), b.data_ptr(), a.shape[0], s)
+            ranks.append(int(a.shape[0]))
+        self.ranks = ranks
+        self.r_max = max(ranks)
+        self.d_in = int(self.A[0].shape[1])
+        self.d_out = int(self.B[0].shape[0])
+        raw = bytes(host)
+        self.table = torch.frombuffer(bytearray(raw), dtype=torch.uint8).to(self.device)
+
+    def __len__(self) -> int:
+        return len(self.A)
+
+    @property
+    def ptr(self) -> int:
+        return self.table.data_ptr()
+
+
+class GradTable:
+    """Device-resident table of fp32 gradient targets (lora_adapter_grad structs).
+
+    dA[a]: [r_a, d_in], dB[a]: [d_out, r_a] float32 GPU tensors, or None for
+    adapters that are not trained.
+    """
+
+    def __init__(self, dA: Sequence[Optional[torch.Tensor]], dB: Sequence[Optional[torch.Tensor]]):
+        if len(dA) != len(dB) or len(dA) == 0:
+            raise ValueError("dA and dB must have the same nonzero length")
+        self.dA = list(dA)
+        self.dB = list(dB)
+        host = (_abi.LoraAdapterGrad * len(dA))()
+        device = None
+        for i, (ga, gb) in enumerate(zip(self.dA, self.dB)):
+            if (ga is None) != (gb is None):
+                raise ValueError("dA and dB must both be given or both be None")
+            if ga is None:
+                continue
+            _on_gpu(ga, gb)
+            if ga.dtype != torch.float32 or gb.dtype != torch.float32:
+                raise TypeError("gradients are float32")
+            if not ga.is_contiguous() or not gb.is_contiguous():
+                raise ValueError("gradients must be contiguous")
+            device = ga.device
+            host[i] = _abi.LoraAdapterGrad(ga.data_ptr(), gb.data_ptr())
+        if device is None:
+            raise ValueError("at least one adapter needs gradient buffers")
+        self.table = torch.frombuffer(bytearray(bytes(host)), dtype=torch.uint8).to(device)
+
+    @property
+    def ptr(self) -> int:
+        return self.table.data_ptr()
+
+
+class Segments:
+    """Output of lora_segments_build: rows grouped by adapter (device tensors)."""
+
+    def __init__(self, T: int, num_adapters: int, device: torch.device):
+        lib = _abi.load()
+        self.T = T
+        self.num_adapters = num_adapters
+        i32 = dict(dtype=torch.int32, device=device)
+        self.counts = torch.zeros(num_adapters, **i32)
+        self.offsets = torch.zeros(num_adapters + 1, **i32)
+        self.perm = torch.zeros(max(T, 1), **i32)
+        self.err = torch.zeros(1, **i32)
+        self.sched = torch.zeros(max(1, lib.lora_segments_sched_elems(T, num_adapters)), **i32)
+        self.ws = torch.empty(max(1, lib.lora_segments_workspace_bytes(T, num_adapters)), dtype=torch.uint8,
+                              device=device)
+
+    @property
+    def c(self) -> _abi.LoraSegments:
+        return _abi.LoraSegments(self.counts.data_ptr(), self.offsets.data_ptr(), self.perm.data_ptr(),
+                                 self.err.data_ptr(), self.sched.data_ptr())
+
+
+def lora_segments_build(adapter_ids: torch.Tensor, num_adapters: int, out: Optional[Segments] = None) -> Segments:
+    """Group rows by adapter id (-1 = no adapter).  Returns (or refills) a Segments."""
+    _on_gpu(adapter_ids)
+    if adapter_ids.dtype != torch.int32 or adapter_ids.dim() != 1 or not adapter_ids.is_contiguous():
+        raise ValueError("adapter_ids must be a contiguous 1-D int32 tensor")
+    T = int(adapter_ids.shape[0])
+    seg = out if out is not None else Segments(T, num_adapters, adapter_ids.device)
+    if seg.T != T or seg.num_adapters != num_adapters:
+        raise ValueError("Segments buffers were sized for another batch")
+    st = _abi.load().lora_segments_build(adapter_ids.data_ptr(), T, num_adapters, seg.c, seg.ws.data_ptr(),
+                                         seg.ws.numel(), _stream(adapter_ids.device))
+    _abi.check("lora_segments_build", st)
+    return seg
+
+
+def lora_shrink(x: torch.Tensor, adapters: AdapterTable, seg: Segments, v: Optional[torch.Tensor] = None,
+                r_max: Optional[int] = None) -> torch.Tensor:
+    """v[t, :r_a] = A_a x_t (fp32) for every row with an adapter; returns v [T, r_max]."""
+    _on_gpu(x)
+    px, T, d_in, ldx = _rows(x, "x")
+    r_max = adapters.r_max if r_max is None else r_max
+    if v is None:
+        v = torch.zeros((T, (r_max + 3) // 4 * 4), dtype=torch.float32, device=x.device)
+    pv, _, _, ldv = _rows(v, "v")
+    st = _abi.load().lora_shrink(_dtype_code(x), px, ldx, T, d_in, adapters.ptr, len(adapters), r_max, seg.c,
+                                 pv, ldv, _stream(x.device))
+    _abi.check("lora_shrink", st)
+    return v
+
+
+def lora_expand_add(v: torch.Tensor, adapters: AdapterTable, seg: Segments, y: torch.Tensor,
+                    r_max: Optional[int] = None) -> torch.Tensor:
+    """y[t] += s_a B_a v[t, :r_a] in place; returns y."""
+    _on_gpu(v, y)
+    pv, T, _, ldv = _rows(v, "v")
+    py, Ty, d_out, ldy = _rows(y, "y")
+    if Ty != T:
+        raise ValueError("v and y must have the same number of rows")
+    r_max = adapters.r_max if r_max is None else r_max
+    st = _abi.load().lora_expand_add(_dtype_code(y), pv, ldv, T, d_out, adapters.ptr, len(adapters), r_max,
+                                     seg.c, py, ldy, _stream(y.device))
+    _abi.check("lora_expand_add", st)
+    return y
+
+
+def lora_backward(x: torch.Tensor, dy: torch.Tensor, adapters: AdapterTable, grads: GradTable, seg_ft: Segments,
+                  dx: Optional[torch.Tensor] = None, v_saved: Optional[torch.Tensor] = None,
+                  r_max: Optional[int] = None, ws: Optional[torch.Tensor] = None) -> None:
+    """Accumulate dX (if given), dA and dB of the fine-tuning rows x / dy."""
+    _on_gpu(x, dy, dx, v_saved)
+    px, T, d_in, ldx = _rows(x, "x")
+    pdy, Td, d_out, lddy = _rows(dy, "dy")
+    if Td != T:
+        raise ValueError("x and dy must have the same number of rows")
+    pdx, lddx = 0, 0
+    if dx is not None:
+        pdx, Tx, _, lddx = _rows(dx, "dx")
+        if Tx != T or dx.dtype != x.dtype:
+            raise ValueError("dx must match x")
+    pvs, ldv = 0, 0
+    if v_saved is not None:
+        pvs, _, _, ldv = _rows(v_saved, "v_saved")
+    if len(grads.dA) != len(adapters):
+        raise ValueError("the gradient table must have one entry per adapter")
+    r_max = adapters.r_max if r_max is None else r_max
+    lib = _abi.load()
+    need = lib.lora_backward_workspace_bytes(T, r_max)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    st = lib.lora_backward(_dtype_code(x), px, ldx, pdy, lddy, pdx or None, lddx, T, d_in, d_out, adapters.ptr,
+                           grads.ptr, len(adapters), r_max, seg_ft.c, pvs or None, ldv, ws.data_ptr(), ws.numel(),
+                           _stream(x.device))
+    _abi.check("lora_backward", st)

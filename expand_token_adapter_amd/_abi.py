@@ -1,0 +1,94 @@
+"""ctypes declarations of the C ABI in include/lora_batch.h.
+
+Loads ``liblora_batch.so`` built in-tree by ``build.py``.  There is no
+fallback: if the library is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblora_batch.so")
+
+LORA_OK = 0
+LORA_ERR_INVALID_ARG = -1
+LORA_ERR_UNSUPPORTED = -2
+LORA_ERR_WORKSPACE = -3
+LORA_ERR_HIP = -4
+LORA_BF16 = 0
+LORA_F32 = 1
+LORA_MAX_RANK = 128
+LORA_ABI_VERSION = 1
+
+# Every function the header declares, with (restype, argtypes).
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_sz = ctypes.c_size_t
+_vp = ctypes.c_void_p
+
+
+class LoraAdapter(ctypes.Structure):
+    _fields_ = [("A", _vp), ("B", _vp), ("rank", _i32), ("scale", ctypes.c_float)]
+
+
+class LoraAdapterGrad(ctypes.Structure):
+    _fields_ = [("dA", _vp), ("dB", _vp)]
+
+
+class LoraSegments(ctypes.Structure):
+    _fields_ = [("counts", _vp), ("offsets", _vp), ("perm", _vp), ("err", _vp), ("sched", _vp)]
+
+
+SIGNATURES = {
+    "lora_abi_version": (ctypes.c_int, []),
+    "lora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "lora_segments_sched_elems": (_sz, [_i32, _i32]),
+    "lora_segments_workspace_bytes": (_sz, [_i32, _i32]),
+    "lora_backward_workspace_bytes": (_sz, [_i32, _i32]),
+    "lora_segments_build": (ctypes.c_int, [_vp, _i32, _i32, LoraSegments, _vp, _sz, _vp]),
+    "lora_shrink": (ctypes.c_int, [ctypes.c_int, _vp, _i64, _i32, _i32, _vp, _i32, _i32, LoraSegments,
+                                   _vp, _i64, _vp]),
+    "lora_expand_add": (ctypes.c_int, [ctypes.c_int, _vp, _i64, _i32, _i32, _vp, _i32, _i32, LoraSegments,
+                                       _vp, _i64, _vp]),
+    "lora_backward": (ctypes.c_int, [ctypes.c_int, _vp, _i64, _vp, _i64, _vp, _i64, _i32, _i32, _i32, _vp,
+                                     _vp, _i32, _i32, LoraSegments, _vp, _i64, _vp, _sz, _vp]),
+}
+
+_lib = None
+
+
+class LoraError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        msg = status_string(status) if _lib is not None else str(status)
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+
+
+def load() -> ctypes.CDLL:
+    """Load the HIP library (raises if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+            "or `python expand_token_adapter_amd/build.py`")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if lib.lora_abi_version() != LORA_ABI_VERSION:
+        raise RuntimeError("liblora_batch.so ABI version mismatch; rebuild it")
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().lora_status_string(int(status)).decode()
+
+
+def check(fn: str, status: int) -> None:
+    if status != LORA_OK:
+        raise LoraError(fn, status)

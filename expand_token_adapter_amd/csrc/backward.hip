@@ -1,0 +1,169 @@
+// backward.hip -- lora_backward entry point.
+//
+// The LoRA gradients of the fine-tuning rows (DeltaServe, section 3.2: the
+// backward computes the LoRA gradients from the saved layer input).  For
+// y = y0 + s B A x and a given dY:
+//   g  = B^T dy                      shrink kernel, weights read transposed
+//   v  = A x                         shrink kernel (or the caller's saved v)
+//   dX += s A^T g                    expand kernel, weights read transposed
+//   dA += s sum g x^T, dB += s sum dy v^T   token-contraction kernel
+// Four launches; the workspace holds g (by sorted position, row- and
+// rank-major) and v (rank-major).
+#include "host_checks.h"
+#include "lora_kernels.h"
+
+using namespace lora;
+
+namespace lora {
+int run_shrink(int dtype, bool trans_w, const ShrinkParams& p, int32_t T, int32_t num_adapters, hipStream_t st);
+int run_expand(int dtype, bool trans_w, const ExpandParams& p, int32_t T, int32_t num_adapters, int32_t r_max,
+               hipStream_t st);
+
+// Workspace layout of lora_backward (fp32 elements).
+struct BwdWs {
+    int64_t ldg, ldT;         // pitch of g rows; pitch of the rank-major arrays
+    int64_t g, gT, vT, total; // offsets
+    static BwdWs make(int64_t T, int64_t r_max) {
+        BwdWs w;
+        w.ldg = round_up(r_max, 8);
+        w.ldT = round_up(T > 0 ? T : 1, 32);
+        w.g = 0;
+        w.gT = round_up(w.g + T * w.ldg, 64);
+        w.vT = round_up(w.gT + r_max * w.ldT, 64);
+        w.total = round_up(w.vT + r_max * w.ldT, 64);
+        return w;
+    }
+};
+}  // namespace lora
+
+namespace {
+constexpr int64_t kMaxContractGrid = 4096;
+
+// vT[k][pos] = v[perm[pos]][k] for pos < n_valid, k < r_max: the caller's saved v,
+// rank-major by sorted position as the token contraction reads it.
+__global__ void transpose_v_kernel(const float* __restrict__ v, int64_t ldv, const int32_t* __restrict__ perm,
+                                   const int32_t* __restrict__ n_valid, int32_t r_max, float* __restrict__ vT,
+                                   int64_t ldT, int32_t T) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t pos = idx % T;
+    const int64_t k = idx / T;
+    if (k >= r_max || pos >= *n_valid) return;
+    vT[k * ldT + pos] = v[(int64_t)perm[pos] * ldv + k];
+}
+}  // namespace
+
+extern "C" size_t lora_backward_workspace_bytes(int32_t T_ft, int32_t r_max) {
+    if (T_ft < 0 || r_max < 1 || r_max > LORA_MAX_RANK) return 0;
+    return (size_t)BwdWs::make(T_ft, r_max).total * sizeof(float);
+}
+
+extern "C" int lora_backward(int dtype, const void* x, int64_t ldx, const void* dy, int64_t lddy, void* dx,
+                             int64_t lddx, int32_t T_ft, int32_t d_in, int32_t d_out, const lora_adapter* adapters,
+                             const lora_adapter_grad* grads, int32_t num_adapters, int32_t r_max,
+                             lora_segments seg_ft, const float* v_saved, int64_t ldv, void* ws, size_t ws_bytes,
+                             void* stream) {
+    int rc = check_common(dtype, T_ft, num_adapters, r_max, adapters, seg_ft);
+    if (rc != LORA_OK) return rc;
+    if (d_in < 1 || d_out < 1 || !grads || ((uintptr_t)grads & 7u)) return LORA_ERR_INVALID_ARG;
+    if (T_ft == 0) return LORA_OK;
+    if ((rc = check_matrix(x, d_in, ldx)) != LORA_OK) return rc;
+    if ((rc = check_matrix(dy, d_out, lddy)) != LORA_OK) return rc;
+    if (dx && (rc = check_matrix(dx, d_in, lddx)) != LORA_OK) return rc;
+    if (v_saved && (rc = check_f32_rows(v_saved, ldv, r_max)) != LORA_OK) return rc;
+    if (!seg_ft.offsets) return LORA_ERR_INVALID_ARG;
+    const BwdWs w = BwdWs::make(T_ft, r_max);
+    if (!ws || !aligned16(ws) || ws_bytes < (size_t)w.total * sizeof(float)) return LORA_ERR_WORKSPACE;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const SchedLayout sl = SchedLayout::make(T_ft, num_adapters);
+    float* wsf = static_cast<float*>(ws);
+    float* g = wsf + w.g;
+    float* gT = wsf + w.gT;
+    float* vT = wsf + w.vT;
+
+    // 1. g = B^T dy, written by sorted position (row-major for dX, rank-major for dA).
+    ShrinkParams sp{};
+    sp.x = dy;
+    sp.ldx = lddy;
+    sp.K = d_out;
+    sp.adapters = adapters;
+    sp.r_max = r_max;
+    sp.perm = seg_ft.perm;
+    sp.sched = seg_ft.sched;
+    sp.tiles16_off = sl.tiles16;
+    sp.out = g;
+    sp.ldo = w.ldg;
+    sp.out_by_pos = 1;
+    sp.outT = gT;
+    sp.ldT = w.ldT;
+    sp.err = seg_ft.err;
+    sp.rgroups = rank_groups(r_max);
+    if ((rc = run_shrink(dtype, true, sp, T_ft, num_adapters, st)) != LORA_OK) return rc;
+
+    // 2. v = A x, rank-major by sorted position.
+    if (v_saved) {
+        const int64_t n = (int64_t)T_ft * r_max;
+        hipLaunchKernelGGL(transpose_v_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, v_saved, ldv,
+                           seg_ft.perm, seg_ft.offsets + num_adapters, r_max, vT, w.ldT, T_ft);
+        if (hipGetLastError() != hipSuccess) return LORA_ERR_HIP;
+    } else {
+        ShrinkParams vp = sp;
+        vp.x = x;
+        vp.ldx = ldx;
+        vp.K = d_in;
+        vp.out = nullptr;
+        vp.outT = vT;
+        if ((rc = run_shrink(dtype, false, vp, T_ft, num_adapters, st)) != LORA_OK) return rc;
+    }
+
+    // 3. dX += s A^T g.
+    if (dx) {
+        ExpandParams ep{};
+        ep.v = g;
+        ep.ldv = w.ldg;
+        ep.v_by_pos = 1;
+        ep.adapters = adapters;
+        ep.r_max = r_max;
+        ep.perm = seg_ft.perm;
+        ep.sched = seg_ft.sched;
+        ep.tiles64_off = sl.tiles64;
+        ep.y = dx;
+        ep.ldy = lddx;
+        ep.N = d_in;
+        ep.err = seg_ft.err;
+        ep.ncb = (d_in + 63) / 64;
+        if ((rc = run_expand(dtype, true, ep, T_ft, num_adapters, r_max, st)) != LORA_OK) return rc;
+    }
+
+    // 4. dA += s g^T x, dB += s dy^T v.
+    ContractParams cp{};
+    cp.x = x;
+    cp.ldx = ldx;
+    cp.dy = dy;
+    cp.lddy = lddy;
+    cp.gT = gT;
+    cp.vT = vT;
+    cp.ldT = w.ldT;
+    cp.adapters = adapters;
+    cp.grads = grads;
+    cp.r_max = r_max;
+    cp.offsets = seg_ft.offsets;
+    cp.perm = seg_ft.perm;
+    cp.sched = seg_ft.sched;
+    cp.active_off = sl.active;
+    cp.d_in = d_in;
+    cp.d_out = d_out;
+    cp.ncb_in = (d_in + 63) / 64;
+    cp.ncb_out = (d_out + 63) / 64;
+    cp.rgroups = rank_groups(r_max);
+    cp.err = seg_ft.err;
+    const int64_t max_active = num_adapters < T_ft ? num_adapters : T_ft;
+    const int64_t tasks = max_active * cp.rgroups * (cp.ncb_in + cp.ncb_out);
+    const unsigned grid = grid_for(tasks, 1, kMaxContractGrid);
+    const dim3 block(kContractWaves * kWave);
+    if (dtype == LORA_BF16)
+        hipLaunchKernelGGL(contract_kernel<LORA_BF16>, dim3(grid), block, 0, st, cp);
+    else
+        hipLaunchKernelGGL(contract_kernel<LORA_F32>, dim3(grid), block, 0, st, cp);
+    return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}

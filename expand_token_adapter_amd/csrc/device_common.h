@@ -1,0 +1,279 @@
+// device_common.h -- gfx950 building blocks shared by the LoRA kernels:
+// bf16 conversion, MFMA wrappers, per-lane operand fragments and the
+// XCD-aware task walk.
+//
+// MFMA lane layout used throughout (16x16 output tiles, wave64):
+//   A operand (16 x K):  lane l supplies row  m = l % 16, a group of K values
+//   B operand (K x 16):  lane l supplies column n = l % 16, the same K group
+//   C/D (16 x 16 fp32):  lane l holds D[4 * (l / 16) + i][l % 16], i = 0..3
+// The K values a lane supplies for A and for B are taken from the same K
+// positions, so the product is the full sum over K whatever order the
+// hardware walks them in.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lora_batch.h"
+
+namespace lora {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kNumXcd = 8;  // MI355X: 8 accelerator dies, one L2 each
+
+// ---------------------------------------------------------------- scalars
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// fp32 -> bf16, round to nearest, ties to even; NaN stays NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// ---------------------------------------------------------------- MFMA
+
+__device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4_t mfma_f32(float a, float b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- fragments
+// A fragment is the 8 K-consecutive elements one lane feeds to one 16x16
+// tile step.  bf16: one 16-byte register quad, consumed by one
+// 16x16x32 MFMA.  fp32: two quads, consumed by eight 16x16x4 MFMAs.
+
+template <int DT>
+struct Frag;
+
+template <>
+struct Frag<LORA_BF16> {
+    u32x4_t q;
+    static constexpr int kBytes = 2;
+    __device__ __forceinline__ static Frag zero() { return Frag{u32x4_t{0, 0, 0, 0}}; }
+    // 8 elements at p (16-byte aligned).
+    __device__ __forceinline__ static Frag load(const void* p) {
+        return Frag{*reinterpret_cast<const u32x4_t*>(p)};
+    }
+    // Elements p[i * stride] for i < n (n <= 8), zeros after.
+    __device__ __forceinline__ static Frag load_strided(const void* p, int64_t stride, int n) {
+        const uint16_t* s = reinterpret_cast<const uint16_t*>(p);
+        uint32_t h[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) h[i] = (i < n) ? (uint32_t)s[i * stride] : 0u;
+        return Frag{u32x4_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                            h[6] | (h[7] << 16)}};
+    }
+    // From 8 fp32 values, rounded to bf16 (nearest even).
+    __device__ __forceinline__ static Frag from_f32(const float* f) {
+        uint32_t h[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) h[i] = f32_to_bf16_bits(f[i]);
+        return Frag{u32x4_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                            h[6] | (h[7] << 16)}};
+    }
+    __device__ __forceinline__ float get(int i) const {
+        uint32_t w = q[i >> 1];
+        return bf16_bits_to_f32((i & 1) ? (w >> 16) : (w & 0xffffu));
+    }
+    // Raw 16-bit pattern of element i.
+    __device__ __forceinline__ uint32_t raw(int i) const { return (q[i >> 1] >> (16 * (i & 1))) & 0xffffu; }
+};
+
+template <>
+struct Frag<LORA_F32> {
+    u32x4_t q0, q1;
+    static constexpr int kBytes = 4;
+    __device__ __forceinline__ static Frag zero() {
+        return Frag{u32x4_t{0, 0, 0, 0}, u32x4_t{0, 0, 0, 0}};
+    }
+    __device__ __forceinline__ static Frag load(const void* p) {
+        const u32x4_t* v = reinterpret_cast<const u32x4_t*>(p);
+        return Frag{v[0], v[1]};
+    }
+    __device__ __forceinline__ static Frag load_strided(const void* p, int64_t stride, int n) {
+        const uint32_t* s = reinterpret_cast<const uint32_t*>(p);
+        uint32_t h[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) h[i] = (i < n) ? s[i * stride] : 0u;
+        return Frag{u32x4_t{h[0], h[1], h[2], h[3]}, u32x4_t{h[4], h[5], h[6], h[7]}};
+    }
+    __device__ __forceinline__ static Frag from_f32(const float* f) {
+        return Frag{u32x4_t{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                            __float_as_uint(f[3])},
+                    u32x4_t{__float_as_uint(f[4]), __float_as_uint(f[5]), __float_as_uint(f[6]),
+                            __float_as_uint(f[7])}};
+    }
+    __device__ __forceinline__ float get(int i) const {
+        return __uint_as_float(i < 4 ? q0[i & 3] : q1[i & 3]);
+    }
+    __device__ __forceinline__ uint32_t raw(int i) const { return i < 4 ? q0[i & 3] : q1[i & 3]; }
+};
+
+// acc += A_frag (rows) x B_frag (columns) over the 8-element K group of each lane.
+__device__ __forceinline__ f32x4_t mma(const Frag<LORA_BF16>& a, const Frag<LORA_BF16>& b, f32x4_t c) {
+    return mfma_bf16(a.q, b.q, c);
+}
+__device__ __forceinline__ f32x4_t mma(const Frag<LORA_F32>& a, const Frag<LORA_F32>& b, f32x4_t c) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c = mfma_f32(__uint_as_float(a.q0[e]), __uint_as_float(b.q0[e]), c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c = mfma_f32(__uint_as_float(a.q1[e]), __uint_as_float(b.q1[e]), c);
+    return c;
+}
+
+// An fp32 operand (v, g) fed against element-typed weights.  For bf16 the
+// value is split into hi = bf16(v) and lo = bf16(v - hi), two exact-product
+// MFMAs whose sum carries about 16 significant bits of v; for fp32 the value
+// is used as is.
+template <int DT>
+struct F32Operand;
+
+template <>
+struct F32Operand<LORA_BF16> {
+    Frag<LORA_BF16> hi, lo;
+    __device__ __forceinline__ static F32Operand make(const float* f) {
+        F32Operand o;
+        uint32_t h[8], l[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            h[i] = f32_to_bf16_bits(f[i]);
+            l[i] = f32_to_bf16_bits(f[i] - bf16_bits_to_f32(h[i]));
+        }
+        o.hi.q = u32x4_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+        o.lo.q = u32x4_t{l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16)};
+        return o;
+    }
+    // acc += W x operand   (W as the A operand, this as the B operand)
+    __device__ __forceinline__ f32x4_t mma_right(const Frag<LORA_BF16>& w, f32x4_t c) const {
+        c = mma(w, hi, c);
+        return mma(w, lo, c);
+    }
+    // acc += operand x Q   (this as the A operand, Q as the B operand)
+    __device__ __forceinline__ f32x4_t mma_left(const Frag<LORA_BF16>& q, f32x4_t c) const {
+        c = mma(hi, q, c);
+        return mma(lo, q, c);
+    }
+};
+
+template <>
+struct F32Operand<LORA_F32> {
+    Frag<LORA_F32> f;
+    __device__ __forceinline__ static F32Operand make(const float* v) {
+        F32Operand o;
+        o.f = Frag<LORA_F32>::from_f32(v);
+        return o;
+    }
+    __device__ __forceinline__ f32x4_t mma_right(const Frag<LORA_F32>& w, f32x4_t c) const { return mma(w, f, c); }
+    __device__ __forceinline__ f32x4_t mma_left(const Frag<LORA_F32>& q, f32x4_t c) const { return mma(f, q, c); }
+};
+
+// ---------------------------------------------------------------- element IO
+
+template <int DT>
+struct Elem;
+
+template <>
+struct Elem<LORA_BF16> {
+    __device__ __forceinline__ static float get(const void* p, int64_t i) {
+        return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p)[i]);
+    }
+    // Read 8 consecutive elements (16-byte aligned) as fp32.
+    __device__ __forceinline__ static void load8(const void* p, float* f) {
+        u32x4_t q = *reinterpret_cast<const u32x4_t*>(p);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = bf16_bits_to_f32(q[i] & 0xffffu);
+            f[2 * i + 1] = bf16_bits_to_f32(q[i] >> 16);
+        }
+    }
+    // Write 8 fp32 values, each rounded once to bf16.
+    __device__ __forceinline__ static void store8(void* p, const float* f) {
+        u32x4_t q;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q[i] = f32_to_bf16_bits(f[2 * i]) | (f32_to_bf16_bits(f[2 * i + 1]) << 16);
+        *reinterpret_cast<u32x4_t*>(p) = q;
+    }
+};
+
+template <>
+struct Elem<LORA_F32> {
+    __device__ __forceinline__ static float get(const void* p, int64_t i) {
+        return reinterpret_cast<const float*>(p)[i];
+    }
+    __device__ __forceinline__ static void load8(const void* p, float* f) {
+        const f32x4_t* v = reinterpret_cast<const f32x4_t*>(p);
+        f32x4_t a = v[0], b = v[1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[i] = a[i];
+            f[4 + i] = b[i];
+        }
+    }
+    __device__ __forceinline__ static void store8(void* p, const float* f) {
+        f32x4_t* v = reinterpret_cast<f32x4_t*>(p);
+        v[0] = f32x4_t{f[0], f[1], f[2], f[3]};
+        v[1] = f32x4_t{f[4], f[5], f[6], f[7]};
+    }
+};
+
+// ---------------------------------------------------------------- tasks
+
+// Scheduling metadata written by the segment builder (int32 offsets into
+// lora_segments.sched).  Tile records are {adapter, first sorted position,
+// rows, 0}.
+struct SchedLayout {
+    int64_t active;    // [A] adapters with at least one row, ascending
+    int64_t tiles16;   // [n16_max] records of up to 16 rows
+    int64_t tiles64;   // [n64_max] records of up to 64 rows
+    int64_t total;     // int32 elements
+    __host__ __device__ static SchedLayout make(int64_t T, int64_t A) {
+        SchedLayout s;
+        s.active = 4;
+        s.tiles16 = s.active + ((A + 3) / 4) * 4;
+        int64_t n16 = (T + 15) / 16 + A;
+        s.tiles64 = s.tiles16 + 4 * n16;
+        int64_t n64 = (T + 63) / 64 + A;
+        s.total = s.tiles64 + 4 * n64;
+        return s;
+    }
+    __host__ __device__ static int64_t max_tiles16(int64_t T, int64_t A) { return (T + 15) / 16 + A; }
+    __host__ __device__ static int64_t max_tiles64(int64_t T, int64_t A) { return (T + 63) / 64 + A; }
+};
+// sched[0] = number of 16-row tiles, sched[1] = number of 64-row tiles,
+// sched[2] = number of active adapters.
+
+// Contiguous slice of a task range for the calling wave group.  Workgroups
+// are handed to the 8 XCDs round-robin by index, so workgroups b with the
+// same b % 8 share an L2; giving each such set one contiguous slice keeps
+// neighbouring tasks (same adapter, same weights) in one L2.
+struct TaskSlice {
+    int64_t begin, end, stride;
+};
+__device__ __forceinline__ TaskSlice xcd_slice(int64_t n, int units_per_wg, int unit) {
+    const int x = blockIdx.x % kNumXcd;
+    const int64_t per = (n + kNumXcd - 1) / kNumXcd;
+    TaskSlice s;
+    s.begin = (int64_t)x * per;
+    s.end = s.begin + per < n ? s.begin + per : n;
+    s.begin += (int64_t)(blockIdx.x / kNumXcd) * units_per_wg + unit;
+    s.stride = (int64_t)(gridDim.x / kNumXcd) * units_per_wg;
+    return s;
+}
+
+__device__ __forceinline__ bool adapter_ok(const lora_adapter& ad, int r_max) {
+    return ad.rank >= 1 && ad.rank <= r_max && ad.A != nullptr && ad.B != nullptr &&
+           (((uintptr_t)ad.A | (uintptr_t)ad.B) & 15u) == 0;
+}
+
+}  // namespace lora

@@ -1,0 +1,222 @@
+// segments.hip -- group the rows of a batch by adapter.
+//
+// Multi-LoRA batching applies each row's own adapter inside one shared pass
+// (DeltaServe, section 2.2).  The compute kernels therefore need, for every
+// adapter, the list of its rows: a counting sort of the rows by adapter id.
+//
+// Three kernels, all deterministic (the order inside an adapter is the row
+// order, never the order in which threads happen to run):
+//   1. seg_count   one workgroup per chunk of kChunk rows: each row's rank
+//                  among the earlier rows of its chunk with the same id, and
+//                  the per-(adapter, chunk) counts.
+//   2. seg_scan    one workgroup: per-adapter prefix over chunks, exclusive
+//                  scans over adapters (offsets, tile prefixes, active list).
+//   3. seg_scatter one workgroup per chunk: perm[pos] = row, plus the tile
+//                  records the shrink / expand / backward kernels walk.
+#include "device_common.h"
+
+namespace lora {
+
+constexpr int kChunk = 256;
+constexpr int kScanThreads = 1024;
+
+// Workspace layout (int32 elements), regions aligned to 64 elements.
+struct SegWs {
+    int64_t hist, rank, errc, pre16, pre64, total;
+    static SegWs make(int64_t T, int64_t A) {
+        auto al = [](int64_t n) { return (n + 63) / 64 * 64; };
+        const int64_t nchunks = (T + kChunk - 1) / kChunk;
+        SegWs w;
+        w.hist = 0;
+        w.rank = w.hist + al(A * nchunks);
+        w.errc = w.rank + al(T);
+        w.pre16 = w.errc + al(nchunks);
+        w.pre64 = w.pre16 + al(A);
+        w.total = w.pre64 + al(A);
+        return w;
+    }
+};
+
+__global__ __launch_bounds__(kChunk) void seg_count_kernel(const int32_t* __restrict__ ids, int32_t T, int32_t A,
+                                                           int32_t nchunks, int32_t* __restrict__ hist,
+                                                           int32_t* __restrict__ rank, int32_t* __restrict__ errc) {
+    __shared__ int32_t s_ids[kChunk];
+    __shared__ int32_t s_err[kChunk / kWave];
+    const int c = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int64_t t = (int64_t)c * kChunk + tid;
+    const int32_t id = t < T ? ids[t] : -1;
+    const bool valid = id >= 0 && id < A;
+    const bool bad = t < T && !valid && id != -1;
+    s_ids[tid] = valid ? id : -1;
+    // This workgroup owns column c of hist[A][nchunks]; clear it first.
+    for (int a = tid; a < A; a += kChunk) hist[(int64_t)a * nchunks + c] = 0;
+    __syncthreads();
+    int before = 0, same = 0;
+#pragma unroll 16
+    for (int j = 0; j < kChunk; ++j) {
+        const int eq = s_ids[j] == id;
+        same += eq;
+        before += eq & (j < tid);
+    }
+    if (valid) {
+        rank[t] = before;
+        if (before + 1 == same) hist[(int64_t)id * nchunks + c] = same;  // last row of this id in the chunk
+    }
+    const uint64_t m = __ballot(bad);
+    if ((tid & (kWave - 1)) == 0) s_err[tid / kWave] = __popcll(m);
+    __syncthreads();
+    if (tid == 0) {
+        int e = 0;
+        for (int w = 0; w < kChunk / kWave; ++w) e += s_err[w];
+        errc[c] = e;
+    }
+}
+
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int o = __shfl_up(v, d, kWave);
+        if (lane >= d) v += o;
+    }
+    return v;
+}
+
+// Exclusive scan of one int per thread across the workgroup; returns the
+// exclusive prefix and writes the workgroup total to *total.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* s_tot, int* total) {
+    constexpr int kWaves = kScanThreads / kWave;
+    const int w = threadIdx.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int incl = wave_inclusive_scan(v);
+    if (lane == kWave - 1) s_tot[w] = incl;
+    __syncthreads();
+    int before = 0, all = 0;
+    for (int i = 0; i < kWaves; ++i) {
+        const int x = s_tot[i];
+        before += i < w ? x : 0;
+        all += x;
+    }
+    __syncthreads();
+    *total = all;
+    return before + incl - v;
+}
+
+__global__ __launch_bounds__(kScanThreads) void seg_scan_kernel(int32_t A, int32_t nchunks, int32_t* __restrict__ hist,
+                                                                const int32_t* __restrict__ errc,
+                                                                int32_t* __restrict__ counts,
+                                                                int32_t* __restrict__ offsets,
+                                                                int32_t* __restrict__ sched,
+                                                                int32_t* __restrict__ pre16,
+                                                                int32_t* __restrict__ pre64, int32_t* __restrict__ err,
+                                                                int64_t active_off) {
+    __shared__ int s_tot[4][kScanThreads / kWave];
+    const int tid = threadIdx.x;
+    // Per adapter: exclusive prefix of its chunk counts (in place), total = count.
+    for (int a = tid; a < A; a += kScanThreads) {
+        int32_t* h = hist + (int64_t)a * nchunks;
+        int run = 0;
+        for (int c = 0; c < nchunks; ++c) {
+            const int x = h[c];
+            h[c] = run;
+            run += x;
+        }
+        counts[a] = run;
+    }
+    __syncthreads();
+    int carry_c = 0, carry16 = 0, carry64 = 0, carry_act = 0;
+    int32_t* active = sched + active_off;
+    for (int base = 0; base < A; base += kScanThreads) {
+        const int a = base + tid;
+        const int c = a < A ? counts[a] : 0;
+        int tc, t16, t64, tact;
+        const int ec = block_exclusive_scan(c, s_tot[0], &tc);
+        const int e16 = block_exclusive_scan((c + 15) / 16, s_tot[1], &t16);
+        const int e64 = block_exclusive_scan((c + 63) / 64, s_tot[2], &t64);
+        const int eact = block_exclusive_scan(c > 0 ? 1 : 0, s_tot[3], &tact);
+        if (a < A) {
+            offsets[a] = carry_c + ec;
+            pre16[a] = carry16 + e16;
+            pre64[a] = carry64 + e64;
+            if (c > 0) active[carry_act + eact] = a;
+        }
+        carry_c += tc;
+        carry16 += t16;
+        carry64 += t64;
+        carry_act += tact;
+    }
+    if (tid == 0) {
+        offsets[A] = carry_c;
+        sched[0] = carry16;
+        sched[1] = carry64;
+        sched[2] = carry_act;
+        sched[3] = 0;
+        int e = 0;
+        for (int c = 0; c < nchunks; ++c) e += errc[c];
+        err[0] = e;
+    }
+}
+
+__global__ __launch_bounds__(kChunk) void seg_scatter_kernel(const int32_t* __restrict__ ids, int32_t T, int32_t A,
+                                                             int32_t nchunks, const int32_t* __restrict__ hist,
+                                                             const int32_t* __restrict__ rank,
+                                                             const int32_t* __restrict__ counts,
+                                                             const int32_t* __restrict__ offsets,
+                                                             const int32_t* __restrict__ pre16,
+                                                             const int32_t* __restrict__ pre64,
+                                                             int32_t* __restrict__ perm, int32_t* __restrict__ sched,
+                                                             int64_t tiles16_off, int64_t tiles64_off) {
+    const int c = blockIdx.x;
+    const int64_t t = (int64_t)c * kChunk + threadIdx.x;
+    if (t >= T) return;
+    const int32_t id = ids[t];
+    if (id < 0 || id >= A) return;
+    const int32_t local = hist[(int64_t)id * nchunks + c] + rank[t];  // position inside the adapter's group
+    const int32_t pos = offsets[id] + local;
+    perm[pos] = (int32_t)t;
+    const int32_t cnt = counts[id];
+    if ((local & 15) == 0) {
+        int32_t* rec = sched + tiles16_off + 4 * (int64_t)(pre16[id] + local / 16);
+        const int32_t rows = cnt - local < 16 ? cnt - local : 16;
+        *reinterpret_cast<int4*>(rec) = make_int4(id, pos, rows, 0);
+    }
+    if ((local & 63) == 0) {
+        int32_t* rec = sched + tiles64_off + 4 * (int64_t)(pre64[id] + local / 64);
+        const int32_t rows = cnt - local < 64 ? cnt - local : 64;
+        *reinterpret_cast<int4*>(rec) = make_int4(id, pos, rows, 0);
+    }
+}
+
+}  // namespace lora
+
+using namespace lora;
+
+extern "C" size_t lora_segments_workspace_bytes(int32_t T, int32_t num_adapters) {
+    if (T < 0 || num_adapters < 1) return 0;
+    return (size_t)SegWs::make(T, num_adapters).total * sizeof(int32_t);
+}
+
+extern "C" int lora_segments_build(const int32_t* adapter_ids, int32_t T, int32_t num_adapters, lora_segments seg,
+                                   void* ws, size_t ws_bytes, void* stream) {
+    if (T < 0 || num_adapters < 1) return LORA_ERR_INVALID_ARG;
+    if (T == 0) return LORA_OK;
+    if (!adapter_ids || !seg.counts || !seg.offsets || !seg.perm || !seg.err || !seg.sched) return LORA_ERR_INVALID_ARG;
+    if (((uintptr_t)seg.sched & 15u) != 0) return LORA_ERR_INVALID_ARG;
+    const SegWs w = SegWs::make(T, num_adapters);
+    if (!ws || ws_bytes < (size_t)w.total * sizeof(int32_t)) return LORA_ERR_WORKSPACE;
+    const int64_t nchunks64 = ((int64_t)T + kChunk - 1) / kChunk;
+    const int32_t nchunks = (int32_t)nchunks64;
+    const SchedLayout sl = SchedLayout::make(T, num_adapters);
+    int32_t* wsi = static_cast<int32_t*>(ws);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipLaunchKernelGGL(seg_count_kernel, dim3(nchunks), dim3(kChunk), 0, st, adapter_ids, T, num_adapters, nchunks,
+                       wsi + w.hist, wsi + w.rank, wsi + w.errc);
+    hipLaunchKernelGGL(seg_scan_kernel, dim3(1), dim3(kScanThreads), 0, st, num_adapters, nchunks, wsi + w.hist,
+                       wsi + w.errc, seg.counts, seg.offsets, seg.sched, wsi + w.pre16, wsi + w.pre64, seg.err,
+                       sl.active);
+    hipLaunchKernelGGL(seg_scatter_kernel, dim3(nchunks), dim3(kChunk), 0, st, adapter_ids, T, num_adapters, nchunks,
+                       wsi + w.hist, wsi + w.rank, seg.counts, seg.offsets, wsi + w.pre16, wsi + w.pre64, seg.perm,
+                       seg.sched, sl.tiles16, sl.tiles64);
+    return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}

@@ -1,0 +1,207 @@
+/*
+ * lora_batch.h -- C ABI of the multi-LoRA batched adapter library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method.  LoRA replaces the update of a frozen weight W in R^{d x k} by a
+ * low-rank product Delta W = B A with A in R^{r x k} and B in R^{d x r}
+ * (DeltaServe, section 2.2), so a layer computes h(x) = W x + B A x (MOLT,
+ * section 2.1, displayed equation).  Multi-LoRA batching lets rows that use
+ * different adapters share one base pass while each row applies the low-rank
+ * weights of its own adapter (DeltaServe, section 2.2; the adapter-caching page
+ * on kernel-level batching of several adapters).  A fine-tuning sample is an
+ * ordinary batch entry routed to a reserved adapter (DeltaServe, section 3.2,
+ * "Mixed forward batch"), and the fine-tuning backward computes the LoRA
+ * gradients from the saved layer input (DeltaServe, section 3.2, "Backward
+ * subprocess").  The caller computes the base output y0 = W x; this library
+ * adds, for every row t bound to adapter a = a(t),
+ *
+ *     v_t = A_a x_t                      (lora_shrink,    fp32 [r_a])
+ *     y_t += s_a * B_a v_t               (lora_expand_add)
+ *
+ * and for fine-tuning rows, given dY = dL/dy,
+ *
+ *     g_t = B_a^T dy_t,  dX_t += s_a A_a^T g_t,
+ *     dA_a += s_a sum_t g_t x_t^T,  dB_a += s_a sum_t dy_t v_t^T   (lora_backward)
+ *
+ * s_a is a per-adapter multiplier (alpha / r; DeltaServe section 4.1 uses
+ * alpha = 32 at r = 16, i.e. s = 2).
+ *
+ * Conventions shared by every call
+ *   - Matrices are row-major.  d_in = k and d_out = d in the pages' notation.
+ *     A_a is [r_a, d_in], B_a is [d_out, r_a]; x is [T, d_in] with row pitch
+ *     ldx elements; y is [T, d_out] with pitch ldy.
+ *   - Element type (lora_dtype) applies to x, y, dY, dX, A_a and B_a.  v, g,
+ *     dA and dB are always fp32.  bf16 results (y, dX) are formed in fp32 and
+ *     rounded once, to nearest even.
+ *   - All data pointers are DEVICE pointers unless stated; the lora_segments
+ *     struct itself is passed by value from the host and holds device
+ *     pointers.  `stream` is a hipStream_t (NULL = the null stream).  Every
+ *     compute call only enqueues work on `stream`; none synchronizes.
+ *   - Ownership: the caller allocates and owns every buffer, including
+ *     workspaces (sized by the *_workspace_bytes queries) and the
+ *     device-resident adapter and gradient tables.  The library allocates no
+ *     memory and keeps no mutable global state; calls on different streams are
+ *     independent when they use different output and workspace buffers.
+ *   - Requirements checked on the host before anything is enqueued (a failing
+ *     check returns a negative status and enqueues nothing):
+ *       non-NULL required pointers; T >= 0; d_in, d_out >= 1; num_adapters >= 1;
+ *       1 <= r_max <= LORA_MAX_RANK; leading dimensions >= the row length;
+ *       x, y, dY, dX, v pointers 16-byte aligned; d_in, d_out and every
+ *       element-matrix pitch a multiple of 8 (else LORA_ERR_UNSUPPORTED);
+ *       fp32 pitches ldv a multiple of 4 and >= r_max; workspace large enough.
+ *     T == 0 returns LORA_OK and enqueues nothing.
+ *   - Data checked on the device: adapter ids outside [-1, num_adapters) and
+ *     table entries with rank outside [1, r_max], a NULL or non-16-byte-aligned
+ *     A/B pointer, or a NULL gradient entry for a trained adapter.  Such rows
+ *     are skipped (never read or written out of bounds) and *seg.err is
+ *     increased; a nonzero *seg.err after the stream completes means the call
+ *     met bad data.  lora_segments_build sets *err to the number of bad ids;
+ *     later calls on the same segments only add to it.
+ *   - Rows with adapter id -1 carry no adapter: y and v rows are left as they
+ *     are.
+ *   - Results are deterministic: every reduction runs in a fixed order and no
+ *     floating-point atomics are used, so repeated calls give identical bits.
+ */
+#ifndef LORA_BATCH_H
+#define LORA_BATCH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LORA_ABI_VERSION 1
+#define LORA_MAX_RANK 128
+
+/* Status codes returned by every entry point. */
+enum {
+    LORA_OK = 0,
+    LORA_ERR_INVALID_ARG = -1, /* bad pointer, size, pitch or enum */
+    LORA_ERR_UNSUPPORTED = -2, /* valid but outside what the kernels cover */
+    LORA_ERR_WORKSPACE = -3,   /* workspace missing or too small */
+    LORA_ERR_HIP = -4          /* a HIP launch failed */
+};
+
+/* Element type of x, y, dY, dX, A and B. */
+enum { LORA_BF16 = 0, LORA_F32 = 1 };
+
+/* One adapter of the device-resident table (24 bytes).
+ * A: [rank, d_in] and B: [d_out, rank], row-major, 16-byte aligned, element
+ * type of the call.  scale multiplies the adapter's delta. */
+typedef struct lora_adapter {
+    const void* A;
+    const void* B;
+    int32_t rank;
+    float scale;
+} lora_adapter;
+
+/* Gradient targets of one adapter (device table, 16 bytes).  dA: [rank, d_in]
+ * and dB: [d_out, rank], fp32 row-major, accumulated into ("+=").  Entries of
+ * adapters without fine-tuning rows may be NULL. */
+typedef struct lora_adapter_grad {
+    float* dA;
+    float* dB;
+} lora_adapter_grad;
+
+/* Rows grouped by adapter (all device pointers, filled by lora_segments_build).
+ *   counts [A]     rows per adapter
+ *   offsets[A+1]   exclusive prefix sum of counts; offsets[A] = rows with a valid id
+ *   perm   [T]     row indices grouped by adapter, ascending inside a group
+ *                  (entries past offsets[A] are unspecified)
+ *   err    [1]     device-side error count (see the conventions above)
+ *   sched  [lora_segments_sched_elems(T, A)]  scheduling metadata read by the
+ *                  compute kernels (tile prefix sums, active-adapter list);
+ *                  opaque to the caller. */
+typedef struct lora_segments {
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* perm;
+    int32_t* err;
+    int32_t* sched;
+} lora_segments;
+
+/* LORA_ABI_VERSION of the built library. */
+int lora_abi_version(void);
+
+/* Static, NUL-terminated description of a status code (host). */
+const char* lora_status_string(int status);
+
+/* Number of int32 elements of lora_segments.sched for T rows and
+ * num_adapters adapters (host, pure).  sched must be 16-byte aligned. */
+size_t lora_segments_sched_elems(int32_t T, int32_t num_adapters);
+
+/* Workspace bytes of lora_segments_build (host, pure). */
+size_t lora_segments_workspace_bytes(int32_t T, int32_t num_adapters);
+
+/* Workspace bytes of lora_backward for T_ft rows and maximum rank r_max
+ * (host, pure). */
+size_t lora_backward_workspace_bytes(int32_t T_ft, int32_t r_max);
+
+/*
+ * Group the rows of a batch by adapter: which weights each row applies
+ * (DeltaServe, section 2.2, multi-LoRA batching; the reserved fine-tuning
+ * adapter of section 3.2 is an ordinary id).
+ *   adapter_ids [T] int32 device: a(t) in [0, num_adapters), or -1 for none.
+ *   seg: output buffers (see lora_segments).  ws: device workspace of
+ *   lora_segments_workspace_bytes(T, num_adapters) bytes; its contents on
+ *   entry do not matter.
+ * Integer outputs are exact and unique (stable grouping).  Three kernels.
+ */
+int lora_segments_build(const int32_t* adapter_ids, int32_t T, int32_t num_adapters,
+                        lora_segments seg, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Shrink: v_t = A_{a(t)} x_t with fp32 accumulation, for every row with an
+ * adapter (the "A x" of h(x) = W x + B A x, MOLT section 2.1).
+ *   x [T, ldx] (dtype), adapters [num_adapters] device table, seg from
+ *   lora_segments_build over the same T rows, v [T, ldv] fp32 output
+ *   (ldv >= r_max, multiple of 4).  Row t of v receives columns 0..r_a-1;
+ *   columns r_a..r_max-1 are unspecified; rows without an adapter are left
+ *   unchanged.
+ */
+int lora_shrink(int dtype, const void* x, int64_t ldx, int32_t T, int32_t d_in,
+                const lora_adapter* adapters, int32_t num_adapters, int32_t r_max,
+                lora_segments seg, float* v, int64_t ldv, void* stream);
+
+/*
+ * Expand-add: y_t += s_{a(t)} B_{a(t)} v_t, computed in fp32 and rounded once to
+ * the element type; the delta is added to the caller's base output (the
+ * adapter-caching page: the adapter's activations are added to the backbone
+ * layer's outputs).
+ *   v [T, ldv] fp32 from lora_shrink; y [T, ldy] (dtype) in/out.
+ *   Only columns 0..r_a-1 of each v row are read.
+ */
+int lora_expand_add(int dtype, const float* v, int64_t ldv, int32_t T, int32_t d_out,
+                    const lora_adapter* adapters, int32_t num_adapters, int32_t r_max,
+                    lora_segments seg, void* y, int64_t ldy, void* stream);
+
+/*
+ * LoRA backward over T_ft fine-tuning rows (DeltaServe, section 3.2: the
+ * backward computes the LoRA gradients from the saved layer input).
+ *   x  [T_ft, ldx]  layer input of the fine-tuning rows (dtype)
+ *   dy [T_ft, lddy] dL/dy of those rows (dtype)
+ *   dx [T_ft, lddx] in/out, dX += s A^T B^T dy (dtype); NULL skips dX
+ *   grads [num_adapters] device table; dA_a += s (B_a^T dy) x^T and
+ *         dB_a += s dy (A_a x)^T, summed over the rows of adapter a (fp32)
+ *   seg_ft: lora_segments_build over the fine-tuning rows' ids (row indices
+ *         0..T_ft-1 refer to x, dy, dx)
+ *   v_saved [T_ft, ldv] fp32: v = A x of these rows as lora_shrink wrote it,
+ *         or NULL to recompute it from x
+ *   ws: lora_backward_workspace_bytes(T_ft, r_max) bytes of device memory.
+ * The caller passes a compact view of the fine-tuning rows; a contiguous
+ * fine-tuning tail of a mixed batch is passed by pointer offset, no copy.
+ */
+int lora_backward(int dtype, const void* x, int64_t ldx, const void* dy, int64_t lddy,
+                  void* dx, int64_t lddx, int32_t T_ft, int32_t d_in, int32_t d_out,
+                  const lora_adapter* adapters, const lora_adapter_grad* grads,
+                  int32_t num_adapters, int32_t r_max, lora_segments seg_ft,
+                  const float* v_saved, int64_t ldv, void* ws, size_t ws_bytes,
+                  void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LORA_BATCH_H */

@@ -1,0 +1,139 @@
+"""Host-side tests of the C ABI: the library loads, exports every declared
+symbol, answers its pure queries, and rejects bad arguments before touching
+the GPU (every call here fails validation, so no HIP call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from expand_token_adapter_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lora_batch.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lora_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _abi.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_abi.SIGNATURES), "binding and header disagree"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.lora_abi_version() == 1
+    for s in (0, -1, -2, -3, -4, 7):
+        assert isinstance(_abi.status_string(s), str) and _abi.status_string(s)
+
+
+def test_struct_sizes_match_header():
+    assert ctypes.sizeof(_abi.LoraAdapter) == 24
+    assert ctypes.sizeof(_abi.LoraAdapterGrad) == 16
+    assert ctypes.sizeof(_abi.LoraSegments) == 40
+
+
+def test_workspace_queries(lib):
+    assert lib.lora_segments_workspace_bytes(0, 4) > 0
+    assert lib.lora_segments_workspace_bytes(-1, 4) == 0
+    assert lib.lora_segments_workspace_bytes(10, 0) == 0
+    a = lib.lora_segments_workspace_bytes(1000, 32)
+    b = lib.lora_segments_workspace_bytes(5000, 32)
+    assert b > a >= 4 * 1000
+    assert lib.lora_backward_workspace_bytes(2048, 64) >= 3 * 2048 * 64 * 4
+    assert lib.lora_backward_workspace_bytes(16, 0) == 0
+    assert lib.lora_backward_workspace_bytes(16, 129) == 0
+    # 16-row and 64-row tile records for every row plus one partial tile per adapter
+    n = lib.lora_segments_sched_elems(1000, 10)
+    assert n >= 4 * ((1000 + 15) // 16 + 10) + 4 * ((1000 + 63) // 64 + 10)
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
+
+
+def _seg(ok=True):
+    p = FAKE if ok else 0
+    return _abi.LoraSegments(FAKE, FAKE, FAKE, FAKE, p)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=5), _abi.LORA_ERR_INVALID_ARG),
+    (dict(T=-1), _abi.LORA_ERR_INVALID_ARG),
+    (dict(A=0), _abi.LORA_ERR_INVALID_ARG),
+    (dict(r_max=0), _abi.LORA_ERR_INVALID_ARG),
+    (dict(r_max=129), _abi.LORA_ERR_INVALID_ARG),
+    (dict(adapters=0), _abi.LORA_ERR_INVALID_ARG),
+    (dict(seg_ok=False), _abi.LORA_ERR_INVALID_ARG),
+    (dict(x=0), _abi.LORA_ERR_INVALID_ARG),
+    (dict(x=FAKE + 4), _abi.LORA_ERR_INVALID_ARG),
+    (dict(ld=100), _abi.LORA_ERR_INVALID_ARG),
+    (dict(d=100, ld=100), _abi.LORA_ERR_UNSUPPORTED),
+    (dict(ld=260), _abi.LORA_ERR_UNSUPPORTED),
+    (dict(v=0), _abi.LORA_ERR_INVALID_ARG),
+    (dict(ldv=6), _abi.LORA_ERR_INVALID_ARG),
+    (dict(ldv=4), _abi.LORA_ERR_INVALID_ARG),
+])
+def test_shrink_and_expand_reject_bad_arguments(lib, kw, code):
+    a = dict(dtype=0, T=64, A=4, r_max=8, adapters=FAKE, seg_ok=True, x=FAKE, ld=256, d=256, v=FAKE, ldv=8)
+    a.update(kw)
+    st = lib.lora_shrink(a["dtype"], a["x"], a["ld"], a["T"], a["d"], a["adapters"], a["A"], a["r_max"],
+                         _seg(a["seg_ok"]), a["v"], a["ldv"], None)
+    assert st == code
+    st = lib.lora_expand_add(a["dtype"], a["v"], a["ldv"], a["T"], a["d"], a["adapters"], a["A"], a["r_max"],
+                             _seg(a["seg_ok"]), a["x"], a["ld"], None)
+    assert st == code
+
+
+def test_zero_rows_is_a_no_op(lib):
+    st = lib.lora_shrink(0, 0, 0, 0, 256, FAKE, 4, 8, _seg(), 0, 0, None)
+    assert st == _abi.LORA_OK
+    st = lib.lora_expand_add(0, 0, 0, 0, 256, FAKE, 4, 8, _seg(), 0, 0, None)
+    assert st == _abi.LORA_OK
+    st = lib.lora_segments_build(0, 0, 4, _seg(), 0, 0, None)
+    assert st == _abi.LORA_OK
+    st = lib.lora_backward(0, 0, 0, 0, 0, 0, 0, 0, 256, 256, FAKE, FAKE, 4, 8, _seg(), 0, 0, 0, 0, None)
+    assert st == _abi.LORA_OK
+
+
+def test_segments_build_rejects(lib):
+    need = lib.lora_segments_workspace_bytes(100, 4)
+    assert lib.lora_segments_build(FAKE, -1, 4, _seg(), FAKE, need, None) == _abi.LORA_ERR_INVALID_ARG
+    assert lib.lora_segments_build(FAKE, 100, 0, _seg(), FAKE, need, None) == _abi.LORA_ERR_INVALID_ARG
+    assert lib.lora_segments_build(0, 100, 4, _seg(), FAKE, need, None) == _abi.LORA_ERR_INVALID_ARG
+    assert lib.lora_segments_build(FAKE, 100, 4, _seg(False), FAKE, need, None) == _abi.LORA_ERR_INVALID_ARG
+    assert lib.lora_segments_build(FAKE, 100, 4, _seg(), FAKE, need - 1, None) == _abi.LORA_ERR_WORKSPACE
+    assert lib.lora_segments_build(FAKE, 100, 4, _seg(), 0, need, None) == _abi.LORA_ERR_WORKSPACE
+
+
+def test_backward_rejects(lib):
+    need = lib.lora_backward_workspace_bytes(16, 8)
+
+    def call(**kw):
+        a = dict(dtype=0, x=FAKE, ldx=256, dy=FAKE, lddy=256, dx=FAKE, lddx=256, T=16, d_in=256, d_out=256,
+                 adapters=FAKE, grads=FAKE, A=4, r_max=8, seg=_seg(), vs=0, ldv=0, ws=FAKE, wsb=need)
+        a.update(kw)
+        return lib.lora_backward(a["dtype"], a["x"], a["ldx"], a["dy"], a["lddy"], a["dx"], a["lddx"], a["T"],
+                                 a["d_in"], a["d_out"], a["adapters"], a["grads"], a["A"], a["r_max"], a["seg"],
+                                 a["vs"], a["ldv"], a["ws"], a["wsb"], None)
+
+    assert call(grads=0) == _abi.LORA_ERR_INVALID_ARG
+    assert call(grads=FAKE + 4) == _abi.LORA_ERR_INVALID_ARG
+    assert call(dy=0) == _abi.LORA_ERR_INVALID_ARG
+    assert call(lddy=100) == _abi.LORA_ERR_INVALID_ARG
+    assert call(d_out=100, lddy=100) == _abi.LORA_ERR_UNSUPPORTED
+    assert call(dx=FAKE + 2) == _abi.LORA_ERR_INVALID_ARG
+    assert call(vs=FAKE, ldv=4) == _abi.LORA_ERR_INVALID_ARG
+    assert call(wsb=need - 1) == _abi.LORA_ERR_WORKSPACE
+    assert call(ws=FAKE + 8) == _abi.LORA_ERR_WORKSPACE
+    assert call(seg=_seg(False)) == _abi.LORA_ERR_INVALID_ARG

@@ -1,0 +1,233 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bars: segment outputs bit-exact; y, dX, dA, dB within max|err| <= 2e-2 *
+max|ref| (bf16) or 1e-5 * max|ref| (fp32) per tensor; the same rule on the
+delta alone (base output zero), so the check sees the low-rank term itself.
+"""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from gpu_helpers import TOL, GpuCase, rel_err
+    import expand_token_adapter_amd as lb
+
+oracle.set_threads(16)
+_config = functools.lru_cache(maxsize=None)(workloads.config)
+
+
+def _ids_case(kind, T, A, rng):
+    if kind == "random":
+        return rng.integers(-1, A, size=T)
+    if kind == "sorted":
+        return np.sort(rng.integers(0, A, size=T))
+    if kind == "reverse":
+        return np.sort(rng.integers(0, A, size=T))[::-1]
+    if kind == "same":
+        return np.full(T, A - 1)
+    if kind == "none":
+        return np.full(T, -1)
+    if kind == "zipf":
+        p = np.arange(1, A + 1, dtype=float) ** -1.1
+        return rng.choice(A, size=T, p=p / p.sum())
+    if kind == "bad":
+        return rng.integers(-4, A + 4, size=T)
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("kind", ["random", "sorted", "reverse", "same", "none", "zipf", "bad"])
+@pytest.mark.parametrize("T,A", [(1, 1), (255, 3), (257, 64), (2048, 320), (10368, 32), (6000, 1500)])
+def test_segments_bit_exact(kind, T, A):
+    rng = np.random.default_rng(T * 7919 + A)
+    ids = np.ascontiguousarray(_ids_case(kind, T, A, rng), dtype=np.int32)
+    seg = lb.lora_segments_build(torch.from_numpy(ids).cuda(), A)
+    torch.cuda.synchronize()
+    counts, offsets, perm, err = oracle.segments(ids, A)
+    assert np.array_equal(seg.counts.cpu().numpy(), counts)
+    assert np.array_equal(seg.offsets.cpu().numpy(), offsets)
+    n = int(offsets[-1])
+    assert np.array_equal(seg.perm.cpu().numpy()[:n], perm)
+    assert int(seg.err.item()) == err
+
+
+def _check_forward(case, tol):
+    y, v, seg = case.forward()
+    y_ref, v_ref = case.oracle_forward()
+    assert int(seg.err.item()) == 0
+    e = rel_err(y, y_ref)
+    assert e <= tol, f"y max|err|/max|ref| = {e:.3e} > {tol}"
+    ranks = case.wl.ranks
+    ids = case.wl.ids
+    vg = v.double().cpu().numpy()
+    mask = np.zeros_like(v_ref, dtype=bool)
+    for t in np.nonzero(ids >= 0)[0]:
+        mask[t, :ranks[ids[t]]] = True
+    ev = float(np.max(np.abs(vg[:, :v_ref.shape[1]][mask] - v_ref[mask])) / np.max(np.abs(v_ref[mask])))
+    assert ev <= tol, f"v max|err|/max|ref| = {ev:.3e}"
+    # rows without an adapter are untouched, bit for bit
+    none = ids < 0
+    if none.any():
+        assert torch.equal(y[torch.from_numpy(none).cuda()], case.y0[torch.from_numpy(none).cuda()])
+    return y, e
+
+
+def _small_mixed(dtype, seed=0):
+    """Several tiles, a ragged tail, ragged ranks (incl. ones not a multiple of 8 or 16)."""
+    rng = np.random.default_rng(seed)
+    parts = [rng.integers(-1, 7, size=37), np.full(130, 3), np.full(77, 6), rng.integers(0, 7, size=19)]
+    ids = np.concatenate(parts).astype(np.int32)
+    ranks = [8, 24, 5, 40, 128, 16, 64]
+    return workloads.custom(ids, ranks, 328, 200, dtype, seed=seed, name="small-mixed",
+                            scales=[2.0, 0.5, 1.0, -1.5, 2.0, 3.0, 0.25])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("y0_zero", [False, True])
+def test_forward_small_mixed(dtype, y0_zero):
+    case = GpuCase(_small_mixed(dtype), y0_zero=y0_zero)
+    _check_forward(case, TOL[dtype])
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("y0_zero", [False, True])
+def test_forward_configs_full_size(idx, y0_zero):
+    wl = _config(idx)
+    print(f"forward {wl.name} T={wl.T} y0_zero={y0_zero}", flush=True)
+    case = GpuCase(wl, y0_zero=y0_zero)
+    _check_forward(case, TOL[wl.dtype])
+
+
+def test_forward_b_zero_is_bit_exact_identity():
+    wl = _small_mixed("bf16")
+    wl.B = [np.zeros_like(b) for b in wl.B]
+    case = GpuCase(wl)
+    y, _, _ = case.forward()
+    assert torch.equal(y, case.y0)
+
+
+def test_forward_deterministic_and_linear_in_scale():
+    wl = _small_mixed("f32")
+    case = GpuCase(wl, y0_zero=True)
+    y1, _, _ = case.forward()
+    y2, _, _ = case.forward()
+    assert torch.equal(y1, y2)
+    wl2 = _small_mixed("f32")
+    wl2.scales = wl2.scales * 2
+    y3, _, _ = GpuCase(wl2, y0_zero=True).forward()
+    torch.testing.assert_close(y3, 2 * y1, rtol=1e-6, atol=1e-6)
+
+
+def test_forward_bad_table_entries_are_skipped_and_counted():
+    wl = _small_mixed("bf16")
+    case = GpuCase(wl)
+    # adapter 2: rank above r_max passed to the call -> skipped, err counted
+    y = case.y0.clone()
+    seg = lb.lora_segments_build(case.ids, wl.num_adapters)
+    v = lb.lora_shrink(case.x, case.table, seg, r_max=64)
+    lb.lora_expand_add(v, case.table, seg, y, r_max=64)
+    torch.cuda.synchronize()
+    assert int(seg.err.item()) > 0
+    rows128 = torch.from_numpy(wl.ids == 4).cuda()  # rank-128 adapter exceeds r_max=64
+    assert torch.equal(y[rows128], case.y0[rows128])
+    ok = torch.from_numpy(wl.ids == 3).cuda()
+    assert not torch.equal(y[ok], case.y0[ok])
+
+
+def test_empty_batch_is_a_no_op():
+    wl = _small_mixed("bf16")
+    case = GpuCase(wl)
+    ids = torch.zeros(0, dtype=torch.int32, device="cuda")
+    seg = lb.lora_segments_build(ids, wl.num_adapters)
+    x = case.x[:0]
+    v = lb.lora_shrink(x, case.table, seg)
+    y = case.y0[:0].clone()
+    lb.lora_expand_add(v, case.table, seg, y)
+    torch.cuda.synchronize()
+    assert v.shape[0] == 0
+
+
+# ------------------------------------------------------------------ backward
+
+def _check_backward(case, tol, v_saved=None, init=False, with_dx=True):
+    wl = case.wl
+    rng = np.random.default_rng(99)
+    dx0 = dA0 = dB0 = None
+    if init:
+        dx_init = rng.standard_normal((wl.ft_count, wl.d_in)).astype(np.float32)
+        dx0 = workloads.fp32_to_bf16_bits(dx_init) if wl.dtype == "bf16" else dx_init
+        dA0 = [rng.standard_normal(a.shape) .astype(np.float32).astype(np.float64) for a in wl.A]
+        dB0 = [rng.standard_normal(b.shape).astype(np.float32).astype(np.float64) for b in wl.B]
+    dx, dA, dB, seg_ft = case.backward(v_saved=v_saved, dx0=dx0, dA0=dA0, dB0=dB0, with_dx=with_dx)
+    dx_ref, dA_ref, dB_ref, _, _ = case.oracle_backward(dx0=dx0, dA0=dA0, dB0=dB0)
+    assert int(seg_ft.err.item()) == 0
+    errs = {}
+    if with_dx:
+        errs["dx"] = rel_err(dx, dx_ref)
+    used = sorted(set(wl.ft_ids.tolist()))
+    for a in used:
+        errs[f"dA{a}"] = rel_err(dA[a], dA_ref[a])
+        errs[f"dB{a}"] = rel_err(dB[a], dB_ref[a])
+    for a in range(wl.num_adapters):
+        if a not in used and not init:
+            assert not dA[a].any() and not dB[a].any()
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, f"backward errors above {tol}: {bad}"
+    return errs
+
+
+def _small_ft(dtype, seed=1):
+    """Fine-tuning rows of three adapters (ragged ranks), several windows and a ragged tail."""
+    rng = np.random.default_rng(seed)
+    ids = np.concatenate([np.full(70, 1), rng.integers(0, 3, size=45), np.full(150, 2)]).astype(np.int32)
+    T = ids.shape[0]
+    return workloads.custom(ids, [16, 40, 8], 264, 392, dtype, seed=seed, name="small-ft",
+                            scales=[2.0, -0.5, 1.5], ft_start=0, ft_count=T)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_small(dtype):
+    _check_backward(GpuCase(_small_ft(dtype)), TOL[dtype])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_accumulates_into_nonzero_buffers(dtype):
+    _check_backward(GpuCase(_small_ft(dtype)), TOL[dtype], init=True)
+
+
+def test_backward_without_dx_and_with_saved_v():
+    case = GpuCase(_small_ft("bf16"))
+    y, v, _ = case.forward()
+    _check_backward(case, TOL["bf16"], v_saved=v, with_dx=False)
+
+
+@pytest.mark.parametrize("idx", [1, 3, 4])
+def test_backward_configs_full_size(idx):
+    wl = _config(idx)
+    print(f"backward {wl.name} T_ft={wl.ft_count}", flush=True)
+    case = GpuCase(wl)
+    errs = _check_backward(case, TOL[wl.dtype])
+    print(errs, flush=True)
+
+
+def test_backward_config3_saved_v_matches_recompute():
+    wl = _config(3)
+    case = GpuCase(wl)
+    _, v, _ = case.forward()
+    s, n = wl.ft_start, wl.ft_count
+    _check_backward(case, TOL["bf16"], v_saved=v[s:s + n])
+
+
+def test_backward_deterministic():
+    case = GpuCase(_small_ft("bf16"))
+    a = case.backward()
+    b = case.backward()
+    assert torch.equal(a[0], b[0])
+    for x, y in zip(a[1] + a[2], b[1] + b[2]):
+        assert torch.equal(x, y)
