@@ -1,0 +1,247 @@
+"""Throughput of the multi-LoRA batched adapter path on one MI355X.
+
+One step = the whole hot path over one mixed co-serving batch (seed 0):
+  lora_segments_build (all rows) -> lora_shrink -> lora_expand_add
+  -> lora_segments_build (fine-tuning rows) -> lora_backward (dX, dA, dB),
+with the forward's v of the fine-tuning rows passed to the backward as the
+saved v.  Workload: 128 decode rows, 8 prefill segments of U[128, 1024]
+rows, 2 fine-tuning segments of 1024 rows on the reserved adapter; 32
+adapters with ranks drawn from {8, 16, 32, 64}, scale 2.0; d_in 4096 ->
+d_out 14336; bf16 elements (DeltaServe section 3.2, "Mixed forward batch").
+
+Inputs are resident in HBM before the timed region.  Consecutive steps use
+different copies of every buffer (weights included, `--sets` copies), so a
+step never finds the previous step's data in the 256 MB Infinity Cache.
+
+Prints one JSON line.  `value` = rows of the batch per second of step time.
+`roofline` is for the dominant kernel (lora_expand_add: the read-modify-write
+of y), timed with HIP events around its launch on the stream it runs on.
+`cpu_baseline` times the fp64 oracle on the host on the same batch.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--sets", type=int, default=3, help="rotating copies of every buffer")
+    ap.add_argument("--graph", action="store_true", help="replay each step from a captured HIP graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-min-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def algorithmic(wl):
+    """Minimum bytes / FLOPs of each kernel of one step (realized batch)."""
+    e = 2
+    T, d_in, d_out = wl.T, wl.d_in, wl.d_out
+    ids = wl.ids
+    ranks = wl.ranks.astype(np.int64)
+    valid = ids >= 0
+    sum_rt = int(ranks[ids[valid]].sum())            # sum over rows of r_a(t)
+    used = np.unique(ids[valid])
+    sum_ru = int(ranks[used].sum())                  # sum over used adapters of r_a
+    n_valid = int(valid.sum())
+    out = {}
+    out["segments"] = dict(bytes=4 * T + 4 * T + 4 * (2 * wl.num_adapters + 1), flops=0)
+    out["shrink"] = dict(bytes=e * n_valid * d_in + e * d_in * sum_ru + 4 * sum_rt, flops=2 * d_in * sum_rt)
+    out["expand"] = dict(bytes=4 * sum_rt + e * d_out * sum_ru + 2 * e * n_valid * d_out, flops=2 * d_out * sum_rt)
+    ft = wl.ft_ids
+    Tf = wl.ft_count
+    rft = ranks[ft].astype(np.int64)
+    uft = np.unique(ft)
+    r_u = int(ranks[uft].sum())
+    out["backward"] = dict(
+        bytes=e * Tf * d_in + e * Tf * d_out + 2 * e * Tf * d_in + e * r_u * (d_in + d_out)
+        + 8 * r_u * (d_in + d_out) + 4 * int(rft.sum()),
+        flops=4 * int(rft.sum()) * (d_in + d_out))
+    out["step"] = dict(bytes=sum(v["bytes"] for v in out.values()), flops=sum(v["flops"] for v in out.values()))
+    return out
+
+
+def cpu_baseline(wl, min_seconds):
+    """The fp64 oracle on the host: forward of every row + backward of the fine-tuning rows."""
+    import oracle
+    threads = min(16, os.cpu_count() or 1)
+    oracle.set_threads(threads)
+    ref = oracle.from_workload(wl)
+    s, n = wl.ft_start, wl.ft_count
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.forward(ref["x"], ref["ids"], ref["ranks"], ref["scales"], ref["A"], ref["B"], ref["y0"])
+        oracle.backward(ref["x"][s:s + n], ref["dy"], ref["ids"][s:s + n], ref["ranks"], ref["scales"],
+                        ref["A"], ref["B"])
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or reps >= 50:
+            break
+    return {"value": reps * wl.T / el, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"the full batch ({wl.T} rows forward + {n} fine-tuning rows backward), "
+                      f"repeated {reps}x in {el:.1f} s, fp64 plain loops, OpenMP over rows"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
+              "the multi-GPU layout is described in DESIGN.md and not built", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import expand_token_adapter_amd as lb
+    import workloads
+
+    dev = torch.device("cuda:0")
+    wl = workloads.config(3, seed=0)
+    T, s, n = wl.T, wl.ft_start, wl.ft_count
+    alg = algorithmic(wl)
+
+    def dev_bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    base = dict(A=[dev_bf16(a) for a in wl.A], B=[dev_bf16(b) for b in wl.B], x=dev_bf16(wl.x),
+                y=dev_bf16(wl.y0), dy=dev_bf16(wl.dy))
+    ids = torch.from_numpy(wl.ids).to(dev)
+    ft_ids = ids[s:s + n].contiguous()
+    r_ft = int(wl.ranks[0])
+    sets = []
+    for k in range(args.sets):
+        c = (lambda t: t) if k == 0 else (lambda t: t.clone())
+        A = [c(a) for a in base["A"]]
+        B = [c(b) for b in base["B"]]
+        st = dict(A=A, B=B, table=lb.AdapterTable(A, B, wl.scales.tolist()), x=c(base["x"]), y=c(base["y"]),
+                  dy=c(base["dy"]), ids=ids.clone(), ft_ids=ft_ids.clone())
+        st["dx"] = torch.zeros((n, wl.d_in), dtype=torch.bfloat16, device=dev)
+        st["v"] = torch.zeros((T, (st["table"].r_max + 3) // 4 * 4), dtype=torch.float32, device=dev)
+        st["dA"] = [torch.zeros(a.shape, dtype=torch.float32, device=dev) for a in A]
+        st["dB"] = [torch.zeros(b.shape, dtype=torch.float32, device=dev) for b in B]
+        st["grads"] = lb.GradTable(st["dA"], st["dB"])
+        st["seg"] = lb.Segments(T, wl.num_adapters, dev)
+        st["seg_ft"] = lb.Segments(n, wl.num_adapters, dev)
+        st["ws"] = torch.empty(lb.lora_backward_workspace_bytes(n, st["table"].r_max), dtype=torch.uint8,
+                               device=dev)
+        sets.append(st)
+    torch.cuda.synchronize()
+
+    def step(st, ev=None):
+        lb.lora_segments_build(st["ids"], wl.num_adapters, out=st["seg"])
+        lb.lora_shrink(st["x"], st["table"], st["seg"], v=st["v"])
+        if ev is not None:
+            ev[0].record()
+        lb.lora_expand_add(st["v"], st["table"], st["seg"], st["y"])
+        if ev is not None:
+            ev[1].record()
+        lb.lora_segments_build(st["ft_ids"], wl.num_adapters, out=st["seg_ft"])
+        lb.lora_backward(st["x"][s:s + n], st["dy"], st["table"], st["grads"], st["seg_ft"], dx=st["dx"],
+                         v_saved=st["v"][s:s + n], ws=st["ws"])
+
+    graphs = None
+    if args.graph:
+        side = torch.cuda.Stream(device=dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            for st in sets:
+                step(st)
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize()
+        graphs = []
+        for st in sets:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(st)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def run(i, ev=None):
+        if graphs is not None:
+            graphs[i % len(sets)].replay()
+        else:
+            step(sets[i % len(sets)], ev)
+
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        run(args.warmup + i, None if graphs is not None else evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / K
+
+    # Dominant kernel: average duration of lora_expand_add from events recorded
+    # right before and after its launch on the current stream.  Under graph
+    # replay the events cannot sit inside the graph, so a separate eager loop
+    # of back-to-back expand launches (same rotating buffers) is timed instead.
+    if graphs is None:
+        kern_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        kern_how = "events around each launch inside the timed steps"
+    else:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for i in range(3):
+            st = sets[i % len(sets)]
+            lb.lora_expand_add(st["v"], st["table"], st["seg"], st["y"])
+        e0.record()
+        for i in range(K):
+            st = sets[i % len(sets)]
+            lb.lora_expand_add(st["v"], st["table"], st["seg"], st["y"])
+        e1.record()
+        torch.cuda.synchronize()
+        kern_ms = e0.elapsed_time(e1) / K
+        kern_how = "events around back-to-back launches"
+    errs = [int(st["seg"].err.item()) + int(st["seg_ft"].err.item()) for st in sets]
+    if any(errs):
+        raise RuntimeError(f"device-side data errors reported: {errs}")
+
+    ex = alg["expand"]
+    achieved = ex["bytes"] / (kern_ms * 1e-3) / 1e9
+    line = {
+        "metric": "LoRA delta tokens/s + achieved HBM GB/s (or MFMA %) vs peak, mixed multi-LoRA batch",
+        "value": T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "mixed-coserve-32x-4096to14336", "rows": T, "ft_rows": n, "d_in": wl.d_in,
+                   "d_out": wl.d_out, "adapters": wl.num_adapters, "ranks": "U{8,16,32,64}",
+                   "ft_adapter_rank": r_ft, "seed": 0, "input_sets": args.sets,
+                   "launch": "graph" if graphs is not None else "eager"},
+        "step_algorithmic_GBps": alg["step"]["bytes"] / (ms * 1e-3) / 1e9,
+        "step_algorithmic_bytes": alg["step"]["bytes"],
+        "roofline": {"bound": "hbm", "kernel": "lora_expand_add (expand_kernel)", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": ex["bytes"], "avg_launch_ms": kern_ms, "timing": kern_how,
+                     "mfma_frac": ex["flops"] / (kern_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_min_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
