@@ -128,7 +128,7 @@ def main():
         st = dict(A=A, B=B, table=lb.AdapterTable(A, B, wl.scales.tolist()), x=c(base["x"]), y=c(base["y"]),
                   dy=c(base["dy"]), ids=ids.clone(), ft_ids=ft_ids.clone())
         st["dx"] = torch.zeros((n, wl.d_in), dtype=torch.bfloat16, device=dev)
-        st["v"] = torch.zeros((T, (st["table"].r_max + 3) // 4 * 4), dtype=torch.float32, device=dev)
+        st["v"] = torch.zeros((T, (st["table"].r_max + 7) // 8 * 8), dtype=torch.float32, device=dev)
         st["dA"] = [torch.zeros(a.shape, dtype=torch.float32, device=dev) for a in A]
         st["dB"] = [torch.zeros(b.shape, dtype=torch.float32, device=dev) for b in B]
         st["grads"] = lb.GradTable(st["dA"], st["dB"])

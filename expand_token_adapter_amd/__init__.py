@@ -193,7 +193,7 @@ def lora_shrink(x: torch.Tensor, adapters: AdapterTable, seg: Segments, v: Optio
     px, T, d_in, ldx = _rows(x, "x")
     r_max = adapters.r_max if r_max is None else r_max
     if v is None:
-        v = torch.zeros((T, (r_max + 3) // 4 * 4), dtype=torch.float32, device=x.device)
+        v = torch.zeros((T, (r_max + 7) // 8 * 8), dtype=torch.float32, device=x.device)
     pv, _, _, ldv = _rows(v, "v")
     st = _abi.load().lora_shrink(_dtype_code(x), px, ldx, T, d_in, adapters.ptr, len(adapters), r_max, seg.c,
                                  pv, ldv, _stream(x.device))

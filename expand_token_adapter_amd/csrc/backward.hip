@@ -131,7 +131,6 @@ extern "C" int lora_backward(int dtype, const void* x, int64_t ldx, const void* 
         ep.ldy = lddx;
         ep.N = d_in;
         ep.err = seg_ft.err;
-        ep.ncb = (d_in + 63) / 64;
         if ((rc = run_expand(dtype, true, ep, T_ft, num_adapters, r_max, st)) != LORA_OK) return rc;
     }
 
@@ -155,7 +154,7 @@ extern "C" int lora_backward(int dtype, const void* x, int64_t ldx, const void* 
     cp.d_out = d_out;
     cp.ncb_in = (d_in + 63) / 64;
     cp.ncb_out = (d_out + 63) / 64;
-    cp.rgroups = rank_groups(r_max);
+    cp.rgroups = (r_max + 16 * kContractMB - 1) / (16 * kContractMB);
     cp.err = seg_ft.err;
     const int64_t max_active = num_adapters < T_ft ? num_adapters : T_ft;
     const int64_t tasks = max_active * cp.rgroups * (cp.ncb_in + cp.ncb_out);

@@ -29,13 +29,18 @@ constexpr int kNumXcd = 8;  // MI355X: 8 accelerator dies, one L2 each
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// fp32 -> bf16, round to nearest, ties to even; NaN stays NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+// Two fp32 values -> packed bf16 pair (first value in the low half), round to
+// nearest even by the hardware conversion (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
+
+// Wait for this wave's LDS operations, then barrier the workgroup.  Global
+// loads still in flight stay in flight (unlike __syncthreads, which also
+// drains them).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // ---------------------------------------------------------------- MFMA
 
@@ -76,11 +81,8 @@ struct Frag<LORA_BF16> {
     }
     // From 8 fp32 values, rounded to bf16 (nearest even).
     __device__ __forceinline__ static Frag from_f32(const float* f) {
-        uint32_t h[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) h[i] = f32_to_bf16_bits(f[i]);
-        return Frag{u32x4_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                            h[6] | (h[7] << 16)}};
+        return Frag{u32x4_t{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                            pack_bf16x2(f[6], f[7])}};
     }
     __device__ __forceinline__ float get(int i) const {
         uint32_t w = q[i >> 1];
@@ -144,14 +146,16 @@ struct F32Operand<LORA_BF16> {
     Frag<LORA_BF16> hi, lo;
     __device__ __forceinline__ static F32Operand make(const float* f) {
         F32Operand o;
-        uint32_t h[8], l[8];
+        float r[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            h[i] = f32_to_bf16_bits(f[i]);
-            l[i] = f32_to_bf16_bits(f[i] - bf16_bits_to_f32(h[i]));
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t h = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+            o.hi.q[i] = h;
+            r[2 * i] = f[2 * i] - __uint_as_float(h << 16);
+            r[2 * i + 1] = f[2 * i + 1] - __uint_as_float(h & 0xffff0000u);
         }
-        o.hi.q = u32x4_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-        o.lo.q = u32x4_t{l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16)};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o.lo.q[i] = pack_bf16x2(r[2 * i], r[2 * i + 1]);
         return o;
     }
     // acc += W x operand   (W as the A operand, this as the B operand)
@@ -197,11 +201,19 @@ struct Elem<LORA_BF16> {
             f[2 * i + 1] = bf16_bits_to_f32(q[i] >> 16);
         }
     }
+    // 8 elements held in one 16-byte quad, as fp32.
+    __device__ __forceinline__ static void unpack8(const u32x4_t* q, float* f) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = __uint_as_float(q[0][i] << 16);
+            f[2 * i + 1] = __uint_as_float(q[0][i] & 0xffff0000u);
+        }
+    }
     // Write 8 fp32 values, each rounded once to bf16.
     __device__ __forceinline__ static void store8(void* p, const float* f) {
         u32x4_t q;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) q[i] = f32_to_bf16_bits(f[2 * i]) | (f32_to_bf16_bits(f[2 * i + 1]) << 16);
+        for (int i = 0; i < 4; ++i) q[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
         *reinterpret_cast<u32x4_t*>(p) = q;
     }
 };
@@ -218,6 +230,14 @@ struct Elem<LORA_F32> {
         for (int i = 0; i < 4; ++i) {
             f[i] = a[i];
             f[4 + i] = b[i];
+        }
+    }
+    // 8 elements held in two 16-byte quads.
+    __device__ __forceinline__ static void unpack8(const u32x4_t* q, float* f) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[i] = __uint_as_float(q[0][i]);
+            f[4 + i] = __uint_as_float(q[1][i]);
         }
     }
     __device__ __forceinline__ static void store8(void* p, const float* f) {

@@ -50,8 +50,8 @@ int run_shrink(int dtype, bool trans_w, const ShrinkParams& p, int32_t T, int32_
 int run_expand(int dtype, bool trans_w, const ExpandParams& p, int32_t T, int32_t num_adapters, int32_t r_max,
                hipStream_t st) {
     const int ks = r_max <= 32 ? 1 : (r_max <= 64 ? 2 : 4);
-    const int64_t tasks = SchedLayout::max_tiles64(T, num_adapters) * p.ncb;
-    const unsigned grid = grid_for(tasks, kExpandWaves, kMaxGrid);
+    const int64_t tasks = SchedLayout::max_tiles64(T, num_adapters) * ((p.N + kExpandCols - 1) / kExpandCols);
+    const unsigned grid = grid_for(tasks, 1, kMaxGrid);
     if (dtype == LORA_BF16)
         return trans_w ? launch_expand_t<LORA_BF16, true>(ks, p, grid, st)
                        : launch_expand_t<LORA_BF16, false>(ks, p, grid, st);
@@ -113,6 +113,5 @@ extern "C" int lora_expand_add(int dtype, const float* v, int64_t ldv, int32_t T
     p.ldy = ldy;
     p.N = d_out;
     p.err = seg.err;
-    p.ncb = (d_out + 63) / 64;
     return run_expand(dtype, false, p, T, num_adapters, r_max, static_cast<hipStream_t>(stream));
 }

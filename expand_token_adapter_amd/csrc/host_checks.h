@@ -32,7 +32,7 @@ inline int check_common(int dtype, int32_t T, int32_t num_adapters, int32_t r_ma
 }
 
 inline int check_f32_rows(const float* p, int64_t ld, int32_t r_max) {
-    if (!p || !aligned16(p) || ld < r_max || ld % 4 != 0) return LORA_ERR_INVALID_ARG;
+    if (!p || !aligned16(p) || ld < r_max || ld % 8 != 0) return LORA_ERR_INVALID_ARG;
     return LORA_OK;
 }
 

@@ -17,12 +17,16 @@ namespace lora {
 //   W(k, i) = A_a[k][i]     (A_a is [r, K]; v = A x, the "A x" of h(x) = Wx + BAx)
 //   W(k, i) = B_a[i][k]     (TRANS_W: B_a is [K, r]; g = B^T dy in the backward)
 // One workgroup = one 16-row tile x one group of up to 64 ranks.  Its eight
-// waves split K into contiguous slices; each wave runs 16x16 MFMA tiles
-// (A operand = weight rows, B operand = the tile's rows), then the eight
-// partial tiles are summed in wave order through LDS.
+// waves split K into contiguous slices of 64-wide chunks; each wave runs
+// 16x16 MFMA tiles (A operand = weight rows, B operand = the tile's rows)
+// with a two-stage register pipeline over its chunks, then the eight partial
+// tiles are summed in wave order through LDS.  With TRANS_W and bf16, each
+// chunk's weight block (64 rows of B_a, contiguous) is staged in the wave's
+// LDS region as loaded and read back transposed with ds_read_b64_tr_b16.
 
 constexpr int kShrinkWaves = 8;
 constexpr int kShrinkThreads = kShrinkWaves * kWave;
+constexpr int kWPitch = 72;  // staged weight row: up to 64 ranks + 8 elements of padding
 
 struct ShrinkParams {
     const void* x;   // rows gathered through perm
@@ -42,16 +46,155 @@ struct ShrinkParams {
     int32_t rgroups; // ceil(r_max / 64)
 };
 
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+// Four 16-bit values of one LDS column: lane i of each 16-lane group gets
+// rows row0 + 0..3 of column col0 + i, when lane 4e + c of the group passes
+// the address of (row0 + e, col0 + 4c).  (gfx950 ds_read_b64_tr_b16.)
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+    const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4_t*)((__attribute__((address_space(3))) uint16_t*)(p)));
+    return __builtin_bit_cast(uint2, v);
+}
+
+// Registers of one 64-wide K chunk in flight: the tile's rows (B operand)
+// and, for row-major weights, the weight rows (A operand); for staged
+// transposed weights, the raw 16-byte segments of the weight block.
+template <int DT>
+struct ShrinkStage {
+    Frag<DT> x[2];
+    Frag<DT> w[4][2];
+};
+template <int NSEG>
+struct ShrinkStageTr {
+    Frag<LORA_BF16> x[2];
+    u32x4_t wr[NSEG];
+};
+
+template <int DT>
+__device__ __forceinline__ void shrink_load_x(Frag<DT>* x, const char* xp, int kc, int lg, int K) {
+    constexpr int EB = Frag<DT>::kBytes;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int kk = kc * 64 + 16 * lg + 8 * h;
+        x[h] = Frag<DT>::load(xp + (int64_t)(kk < K ? kk : 0) * EB);  // past K: position 0, zeroed on use
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ void shrink_mask_x(Frag<DT>* xf, const Frag<DT>* x, int kc, int lg, int K) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) xf[h] = kc * 64 + 16 * lg + 8 * h < K ? x[h] : Frag<DT>::zero();
+}
+
+// Row-major weights W(k, i) = A_a[k][i]; or, for fp32 transposed weights,
+// element-wise loads of B_a[i][k].
 template <int DT, bool TRANS_W>
-__global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkParams p) {
+__device__ __forceinline__ void shrink_load(ShrinkStage<DT>& S, const char* xp, const char* wbase, int kc, int lg,
+                                            int lr, int K, int r, int rank0, int nmb) {
+    constexpr int EB = Frag<DT>::kBytes;
+    shrink_load_x<DT>(S.x, xp, kc, lg, K);
+    // Every M-block is loaded (ranks past r read row r - 1: finite, outputs
+    // discarded); unused blocks are skipped in shrink_compute.  Loading
+    // unconditionally keeps the stage in registers.
+    (void)nmb;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+        const int rk = min(rank0 + 16 * mb + lr, r - 1);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int kk = kc * 64 + 16 * lg + 8 * h;
+            const int kq = kk < K ? kk : 0;
+            if (TRANS_W)
+                S.w[mb][h] = Frag<DT>::load_strided(wbase + ((int64_t)kq * r + rk) * EB, r, min(8, K - kq));
+            else
+                S.w[mb][h] = Frag<DT>::load(wbase + ((int64_t)rk * K + kq) * EB);
+        }
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ void shrink_compute(const ShrinkStage<DT>& S, f32x4_t* acc, int kc, int lg, int K,
+                                               int nmb) {
+    Frag<DT> xf[2];
+    shrink_mask_x<DT>(xf, S.x, kc, lg, K);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+        if (mb < nmb)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) acc[mb] = mma(S.w[mb][h], xf[h], acc[mb]);
+}
+
+// Transposed bf16 weights: the chunk's 64 rows of B_a (ranks rank0 ..
+// rank0 + nr) are one contiguous block when nr = r, or row pieces of nr
+// ranks; lanes load 16-byte segments of it (nr a power of two, 8..64).
+template <int NSEG>
+__device__ __forceinline__ void shrink_load_tr(ShrinkStageTr<NSEG>& S, const char* xp, const char* wbase, int kc,
+                                               int lane, int K, int r, int rank0, int nr) {
+    shrink_load_x<LORA_BF16>(S.x, xp, kc, lane >> 4, K);
+    const int nseg = nr >> 3;  // a power of two: 1, 2, 4 or 8
+    const int lseg = __builtin_ctz(nseg);
+    // Segments i >= nseg repeat segment 0 of this lane (in bounds; not staged).
+#pragma unroll
+    for (int i = 0; i < NSEG; ++i) {
+        const int sg = lane + kWave * (i < nseg ? i : 0);
+        const int j = sg >> lseg;
+        const int row = kc * 64 + j < K ? kc * 64 + j : 0;
+        S.wr[i] = *reinterpret_cast<const u32x4_t*>(wbase + ((int64_t)row * r + rank0 + 8 * (sg & (nseg - 1))) * 2);
+    }
+}
+
+template <int NSEG>
+__device__ __forceinline__ void shrink_compute_tr(const ShrinkStageTr<NSEG>& S, f32x4_t* acc, uint16_t* wst, int kc,
+                                                  int lane, int K, int nr, int nmb) {
+    const int lg = lane >> 4;
+    Frag<LORA_BF16> xf[2];
+    shrink_mask_x<LORA_BF16>(xf, S.x, kc, lg, K);
+    const int nseg = nr >> 3;
+    const int lseg = __builtin_ctz(nseg);
+#pragma unroll
+    for (int i = 0; i < NSEG; ++i) {
+        if (i < nseg) {
+            const int sg = lane + kWave * i;
+            *reinterpret_cast<u32x4_t*>(wst + (sg >> lseg) * kWPitch + 8 * (sg & (nseg - 1))) = S.wr[i];
+        }
+    }
+    const int e = (lane & 15) >> 2;
+    const int c = lane & 3;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+        if (mb < nmb) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                // rows 16 lg + 8 h + 0..7 of rank column 16 mb + (lane % 16)
+                const uint16_t* base = wst + (16 * lg + 8 * h + e) * kWPitch + 16 * mb + 4 * c;
+                const uint2 a = lds_read_tr16(base);
+                const uint2 b = lds_read_tr16(base + 4 * kWPitch);
+                Frag<LORA_BF16> wf;
+                wf.q = u32x4_t{a.x, a.y, b.x, b.y};
+                acc[mb] = mma(wf, xf[h], acc[mb]);
+            }
+        }
+    }
+}
+
+template <int DT, bool TRANS_W>
+__global__ __launch_bounds__(kShrinkThreads) __attribute__((amdgpu_waves_per_eu(DT == LORA_BF16 ? 4 : 2)))
+void shrink_kernel(ShrinkParams p) {
     using F = Frag<DT>;
     constexpr int EB = F::kBytes;
-    __shared__ f32x4_t s_red[kShrinkWaves][4][kWave];
+    constexpr bool kTr = TRANS_W && DT == LORA_BF16;
+    constexpr int kRedBytes = kShrinkWaves * 4 * kWave * 16;
+    constexpr int kStageBytes = kTr ? kShrinkWaves * 64 * kWPitch * 2 : 0;
+    __shared__ __attribute__((aligned(16))) char s_mem[kRedBytes > kStageBytes ? kRedBytes : kStageBytes];
+    f32x4_t* s_red = reinterpret_cast<f32x4_t*>(s_mem);
 
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x & (kWave - 1);
     const int lr = lane & 15;  // MFMA row / column within the 16x16 tile
     const int lg = lane >> 4;  // K group of this lane
+    uint16_t* wst = reinterpret_cast<uint16_t*>(s_mem) + wave * 64 * kWPitch;  // this wave's staging rows
     const int64_t n_tasks = (int64_t)p.sched[0] * p.rgroups;
     const TaskSlice ts = xcd_slice(n_tasks, 1, 0);
     const int nkc = (p.K + 63) / 64;
@@ -70,12 +213,13 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkParams p) 
         const int r = ad.rank;
         const int rank0 = rg * 64;
         if (rank0 >= r) continue;
-        const int nmb = min(4, (r - rank0 + 15) / 16);
+        const int nr = min(64, r - rank0);
+        const int nmb = (nr + 15) / 16;
         const int pos0 = rec.y;
         const int nrows = rec.z;
 
-        const bool row_ok = lr < nrows;
-        const int64_t xrow = row_ok ? p.perm[pos0 + lr] : 0;
+        // Rows past the tile read row pos0 (finite data; their outputs are discarded).
+        const int64_t xrow = p.perm[pos0 + (lr < nrows ? lr : 0)];
         const char* xp = static_cast<const char*>(p.x) + xrow * p.ldx * EB;
         const char* wbase = static_cast<const char*>(TRANS_W ? ad.B : ad.A);
 
@@ -83,55 +227,80 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkParams p) 
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-        for (int kc = kc0; kc < kc1; ++kc) {
-            F xf[2];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int kk = kc * 64 + 16 * lg + 8 * h;
-                xf[h] = (row_ok && kk < p.K) ? F::load(xp + (int64_t)kk * EB) : F::zero();
-            }
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {
-                if (mb < nmb) {
-                    const int rk = rank0 + 16 * mb + lr;
+        // Two chunks per iteration, all of their loads issued before their
+        // MFMAs.  Transposed weights that cannot be staged in 16-byte segments
+        // (fp32, or a rank that is not a multiple of 8) take a plain
+        // one-chunk-at-a-time loop.
+        // Staged path: bf16 and the group's rank count a power of two >= 8.
+        const bool staged = kTr && nr >= 8 && (nr & (nr - 1)) == 0 && (r & 7) == 0;
+        if (TRANS_W && !staged) {
+            for (int kc = kc0; kc < kc1; ++kc) {
+                F xr[2], xf[2];
+                shrink_load_x<DT>(xr, xp, kc, lg, p.K);
+                shrink_mask_x<DT>(xf, xr, kc, lg, p.K);
+                for (int mb = 0; mb < nmb; ++mb) {
+                    const int rk = min(rank0 + 16 * mb + lr, r - 1);
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
                         const int kk = kc * 64 + 16 * lg + 8 * h;
-                        F wf = F::zero();
-                        if (rk < r && kk < p.K) {
-                            if (TRANS_W)
-                                wf = F::load_strided(wbase + ((int64_t)kk * r + rk) * EB, r, min(8, p.K - kk));
-                            else
-                                wf = F::load(wbase + ((int64_t)rk * p.K + kk) * EB);
-                        }
-                        acc[mb] = mma(wf, xf[h], acc[mb]);
+                        const int kq = kk < p.K ? kk : 0;
+                        const F wf = F::load_strided(wbase + ((int64_t)kq * r + rk) * EB, r, min(8, p.K - kq));
+                        // acc[mb] with a runtime mb: select into the four accumulators
+#pragma unroll
+                        for (int m = 0; m < 4; ++m)
+                            if (m == mb) acc[m] = mma(wf, xf[h], acc[m]);
                     }
                 }
             }
+        } else if (kTr && nr <= 32) {
+            for (int kc = kc0; kc < kc1; kc += 2) {
+                const bool two = kc + 1 < kc1;
+                ShrinkStageTr<4> S0, S1;
+                shrink_load_tr(S0, xp, wbase, kc, lane, p.K, r, rank0, nr);
+                shrink_load_tr(S1, xp, wbase, two ? kc + 1 : kc, lane, p.K, r, rank0, nr);
+                shrink_compute_tr(S0, acc, wst, kc, lane, p.K, nr, nmb);
+                if (two) shrink_compute_tr(S1, acc, wst, kc + 1, lane, p.K, nr, nmb);
+            }
+        } else if (kTr) {
+            for (int kc = kc0; kc < kc1; ++kc) {
+                ShrinkStageTr<8> S0;
+                shrink_load_tr(S0, xp, wbase, kc, lane, p.K, r, rank0, nr);
+                shrink_compute_tr(S0, acc, wst, kc, lane, p.K, nr, nmb);
+            }
+        } else {
+            for (int kc = kc0; kc < kc1; kc += 2) {
+                const bool two = kc + 1 < kc1;
+                ShrinkStage<DT> S0, S1;
+                shrink_load<DT, TRANS_W>(S0, xp, wbase, kc, lg, lr, p.K, r, rank0, nmb);
+                shrink_load<DT, TRANS_W>(S1, xp, wbase, two ? kc + 1 : kc, lg, lr, p.K, r, rank0, nmb);
+                shrink_compute<DT>(S0, acc, kc, lg, p.K, nmb);
+                if (two) shrink_compute<DT>(S1, acc, kc + 1, lg, p.K, nmb);
+            }
         }
 
+        __syncthreads();  // staging rows are reused as the reduction buffer
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) s_red[wave][mb][lane] = acc[mb];
+        for (int mb = 0; mb < 4; ++mb) s_red[(wave * 4 + mb) * kWave + lane] = acc[mb];
         __syncthreads();
         if (threadIdx.x < 4 * kWave) {
             const int mb = threadIdx.x / kWave;
             const int l = threadIdx.x & (kWave - 1);
             if (mb < nmb) {
-                f32x4_t s = s_red[0][mb][l];
+                f32x4_t sum = s_red[mb * kWave + l];
 #pragma unroll
-                for (int w = 1; w < kShrinkWaves; ++w) s += s_red[w][mb][l];
+                for (int w = 1; w < kShrinkWaves; ++w) sum += s_red[(w * 4 + mb) * kWave + l];
                 const int n = l & 15;
                 const int rk = rank0 + 16 * mb + 4 * (l >> 4);  // D rows 4*(l/16)+i
                 if (n < nrows && rk < r) {
                     const int pos = pos0 + n;
                     if (p.out) {
                         const int64_t row = p.out_by_pos ? pos : p.perm[pos];
-                        *reinterpret_cast<f32x4_t*>(p.out + row * p.ldo + rk) = s;
+                        *reinterpret_cast<f32x4_t*>(p.out + row * p.ldo + rk) = sum;
                     }
                     if (p.outT) {
 #pragma unroll
                         for (int i = 0; i < 4; ++i)
-                            if (rk + i < r) p.outT[(int64_t)(rk + i) * p.ldT + pos] = s[i];
+                            if (rk + i < r) p.outT[(int64_t)(rk + i) * p.ldT + pos] = sum[i];
                     }
                 }
             }
@@ -145,13 +314,17 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkParams p) 
 // Y[row][c] += s_a * sum_k V[row][k] * W(c, k) for the rows of one adapter:
 //   W(c, k) = B_a[c][k]     (B_a is [N, r]; y += s B v, forward)
 //   W(c, k) = A_a[k][c]     (TRANS_W: A_a is [r, N]; dX += s A^T g, backward)
-// One wave = one 64-row tile x 64 output columns.  The wave loads the
-// weight block once (A operand, KS x 32 ranks) and keeps it in registers
-// while it walks the tile in 16-row steps.  Output columns are assigned to
-// MFMA rows so that each lane ends up owning 16 consecutive columns of one
-// row: 32-byte (bf16) read-modify-write of y per lane, 128 bytes per row.
+// One workgroup = one 64-row tile x 256 output columns; each of its four
+// waves owns 64 columns and keeps that weight block (A operand, KS x 32
+// ranks) in registers.  The fp32 V rows of the tile are converted once per
+// workgroup into MFMA B-operand fragments in LDS (bf16: hi = bf16(v),
+// lo = bf16(v - hi)).  Every wave issues all of its y loads for the tile up
+// front, then runs the tile in 16-row steps.  Output columns are assigned to
+// MFMA rows so that each lane owns 16 consecutive columns of one row: 32-byte
+// (bf16) read-modify-write per lane, 128 contiguous bytes per row and wave.
 
 constexpr int kExpandWaves = 4;
+constexpr int kExpandCols = kExpandWaves * 64;
 
 struct ExpandParams {
     const float* v;  // [row][ldv]; row = original row, or sorted position if v_by_pos
@@ -166,7 +339,6 @@ struct ExpandParams {
     int64_t ldy;
     int32_t N;       // output columns (d_out, or d_in for dX)
     int32_t* err;
-    int32_t ncb;     // column blocks of 64
 };
 
 // Output column of MFMA row m in column block mb (0..3) of a 64-column block.
@@ -176,118 +348,196 @@ template <int DT, bool TRANS_W, int KS>
 __global__ __launch_bounds__(kExpandWaves * kWave) void expand_kernel(ExpandParams p) {
     using F = Frag<DT>;
     using E = Elem<DT>;
+    using O = F32Operand<DT>;
     constexpr int EB = F::kBytes;
+    constexpr int YQ = EB;  // 16-byte quads per lane per 16-row step (16 columns)
+    constexpr int kThreads = kExpandWaves * kWave;
+    constexpr int kFragPerThread = 4 * KS * kWave / kThreads;  // = KS
+    static_assert(sizeof(O) == 32, "fragment pair is two quads");
+    __shared__ u32x4_t s_frag[4 * KS * kWave * 2];
+
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x & (kWave - 1);
     const int lr = lane & 15;
     const int lg = lane >> 4;
-    const int64_t n_tasks = (int64_t)p.sched[1] * p.ncb;
-    const TaskSlice ts = xcd_slice(n_tasks, kExpandWaves, wave);
+    const int ncg = (p.N + kExpandCols - 1) / kExpandCols;
+    const int64_t n_tasks = (int64_t)p.sched[1] * ncg;
+    const TaskSlice ts = xcd_slice(n_tasks, 1, 0);
+    const char* ybase = static_cast<const char*>(p.y);
 
     for (int64_t task = ts.begin; task < ts.end; task += ts.stride) {
-        const int tile = (int)(task / p.ncb);
-        const int cb = (int)(task % p.ncb);
+        const int tile = (int)(task / ncg);
+        const int cg = (int)(task % ncg);
         const int4 rec = *reinterpret_cast<const int4*>(p.sched + p.tiles64_off + 4 * (int64_t)tile);
         const lora_adapter ad = p.adapters[rec.x];
         if (!adapter_ok(ad, p.r_max)) {
-            if (cb == 0 && lane == 0) atomicAdd(p.err, 1);
+            if (cg == 0 && threadIdx.x == 0) atomicAdd(p.err, 1);
             continue;
         }
         const int r = ad.rank;
         const float s = ad.scale;
-        const int c0 = cb * 64;
         const int pos0 = rec.y;
         const int nrows = rec.z;
+        const int nsub = (nrows + 15) >> 4;
+        const int c0 = cg * kExpandCols + wave * 64;
+        const bool cols_ok = c0 < p.N;
 
-        // Weight block: wf[mb][ks] holds W(col(mb, lr), 32 ks + 8 lg + 0..7).
+        // Row indices first (one round trip), for the y rows of this lane and
+        // for the V rows whose fragments this thread converts.
+        int64_t yrow[4];
+        bool yok[4];
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            yok[st] = cols_ok && 16 * st + lr < nrows;
+            yrow[st] = p.perm[yok[st] ? pos0 + 16 * st + lr : pos0];
+        }
+        int64_t vrow[kFragPerThread];
+        bool vok[kFragPerThread];
+#pragma unroll
+        for (int i = 0; i < kFragPerThread; ++i) {
+            const int f = threadIdx.x + kThreads * i;
+            const int row = 16 * (f / (KS * kWave)) + (f & 15);
+            vok[i] = row < nrows;
+            const int pos = pos0 + (vok[i] ? row : 0);
+            vrow[i] = p.v_by_pos ? pos : p.perm[pos];
+        }
+
+        // V rows first: the fragment conversion waits for them while the weight
+        // and y loads issued after them stay in flight.
+        // (The pitch of V is a multiple of 8 and >= r_max, so 8 values from any
+        // rank group that starts below r stay inside the row.)
+        f32x4_t vq[kFragPerThread][2];
+#pragma unroll
+        for (int i = 0; i < kFragPerThread; ++i) {
+            const int f = threadIdx.x + kThreads * i;
+            const int kk = 32 * ((f / kWave) % KS) + 8 * ((f >> 4) & 3);
+            const bool ld = vok[i] && kk < r;
+            const f32x4_t* src = reinterpret_cast<const f32x4_t*>(p.v + (ld ? vrow[i] * p.ldv + kk : 0));
+            vq[i][0] = src[0];
+            vq[i][1] = src[1];
+        }
+        // 1. Weight block: wf[mb][ks] holds W(c0 + expand_col(mb, lr), 32 ks + 8 lg + 0..7).
         F wf[4][KS];
         const char* wbase = static_cast<const char*>(TRANS_W ? ad.A : ad.B);
-        const bool vec_w = !TRANS_W && (r & 7) == 0;
+        if (!TRANS_W && (r & 7) == 0) {
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-            const int col = c0 + expand_col(mb, lr);
+            for (int mb = 0; mb < 4; ++mb) {
+                const int col = c0 + expand_col(mb, lr);
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int kk = 32 * ks + 8 * lg;
-                const int nval = min(8, r - kk);
-                F w = F::zero();
-                if (col < p.N && nval > 0) {
-                    if (TRANS_W)
-                        w = F::load_strided(wbase + ((int64_t)kk * p.N + col) * EB, p.N, nval);
-                    else if (vec_w && nval == 8)
-                        w = F::load(wbase + ((int64_t)col * r + kk) * EB);
-                    else
-                        w = F::load_strided(wbase + ((int64_t)col * r + kk) * EB, 1, nval);
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int kk = 32 * ks + 8 * lg;
+                    const bool ok = col < p.N && kk < r;
+                    const F w = F::load(wbase + (ok ? (int64_t)col * r + kk : 0) * EB);
+                    wf[mb][ks] = ok ? w : F::zero();
                 }
-                wf[mb][ks] = w;
+            }
+        } else {
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) {
+                const int col = c0 + expand_col(mb, lr);
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int kk = 32 * ks + 8 * lg;
+                    const int nval = (col < p.N) ? max(0, min(8, r - kk)) : 0;
+                    if (TRANS_W)
+                        wf[mb][ks] = F::load_strided(wbase + ((int64_t)(nval ? kk : 0) * p.N + (nval ? col : 0)) * EB,
+                                                     p.N, nval);
+                    else
+                        wf[mb][ks] = F::load_strided(wbase + (nval ? (int64_t)col * r + kk : 0) * EB, 1, nval);
+                }
             }
         }
 
-        for (int st = 0; st * 16 < nrows; ++st) {
-            const bool row_ok = st * 16 + lr < nrows;
-            const int pos = pos0 + st * 16 + lr;
-            const int64_t t = row_ok ? p.perm[pos] : 0;
-            const int64_t vrow = p.v_by_pos ? pos : t;
-            const float* vp = p.v + vrow * p.ldv;
-
-            f32x4_t acc[4];
+        // 2. All y loads of this wave for the tile: row 16 st + lr, columns c0 + 16 lg + 0..15.
+        u32x4_t yq[4][YQ];
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int st = 0; st < 4; ++st) {
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int kk = 32 * ks + 8 * lg;
-                float f[8];
-                if (row_ok && kk + 8 <= r) {
-                    const f32x4_t a = *reinterpret_cast<const f32x4_t*>(vp + kk);
-                    const f32x4_t b = *reinterpret_cast<const f32x4_t*>(vp + kk + 4);
+            for (int h = 0; h < 2; ++h) {
+                const int col = c0 + 16 * lg + 8 * h;
+                const bool ok = yok[st] && col < p.N;
+                const u32x4_t* src =
+                    reinterpret_cast<const u32x4_t*>(ybase + (ok ? yrow[st] * p.ldy + col : 0) * EB);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        f[e] = a[e];
-                        f[4 + e] = b[e];
-                    }
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) f[e] = (row_ok && kk + e < r) ? vp[kk + e] : 0.f;
-                }
-                const F32Operand<DT> vo = F32Operand<DT>::make(f);
-#pragma unroll
-                for (int mb = 0; mb < 4; ++mb) acc[mb] = vo.mma_right(wf[mb][ks], acc[mb]);
+                for (int q = 0; q < YQ / 2; ++q) yq[st][h * (YQ / 2) + q] = src[q];
             }
+        }
 
-            if (row_ok) {
-                char* yp = static_cast<char*>(p.y) + (t * p.ldy + c0 + 16 * lg) * EB;
+        // 3. V fragments of the tile -> LDS (once per workgroup).
+#pragma unroll
+        for (int i = 0; i < kFragPerThread; ++i) {
+            const int f = threadIdx.x + kThreads * i;
+            const int kk = 32 * ((f / kWave) % KS) + 8 * ((f >> 4) & 3);
+            float fv[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                fv[e] = (vok[i] && kk + e < r) ? vq[i][0][e] : 0.f;
+                fv[4 + e] = (vok[i] && kk + 4 + e < r) ? vq[i][1][e] : 0.f;
+            }
+            const O o = O::make(fv);
+            const u32x4_t* oq = reinterpret_cast<const u32x4_t*>(&o);
+            s_frag[2 * f] = oq[0];
+            s_frag[2 * f + 1] = oq[1];
+        }
+        lds_barrier();
+
+        // 4. MFMA and epilogue, 16 rows at a time.
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            if (st < nsub) {
+                f32x4_t acc[4];
+#pragma unroll
+                for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int f = (st * KS + ks) * kWave + lane;
+                    O o;
+                    u32x4_t* oq = reinterpret_cast<u32x4_t*>(&o);
+                    oq[0] = s_frag[2 * f];
+                    oq[1] = s_frag[2 * f + 1];
+#pragma unroll
+                    for (int mb = 0; mb < 4; ++mb) acc[mb] = o.mma_right(wf[mb][ks], acc[mb]);
+                }
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    if (c0 + 16 * lg + 8 * h < p.N) {
+                    const int col = c0 + 16 * lg + 8 * h;
+                    if (yok[st] && col < p.N) {
                         float yv[8];
-                        E::load8(yp + 8 * h * EB, yv);
+                        E::unpack8(&yq[st][h * (YQ / 2)], yv);
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
                             const int j = 8 * h + e;  // column offset 4 mb + i
                             yv[e] = yv[e] + s * acc[j >> 2][j & 3];
                         }
-                        E::store8(yp + 8 * h * EB, yv);
+                        E::store8(static_cast<char*>(p.y) + (yrow[st] * p.ldy + col) * EB, yv);
                     }
                 }
             }
         }
+        lds_barrier();
     }
 }
 
 // ============================================================== token contraction
 //
-// For each adapter a with fine-tuning rows and each block of 64 columns:
+// For each adapter a with fine-tuning rows, each group of 32 ranks and each
+// block of 64 columns:
 //   dA_a[k][c] += s_a * sum_rows g[row][k] * x[row][c]      (c < d_in)
 //   dB_a[c][k] += s_a * sum_rows dy[row][c] * v[row][k]     (c < d_out)
-// The contraction runs over rows, so the row-major x / dy tiles are
-// transposed through LDS (per wave, 32 rows x 64 columns) into MFMA B
-// operands; g and v come pre-transposed ([k][sorted position]) from the
-// shrink kernel.  Four waves split the adapter's rows into contiguous
-// ranges; their partial tiles are summed in wave order through LDS and
-// added to dA / dB, which no other workgroup touches.
+// The contraction runs over rows, so the row-major x / dy tiles (32 rows x
+// 64 columns per wave and step) become MFMA B operands through LDS: bf16
+// tiles are stored as loaded and read back transposed with
+// ds_read_b64_tr_b16; fp32 tiles are written transposed element by element.
+// g and v come rank-major ([k][sorted position]) from the shrink kernel.
+// Four waves split the adapter's rows into contiguous ranges, two 32-row
+// windows per iteration with all loads issued first; their partial tiles
+// are summed in wave order through LDS and added to dA / dB, which no other
+// workgroup touches.
 
 constexpr int kContractWaves = 4;
-constexpr int kCtPitch = 32 + 8;  // LDS row pitch (elements) of a transposed column
+constexpr int kContractMB = 2;    // 16-rank blocks per task (32 ranks)
+constexpr int kCtPitch = 32 + 8;  // fp32 path: LDS pitch (elements) of a transposed column
+constexpr int kQPitch = 64 + 8;   // bf16 path: LDS pitch (elements) of a staged row
 
 struct ContractParams {
     const void* x;
@@ -306,22 +556,102 @@ struct ContractParams {
     int64_t active_off;
     int32_t d_in, d_out;
     int32_t ncb_in, ncb_out;
-    int32_t rgroups;
+    int32_t rgroups;  // ceil(r_max / 32)
     int32_t* err;
 };
 
 template <int DT>
 struct ContractLds {
     static constexpr int EB = Frag<DT>::kBytes;
-    static constexpr int kTransBytes = kContractWaves * 64 * kCtPitch * EB;
-    static constexpr int kRedBytes = kContractWaves * 16 * kWave * 16;
+    // per wave: two window tiles
+    static constexpr int kTileBytes = DT == LORA_BF16 ? 32 * kQPitch * 2 : 64 * kCtPitch * 4;
+    static constexpr int kTransBytes = kContractWaves * 2 * kTileBytes;
+    static constexpr int kRedBytes = kContractWaves * kContractMB * 4 * kWave * 16;
     static constexpr int kBytes = kTransBytes > kRedBytes ? kTransBytes : kRedBytes;
 };
+
+// Raw loads of one 32-row window: this lane's 4 rows x 8 columns of Q and,
+// per rank block, 8 positions of P.
+template <int DT>
+struct ContractWin {
+    Frag<DT> q[4];
+    f32x4_t pv[kContractMB][2];
+};
+
+template <int DT>
+__device__ __forceinline__ void contract_load(ContractWin<DT>& W, const char* q, int64_t ldq, const float* PT,
+                                              int64_t ldT, const int32_t* perm, int win, int lo, int hi, int c0,
+                                              int lcol, int lrow, int rank0, int r, int lane) {
+    constexpr int EB = Frag<DT>::kBytes;
+    int64_t rows[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int pos = win + lrow + j;
+        rows[j] = perm[pos >= lo && pos < hi ? pos : lo];  // outside the range: row lo (finite, P is zero there)
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) W.q[j] = Frag<DT>::load(q + (rows[j] * ldq + c0 + lcol) * EB);
+    const int pp = win + 8 * (lane >> 4);
+#pragma unroll
+    for (int mb = 0; mb < kContractMB; ++mb) {
+        const int rk = min(rank0 + 16 * mb + (lane & 15), r - 1);  // ranks past r: discarded rows
+        const f32x4_t* src = reinterpret_cast<const f32x4_t*>(PT + (int64_t)rk * ldT + pp);
+        W.pv[mb][0] = src[0];
+        W.pv[mb][1] = src[1];
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ void contract_compute(const ContractWin<DT>& W, char* tile, f32x4_t (*acc)[4], int win,
+                                                 int lo, int hi, int lcol, int lrow, int nmb, int lane) {
+    using F = Frag<DT>;
+    const int lr = lane & 15;
+    const int lg = lane >> 4;
+    // 1. Q tile -> LDS;  2. B operands: column 16 nb + lr, window rows 8 lg .. 8 lg + 7.
+    F qf[4];
+    if constexpr (DT == LORA_BF16) {
+        uint16_t* t = reinterpret_cast<uint16_t*>(tile);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4_t*>(t + (lrow + j) * kQPitch + lcol) = W.q[j].q;
+        const int e = lr >> 2;
+        const int c = lane & 3;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+            const uint16_t* base = t + (8 * lg + e) * kQPitch + 16 * nb + 4 * c;
+            const uint2 a = lds_read_tr16(base);
+            const uint2 b = lds_read_tr16(base + 4 * kQPitch);
+            qf[nb].q = u32x4_t{a.x, a.y, b.x, b.y};
+        }
+    } else {
+        float* t = reinterpret_cast<float*>(tile);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) t[(lcol + e) * kCtPitch + lrow + j] = W.q[j].get(e);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) qf[nb] = F::load(t + (16 * nb + lr) * kCtPitch + 8 * lg);
+    }
+    // 3. A operands from P^T (zero outside [lo, hi)), hi/lo split for bf16.
+    const int pp = win + 8 * lg;
+#pragma unroll
+    for (int mb = 0; mb < kContractMB; ++mb) {
+        if (mb < nmb) {
+            float f[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                f[e] = (pp + e >= lo && pp + e < hi) ? W.pv[mb][0][e] : 0.f;
+                f[4 + e] = (pp + 4 + e >= lo && pp + 4 + e < hi) ? W.pv[mb][1][e] : 0.f;
+            }
+            const F32Operand<DT> po = F32Operand<DT>::make(f);
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = po.mma_left(qf[nb], acc[mb][nb]);
+        }
+    }
+}
 
 template <int DT>
 __global__ __launch_bounds__(kContractWaves * kWave) void contract_kernel(ContractParams p) {
     using F = Frag<DT>;
-    constexpr int EB = F::kBytes;
     __shared__ __attribute__((aligned(16))) char s_mem[ContractLds<DT>::kBytes];
 
     const int wave = threadIdx.x / kWave;
@@ -331,7 +661,11 @@ __global__ __launch_bounds__(kContractWaves * kWave) void contract_kernel(Contra
     const int ncb = p.ncb_in + p.ncb_out;
     const int64_t n_tasks = (int64_t)p.sched[2] * p.rgroups * ncb;
     const TaskSlice ts = xcd_slice(n_tasks, 1, 0);
-    char* trans = s_mem + wave * (64 * kCtPitch * EB);  // this wave's [64 columns][kCtPitch] tile
+    char* tileA = s_mem + (2 * wave) * ContractLds<DT>::kTileBytes;
+    char* tileB = s_mem + (2 * wave + 1) * ContractLds<DT>::kTileBytes;
+    // Loader role: lane covers window rows 4*(lane/8)+j (j < 4), columns 8*(lane%8)+e (e < 8).
+    const int lrow = 4 * (lane >> 3);
+    const int lcol = 8 * (lane & 7);
 
     for (int64_t task = ts.begin; task < ts.end; task += ts.stride) {
         const int cb_all = (int)(task % ncb);
@@ -346,15 +680,17 @@ __global__ __launch_bounds__(kContractWaves * kWave) void contract_kernel(Contra
             continue;
         }
         const int r = ad.rank;
-        const int rank0 = rg * 64;
+        const int rank0 = rg * 16 * kContractMB;
         if (rank0 >= r) continue;
-        const int nmb = min(4, (r - rank0 + 15) / 16);
+        const int nmb = min(kContractMB, (r - rank0 + 15) / 16);
         const int cb = is_dA ? cb_all : cb_all - p.ncb_in;
         const int c0 = cb * 64;
         const int N = is_dA ? p.d_in : p.d_out;
         const char* q = static_cast<const char*>(is_dA ? p.x : p.dy);
         const int64_t ldq = is_dA ? p.ldx : p.lddy;
         const float* PT = is_dA ? p.gT : p.vT;
+        // Columns past N (N is a multiple of 8) read column block 0 of the row; never written back.
+        const int cq = c0 + lcol < N ? c0 : -lcol;
 
         const int lo = p.offsets[a];
         const int hi = p.offsets[a + 1];
@@ -364,87 +700,39 @@ __global__ __launch_bounds__(kContractWaves * kWave) void contract_kernel(Contra
         const int wa = w0 + 32 * (int)((int64_t)wave * nwin / kContractWaves);
         const int wb = w0 + 32 * (int)((int64_t)(wave + 1) * nwin / kContractWaves);
 
-        f32x4_t acc[4][4];
+        f32x4_t acc[kContractMB][4];
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
+        for (int mb = 0; mb < kContractMB; ++mb)
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-        // Loader role: lane covers positions 4*(lane/8)+j (j < 4), columns 8*(lane%8)+e (e < 8).
-        const int lrow = 4 * (lane >> 3);
-        const int lcol = 8 * (lane & 7);
-        for (int win = wa; win < wb; win += 32) {
-            // 1. Q tile -> LDS, transposed to [column][position].
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int pos = win + lrow + j;
-                const bool ok = pos >= lo && pos < hi && c0 + lcol < N;
-                F f = F::zero();
-                if (ok) {
-                    const int64_t row = p.perm[pos];
-                    f = F::load(q + (row * ldq + c0 + lcol) * EB);
-                }
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    char* dst = trans + ((lcol + e) * kCtPitch + lrow + j) * EB;
-                    if constexpr (EB == 2)
-                        *reinterpret_cast<uint16_t*>(dst) = (uint16_t)f.raw(e);
-                    else
-                        *reinterpret_cast<uint32_t*>(dst) = f.raw(e);
-                }
-            }
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            // 2. B operands: column 16 nb + lr, positions 8 lg .. 8 lg + 7.
-            F qf[4];
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb) qf[nb] = F::load(trans + ((16 * nb + lr) * kCtPitch + 8 * lg) * EB);
-            // 3. A operands from P^T: rank rank0 + 16 mb + lr, same positions.
-            const int pp = win + 8 * lg;
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {
-                if (mb < nmb) {
-                    const int rk = rank0 + 16 * mb + lr;
-                    float f[8];
-                    if (rk < r) {
-                        const float* src = PT + (int64_t)rk * p.ldT + pp;
-                        const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(src);
-                        const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(src + 4);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            f[e] = (pp + e >= lo && pp + e < hi) ? a0[e] : 0.f;
-                            f[4 + e] = (pp + 4 + e >= lo && pp + 4 + e < hi) ? a1[e] : 0.f;
-                        }
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) f[e] = 0.f;
-                    }
-                    const F32Operand<DT> po = F32Operand<DT>::make(f);
-#pragma unroll
-                    for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = po.mma_left(qf[nb], acc[mb][nb]);
-                }
-            }
-            __builtin_amdgcn_wave_barrier();
+        for (int win = wa; win < wb; win += 64) {
+            const bool two = win + 32 < wb;
+            ContractWin<DT> W0, W1;
+            contract_load<DT>(W0, q, ldq, PT, p.ldT, p.perm, win, lo, hi, cq, lcol, lrow, rank0, r, lane);
+            contract_load<DT>(W1, q, ldq, PT, p.ldT, p.perm, two ? win + 32 : win, lo, hi, cq, lcol, lrow, rank0,
+                              r, lane);
+            contract_compute<DT>(W0, tileA, acc, win, lo, hi, lcol, lrow, nmb, lane);
+            if (two) contract_compute<DT>(W1, tileB, acc, win + 32, lo, hi, lcol, lrow, nmb, lane);
         }
 
         // Fixed-order sum of the four waves' tiles.
         __syncthreads();
         f32x4_t* red = reinterpret_cast<f32x4_t*>(s_mem);
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
+        for (int mb = 0; mb < kContractMB; ++mb)
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb) red[((wave * 4 + mb) * 4 + nb) * kWave + lane] = acc[mb][nb];
+            for (int nb = 0; nb < 4; ++nb) red[((wave * kContractMB + mb) * 4 + nb) * kWave + lane] = acc[mb][nb];
         __syncthreads();
         {
             const int nb = wave;  // this wave finishes column block nb
             const float s = ad.scale;
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {
+            for (int mb = 0; mb < kContractMB; ++mb) {
                 if (mb < nmb) {
-                    f32x4_t sum = red[((0 * 4 + mb) * 4 + nb) * kWave + lane];
+                    f32x4_t sum = red[(mb * 4 + nb) * kWave + lane];
 #pragma unroll
-                    for (int w = 1; w < kContractWaves; ++w) sum += red[((w * 4 + mb) * 4 + nb) * kWave + lane];
+                    for (int w = 1; w < kContractWaves; ++w) sum += red[((w * kContractMB + mb) * 4 + nb) * kWave + lane];
                     const int col = c0 + 16 * nb + lr;
                     if (col < N) {
 #pragma unroll

@@ -48,7 +48,7 @@
  *       1 <= r_max <= LORA_MAX_RANK; leading dimensions >= the row length;
  *       x, y, dY, dX, v pointers 16-byte aligned; d_in, d_out and every
  *       element-matrix pitch a multiple of 8 (else LORA_ERR_UNSUPPORTED);
- *       fp32 pitches ldv a multiple of 4 and >= r_max; workspace large enough.
+ *       fp32 pitches ldv a multiple of 8 and >= r_max; workspace large enough.
  *     T == 0 returns LORA_OK and enqueues nothing.
  *   - Data checked on the device: adapter ids outside [-1, num_adapters) and
  *     table entries with rank outside [1, r_max], a NULL or non-16-byte-aligned
@@ -157,7 +157,7 @@ int lora_segments_build(const int32_t* adapter_ids, int32_t T, int32_t num_adapt
  * adapter (the "A x" of h(x) = W x + B A x, MOLT section 2.1).
  *   x [T, ldx] (dtype), adapters [num_adapters] device table, seg from
  *   lora_segments_build over the same T rows, v [T, ldv] fp32 output
- *   (ldv >= r_max, multiple of 4).  Row t of v receives columns 0..r_a-1;
+ *   (ldv >= r_max, multiple of 8).  Row t of v receives columns 0..r_a-1;
  *   columns r_a..r_max-1 are unspecified; rows without an adapter are left
  *   unchanged.
  */

@@ -83,6 +83,7 @@ def _seg(ok=True):
     (dict(v=0), _abi.LORA_ERR_INVALID_ARG),
     (dict(ldv=6), _abi.LORA_ERR_INVALID_ARG),
     (dict(ldv=4), _abi.LORA_ERR_INVALID_ARG),
+    (dict(ldv=12, r_max=8), _abi.LORA_ERR_INVALID_ARG),
 ])
 def test_shrink_and_expand_reject_bad_arguments(lib, kw, code):
     a = dict(dtype=0, T=64, A=4, r_max=8, adapters=FAKE, seg_ok=True, x=FAKE, ld=256, d=256, v=FAKE, ldv=8)
@@ -134,6 +135,7 @@ def test_backward_rejects(lib):
     assert call(d_out=100, lddy=100) == _abi.LORA_ERR_UNSUPPORTED
     assert call(dx=FAKE + 2) == _abi.LORA_ERR_INVALID_ARG
     assert call(vs=FAKE, ldv=4) == _abi.LORA_ERR_INVALID_ARG
+    assert call(vs=FAKE, ldv=12) == _abi.LORA_ERR_INVALID_ARG
     assert call(wsb=need - 1) == _abi.LORA_ERR_WORKSPACE
     assert call(ws=FAKE + 8) == _abi.LORA_ERR_WORKSPACE
     assert call(seg=_seg(False)) == _abi.LORA_ERR_INVALID_ARG

@@ -191,9 +191,30 @@ def _small_ft(dtype, seed=1):
                             scales=[2.0, -0.5, 1.5], ft_start=0, ft_count=T)
 
 
+def _small_ft_wide(dtype, seed=2):
+    """Ranks 64 / 128 / 32 / 24 (two rank groups, a rank that is not a power of two),
+    row lengths that leave partial 64-wide chunks."""
+    rng = np.random.default_rng(seed)
+    ids = np.concatenate([rng.integers(0, 4, size=29), np.full(97, 1), np.full(40, 3), np.full(33, 0)])
+    ids = ids.astype(np.int32)
+    T = ids.shape[0]
+    return workloads.custom(ids, [64, 128, 32, 24], 320, 136, dtype, seed=seed, name="small-ft-wide",
+                            scales=[2.0, 0.75, -1.0, 1.25], ft_start=0, ft_count=T)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_backward_small(dtype):
     _check_backward(GpuCase(_small_ft(dtype)), TOL[dtype])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_wide_ranks(dtype):
+    _check_backward(GpuCase(_small_ft_wide(dtype)), TOL[dtype])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_forward_wide_ranks(dtype):
+    _check_forward(GpuCase(_small_ft_wide(dtype)), TOL[dtype])
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
