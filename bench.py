@@ -44,7 +44,31 @@ def parse():
     ap.add_argument("--graph", action="store_true", help="replay each step from a captured HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-min-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only time a plain device copy of 256 MiB (reference for counter scaling)")
     return ap.parse_args()
+
+
+def copy_calibration(reps: int = 20):
+    """A plain device-to-device copy of a known size: the achievable copy rate on
+    this GPU, and the per-dispatch reference for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    n = 256 << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    c = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        (b if i % 2 == 0 else c).copy_(a if i % 2 == 0 else b)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copy_ms": ms,
+                      "copy_GBps_read_plus_write": 2 * n / (ms * 1e-3) / 1e9}), flush=True)
 
 
 def algorithmic(wl):
@@ -103,6 +127,9 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
               "the multi-GPU layout is described in DESIGN.md and not built", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import torch
     import expand_token_adapter_amd as lb
     import workloads
@@ -134,14 +161,16 @@ def main():
         st["grads"] = lb.GradTable(st["dA"], st["dB"])
         st["seg"] = lb.Segments(T, wl.num_adapters, dev)
         st["seg_ft"] = lb.Segments(n, wl.num_adapters, dev)
-        st["ws"] = torch.empty(lb.lora_backward_workspace_bytes(n, st["table"].r_max), dtype=torch.uint8,
-                               device=dev)
+        st["ws"] = torch.empty(lb.lora_backward_workspace_bytes(n, wl.d_in, wl.d_out, st["table"].r_max),
+                               dtype=torch.uint8, device=dev)
+        st["ws_shrink"] = torch.empty(lb.lora_shrink_workspace_bytes(T, wl.d_in, st["table"].r_max),
+                                      dtype=torch.uint8, device=dev)
         sets.append(st)
     torch.cuda.synchronize()
 
     def step(st, ev=None):
         lb.lora_segments_build(st["ids"], wl.num_adapters, out=st["seg"])
-        lb.lora_shrink(st["x"], st["table"], st["seg"], v=st["v"])
+        lb.lora_shrink(st["x"], st["table"], st["seg"], v=st["v"], ws=st["ws_shrink"])
         if ev is not None:
             ev[0].record()
         lb.lora_expand_add(st["v"], st["table"], st["seg"], st["y"])

@@ -25,7 +25,8 @@ __all__ = [
     "AdapterTable", "GradTable", "Segments", "LoraError",
     "lora_segments_build", "lora_shrink", "lora_expand_add", "lora_backward",
     "lora_abi_version", "lora_status_string",
-    "lora_segments_workspace_bytes", "lora_backward_workspace_bytes", "lora_segments_sched_elems",
+    "lora_segments_workspace_bytes", "lora_shrink_workspace_bytes", "lora_backward_workspace_bytes",
+    "lora_segments_sched_elems",
 ]
 
 _DTYPES = {torch.bfloat16: LORA_BF16, torch.float32: LORA_F32}
@@ -66,8 +67,12 @@ def lora_segments_workspace_bytes(T: int, num_adapters: int) -> int:
     return _abi.load().lora_segments_workspace_bytes(T, num_adapters)
 
 
-def lora_backward_workspace_bytes(T_ft: int, r_max: int) -> int:
-    return _abi.load().lora_backward_workspace_bytes(T_ft, r_max)
+def lora_shrink_workspace_bytes(T: int, d_in: int, r_max: int) -> int:
+    return _abi.load().lora_shrink_workspace_bytes(T, d_in, r_max)
+
+
+def lora_backward_workspace_bytes(T_ft: int, d_in: int, d_out: int, r_max: int) -> int:
+    return _abi.load().lora_backward_workspace_bytes(T_ft, d_in, d_out, r_max)
 
 
 def lora_segments_sched_elems(T: int, num_adapters: int) -> int:
@@ -187,7 +192,7 @@ def lora_segments_build(adapter_ids: torch.Tensor, num_adapters: int, out: Optio
 
 
 def lora_shrink(x: torch.Tensor, adapters: AdapterTable, seg: Segments, v: Optional[torch.Tensor] = None,
-                r_max: Optional[int] = None) -> torch.Tensor:
+                r_max: Optional[int] = None, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     """v[t, :r_a] = A_a x_t (fp32) for every row with an adapter; returns v [T, r_max]."""
     _on_gpu(x)
     px, T, d_in, ldx = _rows(x, "x")
@@ -195,8 +200,12 @@ def lora_shrink(x: torch.Tensor, adapters: AdapterTable, seg: Segments, v: Optio
     if v is None:
         v = torch.zeros((T, (r_max + 7) // 8 * 8), dtype=torch.float32, device=x.device)
     pv, _, _, ldv = _rows(v, "v")
-    st = _abi.load().lora_shrink(_dtype_code(x), px, ldx, T, d_in, adapters.ptr, len(adapters), r_max, seg.c,
-                                 pv, ldv, _stream(x.device))
+    lib = _abi.load()
+    need = lib.lora_shrink_workspace_bytes(T, d_in, r_max)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    st = lib.lora_shrink(_dtype_code(x), px, ldx, T, d_in, adapters.ptr, len(adapters), r_max, seg.c,
+                         pv, ldv, ws.data_ptr(), ws.numel(), _stream(x.device))
     _abi.check("lora_shrink", st)
     return v
 
@@ -237,7 +246,7 @@ def lora_backward(x: torch.Tensor, dy: torch.Tensor, adapters: AdapterTable, gra
         raise ValueError("the gradient table must have one entry per adapter")
     r_max = adapters.r_max if r_max is None else r_max
     lib = _abi.load()
-    need = lib.lora_backward_workspace_bytes(T, r_max)
+    need = lib.lora_backward_workspace_bytes(T, d_in, d_out, r_max)
     if ws is None or ws.numel() < need:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     st = lib.lora_backward(_dtype_code(x), px, ldx, pdy, lddy, pdx or None, lddx, T, d_in, d_out, adapters.ptr,

@@ -9,28 +9,38 @@
 //   dA += s sum g x^T, dB += s sum dy v^T   token-contraction kernel
 // Four launches; the workspace holds g (by sorted position, row- and
 // rank-major) and v (rank-major).
+#include <algorithm>
+
 #include "host_checks.h"
 #include "lora_kernels.h"
 
 using namespace lora;
 
 namespace lora {
-int run_shrink(int dtype, bool trans_w, const ShrinkParams& p, int32_t T, int32_t num_adapters, hipStream_t st);
+int run_shrink(int dtype, bool trans_w, const ShrinkParams& p, const ReduceParams& rp, int32_t T, int32_t num_adapters,
+               hipStream_t st);
+int64_t shrink_part_ld(int32_t r_max);
+int64_t shrink_part_floats(int32_t T, int32_t K, int32_t r_max);
 int run_expand(int dtype, bool trans_w, const ExpandParams& p, int32_t T, int32_t num_adapters, int32_t r_max,
                hipStream_t st);
 
-// Workspace layout of lora_backward (fp32 elements).
+// Workspace layout of lora_backward (fp32 elements): g by sorted position
+// (row-major and rank-major), v rank-major, and the split-K partials of the
+// shrinks (reused by the g and v passes, which run one after the other).
 struct BwdWs {
-    int64_t ldg, ldT;         // pitch of g rows; pitch of the rank-major arrays
-    int64_t g, gT, vT, total; // offsets
-    static BwdWs make(int64_t T, int64_t r_max) {
+    int64_t ldg, ldT;               // pitch of g rows; pitch of the rank-major arrays
+    int64_t g, gT, vT, part, total; // offsets
+    static BwdWs make(int64_t T, int64_t d_in, int64_t d_out, int64_t r_max) {
         BwdWs w;
         w.ldg = round_up(r_max, 8);
         w.ldT = round_up(T > 0 ? T : 1, 32);
         w.g = 0;
         w.gT = round_up(w.g + T * w.ldg, 64);
         w.vT = round_up(w.gT + r_max * w.ldT, 64);
-        w.total = round_up(w.vT + r_max * w.ldT, 64);
+        w.part = round_up(w.vT + r_max * w.ldT, 64);
+        const int64_t np = std::max(shrink_part_floats((int32_t)T, (int32_t)d_in, (int32_t)r_max),
+                                    shrink_part_floats((int32_t)T, (int32_t)d_out, (int32_t)r_max));
+        w.total = round_up(w.part + np, 64);
         return w;
     }
 };
@@ -52,9 +62,9 @@ __global__ void transpose_v_kernel(const float* __restrict__ v, int64_t ldv, con
 }
 }  // namespace
 
-extern "C" size_t lora_backward_workspace_bytes(int32_t T_ft, int32_t r_max) {
-    if (T_ft < 0 || r_max < 1 || r_max > LORA_MAX_RANK) return 0;
-    return (size_t)BwdWs::make(T_ft, r_max).total * sizeof(float);
+extern "C" size_t lora_backward_workspace_bytes(int32_t T_ft, int32_t d_in, int32_t d_out, int32_t r_max) {
+    if (T_ft < 0 || d_in < 1 || d_out < 1 || r_max < 1 || r_max > LORA_MAX_RANK) return 0;
+    return (size_t)BwdWs::make(T_ft, d_in, d_out, r_max).total * sizeof(float);
 }
 
 extern "C" int lora_backward(int dtype, const void* x, int64_t ldx, const void* dy, int64_t lddy, void* dx,
@@ -71,7 +81,7 @@ extern "C" int lora_backward(int dtype, const void* x, int64_t ldx, const void* 
     if (dx && (rc = check_matrix(dx, d_in, lddx)) != LORA_OK) return rc;
     if (v_saved && (rc = check_f32_rows(v_saved, ldv, r_max)) != LORA_OK) return rc;
     if (!seg_ft.offsets) return LORA_ERR_INVALID_ARG;
-    const BwdWs w = BwdWs::make(T_ft, r_max);
+    const BwdWs w = BwdWs::make(T_ft, d_in, d_out, r_max);
     if (!ws || !aligned16(ws) || ws_bytes < (size_t)w.total * sizeof(float)) return LORA_ERR_WORKSPACE;
 
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -90,15 +100,29 @@ extern "C" int lora_backward(int dtype, const void* x, int64_t ldx, const void* 
     sp.r_max = r_max;
     sp.perm = seg_ft.perm;
     sp.sched = seg_ft.sched;
-    sp.tiles16_off = sl.tiles16;
-    sp.out = g;
-    sp.ldo = w.ldg;
-    sp.out_by_pos = 1;
-    sp.outT = gT;
-    sp.ldT = w.ldT;
+    sp.tiles64_off = sl.tiles64;
+    sp.part = wsf + w.part;
+    sp.ldp = shrink_part_ld(r_max);
+    sp.slice_stride = (int64_t)T_ft * sp.ldp;
+    sp.nslices = shrink_slices(d_out);
     sp.err = seg_ft.err;
     sp.rgroups = rank_groups(r_max);
-    if ((rc = run_shrink(dtype, true, sp, T_ft, num_adapters, st)) != LORA_OK) return rc;
+    ReduceParams rp{};
+    rp.part = sp.part;
+    rp.ldp = sp.ldp;
+    rp.slice_stride = sp.slice_stride;
+    rp.nslices = sp.nslices;
+    rp.adapters = adapters;
+    rp.r_max = r_max;
+    rp.perm = seg_ft.perm;
+    rp.sched = seg_ft.sched;
+    rp.tiles16_off = sl.tiles16;
+    rp.out = g;
+    rp.ldo = w.ldg;
+    rp.out_by_pos = 1;
+    rp.outT = gT;
+    rp.ldT = w.ldT;
+    if ((rc = run_shrink(dtype, true, sp, rp, T_ft, num_adapters, st)) != LORA_OK) return rc;
 
     // 2. v = A x, rank-major by sorted position.
     if (v_saved) {
@@ -111,9 +135,12 @@ extern "C" int lora_backward(int dtype, const void* x, int64_t ldx, const void* 
         vp.x = x;
         vp.ldx = ldx;
         vp.K = d_in;
-        vp.out = nullptr;
-        vp.outT = vT;
-        if ((rc = run_shrink(dtype, false, vp, T_ft, num_adapters, st)) != LORA_OK) return rc;
+        vp.nslices = shrink_slices(d_in);
+        ReduceParams vr = rp;
+        vr.nslices = vp.nslices;
+        vr.out = nullptr;
+        vr.outT = vT;
+        if ((rc = run_shrink(dtype, false, vp, vr, T_ft, num_adapters, st)) != LORA_OK) return rc;
     }
 
     // 3. dX += s A^T g.

@@ -22,6 +22,20 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
+// Pointers into device memory that the compiler cannot prove global (e.g.
+// the adapter weights, read from the device-resident table) would otherwise
+// be accessed with FLAT instructions; gptr() casts them to the global
+// address space so loads and stores are global_* instructions.
+#define LORA_GLOBAL __attribute__((address_space(1)))
+template <typename T>
+__device__ __forceinline__ const LORA_GLOBAL T* gptr(const T* p) {
+    return (const LORA_GLOBAL T*)(p);
+}
+template <typename T>
+__device__ __forceinline__ LORA_GLOBAL T* gptr(T* p) {
+    return (LORA_GLOBAL T*)(p);
+}
+
 constexpr int kWave = 64;
 constexpr int kNumXcd = 8;  // MI355X: 8 accelerator dies, one L2 each
 
@@ -66,13 +80,17 @@ struct Frag<LORA_BF16> {
     u32x4_t q;
     static constexpr int kBytes = 2;
     __device__ __forceinline__ static Frag zero() { return Frag{u32x4_t{0, 0, 0, 0}}; }
-    // 8 elements at p (16-byte aligned).
+    // 8 elements at p in device memory (16-byte aligned).
     __device__ __forceinline__ static Frag load(const void* p) {
+        return Frag{*gptr(reinterpret_cast<const u32x4_t*>(p))};
+    }
+    // 8 elements at p in LDS.
+    __device__ __forceinline__ static Frag load_lds(const void* p) {
         return Frag{*reinterpret_cast<const u32x4_t*>(p)};
     }
-    // Elements p[i * stride] for i < n (n <= 8), zeros after.
+    // Elements p[i * stride] (device memory) for i < n (n <= 8), zeros after.
     __device__ __forceinline__ static Frag load_strided(const void* p, int64_t stride, int n) {
-        const uint16_t* s = reinterpret_cast<const uint16_t*>(p);
+        const LORA_GLOBAL uint16_t* s = gptr(reinterpret_cast<const uint16_t*>(p));
         uint32_t h[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) h[i] = (i < n) ? (uint32_t)s[i * stride] : 0u;
@@ -100,11 +118,15 @@ struct Frag<LORA_F32> {
         return Frag{u32x4_t{0, 0, 0, 0}, u32x4_t{0, 0, 0, 0}};
     }
     __device__ __forceinline__ static Frag load(const void* p) {
+        const LORA_GLOBAL u32x4_t* v = gptr(reinterpret_cast<const u32x4_t*>(p));
+        return Frag{v[0], v[1]};
+    }
+    __device__ __forceinline__ static Frag load_lds(const void* p) {
         const u32x4_t* v = reinterpret_cast<const u32x4_t*>(p);
         return Frag{v[0], v[1]};
     }
     __device__ __forceinline__ static Frag load_strided(const void* p, int64_t stride, int n) {
-        const uint32_t* s = reinterpret_cast<const uint32_t*>(p);
+        const LORA_GLOBAL uint32_t* s = gptr(reinterpret_cast<const uint32_t*>(p));
         uint32_t h[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) h[i] = (i < n) ? s[i * stride] : 0u;
@@ -190,11 +212,11 @@ struct Elem;
 template <>
 struct Elem<LORA_BF16> {
     __device__ __forceinline__ static float get(const void* p, int64_t i) {
-        return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p)[i]);
+        return bf16_bits_to_f32(gptr(reinterpret_cast<const uint16_t*>(p))[i]);
     }
     // Read 8 consecutive elements (16-byte aligned) as fp32.
     __device__ __forceinline__ static void load8(const void* p, float* f) {
-        u32x4_t q = *reinterpret_cast<const u32x4_t*>(p);
+        u32x4_t q = *gptr(reinterpret_cast<const u32x4_t*>(p));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             f[2 * i] = bf16_bits_to_f32(q[i] & 0xffffu);
@@ -214,17 +236,17 @@ struct Elem<LORA_BF16> {
         u32x4_t q;
 #pragma unroll
         for (int i = 0; i < 4; ++i) q[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
-        *reinterpret_cast<u32x4_t*>(p) = q;
+        *gptr(reinterpret_cast<u32x4_t*>(p)) = q;
     }
 };
 
 template <>
 struct Elem<LORA_F32> {
     __device__ __forceinline__ static float get(const void* p, int64_t i) {
-        return reinterpret_cast<const float*>(p)[i];
+        return gptr(reinterpret_cast<const float*>(p))[i];
     }
     __device__ __forceinline__ static void load8(const void* p, float* f) {
-        const f32x4_t* v = reinterpret_cast<const f32x4_t*>(p);
+        const LORA_GLOBAL f32x4_t* v = gptr(reinterpret_cast<const f32x4_t*>(p));
         f32x4_t a = v[0], b = v[1];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -241,7 +263,7 @@ struct Elem<LORA_F32> {
         }
     }
     __device__ __forceinline__ static void store8(void* p, const float* f) {
-        f32x4_t* v = reinterpret_cast<f32x4_t*>(p);
+        LORA_GLOBAL f32x4_t* v = gptr(reinterpret_cast<f32x4_t*>(p));
         v[0] = f32x4_t{f[0], f[1], f[2], f[3]};
         v[1] = f32x4_t{f[4], f[5], f[6], f[7]};
     }
@@ -289,6 +311,37 @@ __device__ __forceinline__ TaskSlice xcd_slice(int64_t n, int units_per_wg, int 
     s.begin += (int64_t)(blockIdx.x / kNumXcd) * units_per_wg + unit;
     s.stride = (int64_t)(gridDim.x / kNumXcd) * units_per_wg;
     return s;
+}
+
+// Table entries and tile records, read with global loads.
+__device__ __forceinline__ lora_adapter load_adapter(const lora_adapter* table, int a) {
+    // One 16-byte and one 8-byte load, issued together.
+    const LORA_GLOBAL u32x4_t* q4 = gptr(reinterpret_cast<const u32x4_t*>(table + a));
+    const LORA_GLOBAL uint64_t* q = gptr(reinterpret_cast<const uint64_t*>(table + a));
+    const u32x4_t ab = q4[0];
+    const uint64_t w2 = q[2];
+    const uint64_t w0 = (uint64_t)ab[0] | ((uint64_t)ab[1] << 32);
+    const uint64_t w1 = (uint64_t)ab[2] | ((uint64_t)ab[3] << 32);
+    lora_adapter ad;
+    ad.A = reinterpret_cast<const void*>(w0);
+    ad.B = reinterpret_cast<const void*>(w1);
+    ad.rank = (int32_t)(uint32_t)w2;
+    ad.scale = __uint_as_float((uint32_t)(w2 >> 32));
+    return ad;
+}
+__device__ __forceinline__ lora_adapter_grad load_grad(const lora_adapter_grad* table, int a) {
+    const LORA_GLOBAL uint64_t* q = gptr(reinterpret_cast<const uint64_t*>(table + a));
+    lora_adapter_grad g;
+    g.dA = reinterpret_cast<float*>(q[0]);
+    g.dB = reinterpret_cast<float*>(q[1]);
+    return g;
+}
+struct TileRec {
+    int adapter, pos0, rows;
+};
+__device__ __forceinline__ TileRec load_tile(const int32_t* sched, int64_t off, int64_t tile) {
+    const u32x4_t v = *gptr(reinterpret_cast<const u32x4_t*>(sched + off + 4 * tile));
+    return TileRec{(int)v[0], (int)v[1], (int)v[2]};
 }
 
 __device__ __forceinline__ bool adapter_ok(const lora_adapter& ad, int r_max) {

@@ -5,6 +5,8 @@
 // h(x) = W x + B A x; DeltaServe section 2.2, multi-LoRA batching).  Both
 // kernels are MFMA tiles over the rows of one adapter at a time, walking the
 // tile records of lora_segments_build.
+#include <algorithm>
+
 #include "host_checks.h"
 #include "lora_kernels.h"
 
@@ -39,12 +41,66 @@ int launch_expand_t(int ks, const ExpandParams& p, unsigned grid, hipStream_t st
 
 namespace lora {
 
-// Shared by the forward and the backward (declared in backward.hip).
-int run_shrink(int dtype, bool trans_w, const ShrinkParams& p, int32_t T, int32_t num_adapters, hipStream_t st) {
-    const int64_t tasks = SchedLayout::max_tiles16(T, num_adapters) * p.rgroups;
+__global__ __launch_bounds__(256) void shrink_reduce_kernel(ReduceParams p) {
+    const int n = threadIdx.x >> 4;  // row of the tile
+    const int q = threadIdx.x & 15;  // rank group of 8
+    const int64_t n_tasks = p.sched[0];
+    for (int64_t tile = blockIdx.x; tile < n_tasks; tile += gridDim.x) {
+        const TileRec rec = load_tile(p.sched, p.tiles16_off, tile);
+        const lora_adapter ad = load_adapter(p.adapters, rec.adapter);
+        if (!adapter_ok(ad, p.r_max)) continue;  // counted by the shrink kernel
+        const int r = ad.rank;
+        const int k = 8 * q;
+        if (n >= rec.rows || k >= r) continue;
+        const int pos = rec.pos0 + n;
+        const float* src = p.part + (int64_t)pos * p.ldp + k;
+        f32x4_t a = f32x4_t{0.f, 0.f, 0.f, 0.f}, b = a;
+        for (int s = 0; s < p.nslices; ++s) {
+            const LORA_GLOBAL f32x4_t* v = gptr(reinterpret_cast<const f32x4_t*>(src + (int64_t)s * p.slice_stride));
+            a += v[0];
+            b += v[1];
+        }
+        // ranks r .. 8q+7 of the last group hold no partial: write zeros there
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (k + i >= r) a[i] = 0.f;
+            if (k + 4 + i >= r) b[i] = 0.f;
+        }
+        if (p.out) {
+            // k + 8 <= round_up(r_max, 8) <= ldo (a multiple of 8)
+            const int64_t row = p.out_by_pos ? pos : p.perm[pos];
+            float* dst = p.out + row * p.ldo + k;
+            *gptr(reinterpret_cast<f32x4_t*>(dst)) = a;
+            *gptr(reinterpret_cast<f32x4_t*>(dst + 4)) = b;
+        }
+        if (p.outT) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (k + i < r) gptr(p.outT)[(int64_t)(k + i) * p.ldT + pos] = a[i];
+                if (k + 4 + i < r) gptr(p.outT)[(int64_t)(k + 4 + i) * p.ldT + pos] = b[i];
+            }
+        }
+    }
+}
+
+// Shared by the forward and the backward (declared in backward.hip): the
+// split-K shrink into partials, then their fixed-order sum.
+int run_shrink(int dtype, bool trans_w, const ShrinkParams& p, const ReduceParams& rp, int32_t T, int32_t num_adapters,
+               hipStream_t st) {
+    const int64_t tasks = SchedLayout::max_tiles64(T, num_adapters) * p.rgroups * p.nslices;
     const unsigned grid = grid_for(tasks, 1, kMaxGrid);
-    return dtype == LORA_BF16 ? launch_shrink_t<LORA_BF16>(trans_w, p, grid, st)
-                              : launch_shrink_t<LORA_F32>(trans_w, p, grid, st);
+    const int rc = dtype == LORA_BF16 ? launch_shrink_t<LORA_BF16>(trans_w, p, grid, st)
+                                      : launch_shrink_t<LORA_F32>(trans_w, p, grid, st);
+    if (rc != LORA_OK) return rc;
+    const unsigned rgrid = (unsigned)std::min<int64_t>(SchedLayout::max_tiles16(T, num_adapters), 4096);
+    hipLaunchKernelGGL(shrink_reduce_kernel, dim3(rgrid), dim3(256), 0, st, rp);
+    return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
+// Workspace of the split-K partials: [slices][T][round_up(r_max, 8)] fp32.
+int64_t shrink_part_ld(int32_t r_max) { return round_up(r_max, 8); }
+int64_t shrink_part_floats(int32_t T, int32_t K, int32_t r_max) {
+    return (int64_t)shrink_slices(K) * (T > 0 ? T : 1) * shrink_part_ld(r_max);
 }
 
 int run_expand(int dtype, bool trans_w, const ExpandParams& p, int32_t T, int32_t num_adapters, int32_t r_max,
@@ -61,15 +117,22 @@ int run_expand(int dtype, bool trans_w, const ExpandParams& p, int32_t T, int32_
 
 }  // namespace lora
 
+extern "C" size_t lora_shrink_workspace_bytes(int32_t T, int32_t d_in, int32_t r_max) {
+    if (T < 0 || d_in < 1 || r_max < 1 || r_max > LORA_MAX_RANK) return 0;
+    return (size_t)shrink_part_floats(T, d_in, r_max) * sizeof(float);
+}
+
 extern "C" int lora_shrink(int dtype, const void* x, int64_t ldx, int32_t T, int32_t d_in,
                            const lora_adapter* adapters, int32_t num_adapters, int32_t r_max, lora_segments seg,
-                           float* v, int64_t ldv, void* stream) {
+                           float* v, int64_t ldv, void* ws, size_t ws_bytes, void* stream) {
     int rc = check_common(dtype, T, num_adapters, r_max, adapters, seg);
     if (rc != LORA_OK) return rc;
     if (d_in < 1) return LORA_ERR_INVALID_ARG;
     if (T == 0) return LORA_OK;
     if ((rc = check_matrix(x, d_in, ldx)) != LORA_OK) return rc;
     if ((rc = check_f32_rows(v, ldv, r_max)) != LORA_OK) return rc;
+    if (!ws || !aligned16(ws) || ws_bytes < (size_t)shrink_part_floats(T, d_in, r_max) * sizeof(float))
+        return LORA_ERR_WORKSPACE;
     const SchedLayout sl = SchedLayout::make(T, num_adapters);
     ShrinkParams p{};
     p.x = x;
@@ -79,15 +142,29 @@ extern "C" int lora_shrink(int dtype, const void* x, int64_t ldx, int32_t T, int
     p.r_max = r_max;
     p.perm = seg.perm;
     p.sched = seg.sched;
-    p.tiles16_off = sl.tiles16;
-    p.out = v;
-    p.ldo = ldv;
-    p.out_by_pos = 0;
-    p.outT = nullptr;
-    p.ldT = 0;
+    p.tiles64_off = sl.tiles64;
+    p.part = static_cast<float*>(ws);
+    p.ldp = shrink_part_ld(r_max);
+    p.slice_stride = (int64_t)T * p.ldp;
+    p.nslices = shrink_slices(d_in);
     p.err = seg.err;
     p.rgroups = rank_groups(r_max);
-    return run_shrink(dtype, false, p, T, num_adapters, static_cast<hipStream_t>(stream));
+    ReduceParams rp{};
+    rp.part = p.part;
+    rp.ldp = p.ldp;
+    rp.slice_stride = p.slice_stride;
+    rp.nslices = p.nslices;
+    rp.adapters = adapters;
+    rp.r_max = r_max;
+    rp.perm = seg.perm;
+    rp.sched = seg.sched;
+    rp.tiles16_off = sl.tiles16;
+    rp.out = v;
+    rp.ldo = ldv;
+    rp.out_by_pos = 0;
+    rp.outT = nullptr;
+    rp.ldT = 0;
+    return run_shrink(dtype, false, p, rp, T, num_adapters, static_cast<hipStream_t>(stream));
 }
 
 extern "C" int lora_expand_add(int dtype, const float* v, int64_t ldv, int32_t T, int32_t d_out,

@@ -16,17 +16,27 @@ namespace lora {
 // out[row][k] = sum_i X[row][i] * W(k, i) for the rows of one adapter, where
 //   W(k, i) = A_a[k][i]     (A_a is [r, K]; v = A x, the "A x" of h(x) = Wx + BAx)
 //   W(k, i) = B_a[i][k]     (TRANS_W: B_a is [K, r]; g = B^T dy in the backward)
-// One workgroup = one 16-row tile x one group of up to 64 ranks.  Its eight
-// waves split K into contiguous slices of 64-wide chunks; each wave runs
-// 16x16 MFMA tiles (A operand = weight rows, B operand = the tile's rows)
-// with a two-stage register pipeline over its chunks, then the eight partial
-// tiles are summed in wave order through LDS.  With TRANS_W and bf16, each
-// chunk's weight block (64 rows of B_a, contiguous) is staged in the wave's
-// LDS region as loaded and read back transposed with ds_read_b64_tr_b16.
+// Split over K.  One workgroup = one tile of up to 64 rows x one group of up
+// to 64 ranks x one slice of kSliceChunks 64-wide K chunks; it writes the
+// slice's partial sums, and shrink_reduce_kernel adds the slices in order.
+// The eight waves cover the tile's 16-row blocks x sub-slices of the K slice
+// (1 x 8, 2 x 4 or 4 x 2, by the tile's row count): every weight chunk is
+// read from L2 once per tile and shared by the row-block waves through L1.
+// Each wave runs up to four 16x16 MFMA tiles (A operand = weight rows,
+// B operand = the block's rows), two chunks per iteration with their loads
+// issued first; the sub-slice tiles of a row block are summed in wave order
+// through LDS.  Within a chunk, lane group g and half h take K offsets
+// 8 g + 32 h .. + 7, so each load instruction reads one contiguous 64-byte
+// half line per row.  With TRANS_W and bf16, each chunk's weight block (64
+// rows of B_a) is staged in the wave's LDS region as loaded and read back
+// transposed with ds_read_b64_tr_b16.
 
 constexpr int kShrinkWaves = 8;
 constexpr int kShrinkThreads = kShrinkWaves * kWave;
-constexpr int kWPitch = 72;  // staged weight row: up to 64 ranks + 8 elements of padding
+constexpr int kSliceChunks = 16;  // K slice = 1024 elements
+constexpr int kWPitch = 72;       // staged weight row: up to 64 ranks + 8 elements of padding
+
+__host__ __device__ constexpr int shrink_slices(int K) { return (K + 64 * kSliceChunks - 1) / (64 * kSliceChunks); }
 
 struct ShrinkParams {
     const void* x;   // rows gathered through perm
@@ -36,12 +46,11 @@ struct ShrinkParams {
     int32_t r_max;
     const int32_t* perm;
     const int32_t* sched;
-    int64_t tiles16_off;
-    float* out;      // [row][ldo] or nullptr; row = original row, or sorted position if out_by_pos
-    int64_t ldo;
-    int32_t out_by_pos;
-    float* outT;     // [k][ldT] indexed by sorted position, or nullptr
-    int64_t ldT;
+    int64_t tiles64_off;
+    float* part;     // partial sums [slice][sorted position][ldp]
+    int64_t ldp;
+    int64_t slice_stride;
+    int32_t nslices;
     int32_t* err;
     int32_t rgroups; // ceil(r_max / 64)
 };
@@ -77,7 +86,7 @@ __device__ __forceinline__ void shrink_load_x(Frag<DT>* x, const char* xp, int k
     constexpr int EB = Frag<DT>::kBytes;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        const int kk = kc * 64 + 16 * lg + 8 * h;
+        const int kk = kc * 64 + 8 * lg + 32 * h;
         x[h] = Frag<DT>::load(xp + (int64_t)(kk < K ? kk : 0) * EB);  // past K: position 0, zeroed on use
     }
 }
@@ -85,26 +94,25 @@ __device__ __forceinline__ void shrink_load_x(Frag<DT>* x, const char* xp, int k
 template <int DT>
 __device__ __forceinline__ void shrink_mask_x(Frag<DT>* xf, const Frag<DT>* x, int kc, int lg, int K) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) xf[h] = kc * 64 + 16 * lg + 8 * h < K ? x[h] : Frag<DT>::zero();
+    for (int h = 0; h < 2; ++h) xf[h] = kc * 64 + 8 * lg + 32 * h < K ? x[h] : Frag<DT>::zero();
 }
 
 // Row-major weights W(k, i) = A_a[k][i]; or, for fp32 transposed weights,
 // element-wise loads of B_a[i][k].
-template <int DT, bool TRANS_W>
+template <int DT, bool TRANS_W, int NMB = 4>
 __device__ __forceinline__ void shrink_load(ShrinkStage<DT>& S, const char* xp, const char* wbase, int kc, int lg,
-                                            int lr, int K, int r, int rank0, int nmb) {
+                                            int lr, int K, int r, int rank0) {
     constexpr int EB = Frag<DT>::kBytes;
     shrink_load_x<DT>(S.x, xp, kc, lg, K);
-    // Every M-block is loaded (ranks past r read row r - 1: finite, outputs
-    // discarded); unused blocks are skipped in shrink_compute.  Loading
-    // unconditionally keeps the stage in registers.
-    (void)nmb;
+    // The first NMB M-blocks are loaded unconditionally (ranks past r read
+    // row r - 1: finite, outputs discarded), which keeps the stage in
+    // registers.
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
+    for (int mb = 0; mb < NMB; ++mb) {
         const int rk = min(rank0 + 16 * mb + lr, r - 1);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const int kk = kc * 64 + 16 * lg + 8 * h;
+            const int kk = kc * 64 + 8 * lg + 32 * h;
             const int kq = kk < K ? kk : 0;
             if (TRANS_W)
                 S.w[mb][h] = Frag<DT>::load_strided(wbase + ((int64_t)kq * r + rk) * EB, r, min(8, K - kq));
@@ -114,16 +122,40 @@ __device__ __forceinline__ void shrink_load(ShrinkStage<DT>& S, const char* xp, 
     }
 }
 
-template <int DT>
-__device__ __forceinline__ void shrink_compute(const ShrinkStage<DT>& S, f32x4_t* acc, int kc, int lg, int K,
-                                               int nmb) {
+template <int DT, int NMB = 4>
+__device__ __forceinline__ void shrink_compute(const ShrinkStage<DT>& S, f32x4_t* acc, int kc, int lg, int K) {
     Frag<DT> xf[2];
     shrink_mask_x<DT>(xf, S.x, kc, lg, K);
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-        if (mb < nmb)
+    for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-            for (int h = 0; h < 2; ++h) acc[mb] = mma(S.w[mb][h], xf[h], acc[mb]);
+        for (int h = 0; h < 2; ++h) acc[mb] = mma(S.w[mb][h], xf[h], acc[mb]);
+}
+
+// Chunk i (0 <= i < n) of a wave's slice [kc0, kc0 + n), visited from a
+// tile-dependent starting point so that the tiles of one adapter, which read
+// the same weight rows, do not all read the same lines at the same time.
+// The order is fixed per tile, so results stay bit-reproducible.
+__device__ __forceinline__ int rotated(int kc0, int n, int rot, int i) {
+    const int j = i + rot;
+    return kc0 + (j < n ? j : j - n);
+}
+
+// Row-major weights, NMB rank blocks: two chunks per iteration, all loads first.
+template <int DT, int NMB>
+__device__ __forceinline__ void shrink_rows_loop(f32x4_t* acc, const char* xp, const char* wbase, int kc0, int kc1,
+                                                 int rot, int lg, int lr, int K, int r, int rank0) {
+    const int n = kc1 - kc0;
+    for (int i = 0; i < n; i += 2) {
+        const bool two = i + 1 < n;
+        const int ka = rotated(kc0, n, rot, i);
+        const int kb = two ? rotated(kc0, n, rot, i + 1) : ka;
+        ShrinkStage<DT> S0, S1;
+        shrink_load<DT, false, NMB>(S0, xp, wbase, ka, lg, lr, K, r, rank0);
+        shrink_load<DT, false, NMB>(S1, xp, wbase, kb, lg, lr, K, r, rank0);
+        shrink_compute<DT, NMB>(S0, acc, ka, lg, K);
+        if (two) shrink_compute<DT, NMB>(S1, acc, kb, lg, K);
+    }
 }
 
 // Transposed bf16 weights: the chunk's 64 rows of B_a (ranks rank0 ..
@@ -141,7 +173,7 @@ __device__ __forceinline__ void shrink_load_tr(ShrinkStageTr<NSEG>& S, const cha
         const int sg = lane + kWave * (i < nseg ? i : 0);
         const int j = sg >> lseg;
         const int row = kc * 64 + j < K ? kc * 64 + j : 0;
-        S.wr[i] = *reinterpret_cast<const u32x4_t*>(wbase + ((int64_t)row * r + rank0 + 8 * (sg & (nseg - 1))) * 2);
+        S.wr[i] = *gptr(reinterpret_cast<const u32x4_t*>(wbase + ((int64_t)row * r + rank0 + 8 * (sg & (nseg - 1))) * 2));
     }
 }
 
@@ -167,8 +199,8 @@ __device__ __forceinline__ void shrink_compute_tr(const ShrinkStageTr<NSEG>& S, 
         if (mb < nmb) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                // rows 16 lg + 8 h + 0..7 of rank column 16 mb + (lane % 16)
-                const uint16_t* base = wst + (16 * lg + 8 * h + e) * kWPitch + 16 * mb + 4 * c;
+                // rows 8 lg + 32 h + 0..7 of rank column 16 mb + (lane % 16)
+                const uint16_t* base = wst + (8 * lg + 32 * h + e) * kWPitch + 16 * mb + 4 * c;
                 const uint2 a = lds_read_tr16(base);
                 const uint2 b = lds_read_tr16(base + 4 * kWPitch);
                 Frag<LORA_BF16> wf;
@@ -195,19 +227,20 @@ void shrink_kernel(ShrinkParams p) {
     const int lr = lane & 15;  // MFMA row / column within the 16x16 tile
     const int lg = lane >> 4;  // K group of this lane
     uint16_t* wst = reinterpret_cast<uint16_t*>(s_mem) + wave * 64 * kWPitch;  // this wave's staging rows
-    const int64_t n_tasks = (int64_t)p.sched[0] * p.rgroups;
+    const int ntiles = p.sched[1];
+    const int64_t n_tasks = (int64_t)ntiles * p.rgroups * p.nslices;
     const TaskSlice ts = xcd_slice(n_tasks, 1, 0);
     const int nkc = (p.K + 63) / 64;
-    const int kc0 = (int)((int64_t)wave * nkc / kShrinkWaves);
-    const int kc1 = (int)((int64_t)(wave + 1) * nkc / kShrinkWaves);
 
     for (int64_t task = ts.begin; task < ts.end; task += ts.stride) {
-        const int tile = (int)(task / p.rgroups);
-        const int rg = (int)(task % p.rgroups);
-        const int4 rec = *reinterpret_cast<const int4*>(p.sched + p.tiles16_off + 4 * (int64_t)tile);
-        const lora_adapter ad = p.adapters[rec.x];
+        // consecutive tasks: consecutive tiles of the same (slice, rank group)
+        const int tile = (int)(task % ntiles);
+        const int rg = (int)((task / ntiles) % p.rgroups);
+        const int sl = (int)(task / ((int64_t)ntiles * p.rgroups));
+        const TileRec rec = load_tile(p.sched, p.tiles64_off, tile);
+        const lora_adapter ad = load_adapter(p.adapters, rec.adapter);
         if (!adapter_ok(ad, p.r_max)) {
-            if (rg == 0 && threadIdx.x == 0) atomicAdd(p.err, 1);
+            if (rg == 0 && sl == 0 && threadIdx.x == 0) atomicAdd(p.err, 1);
             continue;
         }
         const int r = ad.rank;
@@ -215,11 +248,24 @@ void shrink_kernel(ShrinkParams p) {
         if (rank0 >= r) continue;
         const int nr = min(64, r - rank0);
         const int nmb = (nr + 15) / 16;
-        const int pos0 = rec.y;
-        const int nrows = rec.z;
+        const int pos0 = rec.pos0;
+        const int nrows = rec.rows;
 
-        // Rows past the tile read row pos0 (finite data; their outputs are discarded).
-        const int64_t xrow = p.perm[pos0 + (lr < nrows ? lr : 0)];
+        // Wave roles: nbw row blocks x (8 / nbw) sub-slices of this K slice.
+        const int nnb = (nrows + 15) >> 4;
+        const int nbw = nnb == 1 ? 1 : (nnb == 2 ? 2 : 4);
+        const int nsub = kShrinkWaves / nbw;
+        const int nb = wave % nbw;
+        const int sub = wave / nbw;
+        const int c0 = sl * kSliceChunks;
+        const int nch = min(kSliceChunks, nkc - c0);
+        const int kc0 = c0 + sub * nch / nsub;
+        const int kc1 = c0 + (sub + 1) * nch / nsub;
+        const bool active = nb < nnb;
+
+        // Rows past the tile read the tile's first row (finite data; outputs discarded).
+        const int rr = 16 * nb + lr;
+        const int64_t xrow = p.perm[pos0 + (rr < nrows ? rr : 0)];
         const char* xp = static_cast<const char*>(p.x) + xrow * p.ldx * EB;
         const char* wbase = static_cast<const char*>(TRANS_W ? ad.B : ad.A);
 
@@ -227,54 +273,51 @@ void shrink_kernel(ShrinkParams p) {
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-        // Two chunks per iteration, all of their loads issued before their
-        // MFMAs.  Transposed weights that cannot be staged in 16-byte segments
-        // (fp32, or a rank that is not a multiple of 8) take a plain
-        // one-chunk-at-a-time loop.
         // Staged path: bf16 and the group's rank count a power of two >= 8.
         const bool staged = kTr && nr >= 8 && (nr & (nr - 1)) == 0 && (r & 7) == 0;
-        if (TRANS_W && !staged) {
-            for (int kc = kc0; kc < kc1; ++kc) {
-                F xr[2], xf[2];
-                shrink_load_x<DT>(xr, xp, kc, lg, p.K);
-                shrink_mask_x<DT>(xf, xr, kc, lg, p.K);
-                for (int mb = 0; mb < nmb; ++mb) {
-                    const int rk = min(rank0 + 16 * mb + lr, r - 1);
+        if (active) {
+            if (TRANS_W && !staged) {
+                // transposed weights that cannot be staged in 16-byte segments
+                // (fp32, or a rank that is not a multiple of 8): one chunk at a time
+                for (int kc = kc0; kc < kc1; ++kc) {
+                    F xr[2], xf[2];
+                    shrink_load_x<DT>(xr, xp, kc, lg, p.K);
+                    shrink_mask_x<DT>(xf, xr, kc, lg, p.K);
+                    for (int mb = 0; mb < nmb; ++mb) {
+                        const int rk = min(rank0 + 16 * mb + lr, r - 1);
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const int kk = kc * 64 + 16 * lg + 8 * h;
-                        const int kq = kk < p.K ? kk : 0;
-                        const F wf = F::load_strided(wbase + ((int64_t)kq * r + rk) * EB, r, min(8, p.K - kq));
-                        // acc[mb] with a runtime mb: select into the four accumulators
+                        for (int h = 0; h < 2; ++h) {
+                            const int kk = kc * 64 + 8 * lg + 32 * h;
+                            const int kq = kk < p.K ? kk : 0;
+                            const F wf = F::load_strided(wbase + ((int64_t)kq * r + rk) * EB, r, min(8, p.K - kq));
 #pragma unroll
-                        for (int m = 0; m < 4; ++m)
-                            if (m == mb) acc[m] = mma(wf, xf[h], acc[m]);
+                            for (int m = 0; m < 4; ++m)
+                                if (m == mb) acc[m] = mma(wf, xf[h], acc[m]);
+                        }
                     }
                 }
-            }
-        } else if (kTr && nr <= 32) {
-            for (int kc = kc0; kc < kc1; kc += 2) {
-                const bool two = kc + 1 < kc1;
-                ShrinkStageTr<4> S0, S1;
-                shrink_load_tr(S0, xp, wbase, kc, lane, p.K, r, rank0, nr);
-                shrink_load_tr(S1, xp, wbase, two ? kc + 1 : kc, lane, p.K, r, rank0, nr);
-                shrink_compute_tr(S0, acc, wst, kc, lane, p.K, nr, nmb);
-                if (two) shrink_compute_tr(S1, acc, wst, kc + 1, lane, p.K, nr, nmb);
-            }
-        } else if (kTr) {
-            for (int kc = kc0; kc < kc1; ++kc) {
-                ShrinkStageTr<8> S0;
-                shrink_load_tr(S0, xp, wbase, kc, lane, p.K, r, rank0, nr);
-                shrink_compute_tr(S0, acc, wst, kc, lane, p.K, nr, nmb);
-            }
-        } else {
-            for (int kc = kc0; kc < kc1; kc += 2) {
-                const bool two = kc + 1 < kc1;
-                ShrinkStage<DT> S0, S1;
-                shrink_load<DT, TRANS_W>(S0, xp, wbase, kc, lg, lr, p.K, r, rank0, nmb);
-                shrink_load<DT, TRANS_W>(S1, xp, wbase, two ? kc + 1 : kc, lg, lr, p.K, r, rank0, nmb);
-                shrink_compute<DT>(S0, acc, kc, lg, p.K, nmb);
-                if (two) shrink_compute<DT>(S1, acc, kc + 1, lg, p.K, nmb);
+            } else if (kTr && nr <= 32) {
+                for (int kc = kc0; kc < kc1; kc += 2) {
+                    const bool two = kc + 1 < kc1;
+                    ShrinkStageTr<4> S0, S1;
+                    shrink_load_tr(S0, xp, wbase, kc, lane, p.K, r, rank0, nr);
+                    shrink_load_tr(S1, xp, wbase, two ? kc + 1 : kc, lane, p.K, r, rank0, nr);
+                    shrink_compute_tr(S0, acc, wst, kc, lane, p.K, nr, nmb);
+                    if (two) shrink_compute_tr(S1, acc, wst, kc + 1, lane, p.K, nr, nmb);
+                }
+            } else if (kTr) {
+                for (int kc = kc0; kc < kc1; ++kc) {
+                    ShrinkStageTr<8> S0;
+                    shrink_load_tr(S0, xp, wbase, kc, lane, p.K, r, rank0, nr);
+                    shrink_compute_tr(S0, acc, wst, kc, lane, p.K, nr, nmb);
+                }
+            } else if (!TRANS_W) {
+                switch (nmb) {
+                    case 1: shrink_rows_loop<DT, 1>(acc, xp, wbase, kc0, kc1, 0, lg, lr, p.K, r, rank0); break;
+                    case 2: shrink_rows_loop<DT, 2>(acc, xp, wbase, kc0, kc1, 0, lg, lr, p.K, r, rank0); break;
+                    case 3: shrink_rows_loop<DT, 3>(acc, xp, wbase, kc0, kc1, 0, lg, lr, p.K, r, rank0); break;
+                    default: shrink_rows_loop<DT, 4>(acc, xp, wbase, kc0, kc1, 0, lg, lr, p.K, r, rank0); break;
+                }
             }
         }
 
@@ -282,32 +325,49 @@ void shrink_kernel(ShrinkParams p) {
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) s_red[(wave * 4 + mb) * kWave + lane] = acc[mb];
         __syncthreads();
-        if (threadIdx.x < 4 * kWave) {
-            const int mb = threadIdx.x / kWave;
-            const int l = threadIdx.x & (kWave - 1);
-            if (mb < nmb) {
-                f32x4_t sum = s_red[mb * kWave + l];
+        // Waves 0 .. nbw-1 finish row block nb = wave: sub-slices summed in order.
+        if (wave < nbw && active) {
+            float* part = p.part + (int64_t)sl * p.slice_stride;
+            const int n = lr;
+            const int row = 16 * nb + n;
 #pragma unroll
-                for (int w = 1; w < kShrinkWaves; ++w) sum += s_red[(w * 4 + mb) * kWave + l];
-                const int n = l & 15;
-                const int rk = rank0 + 16 * mb + 4 * (l >> 4);  // D rows 4*(l/16)+i
-                if (n < nrows && rk < r) {
-                    const int pos = pos0 + n;
-                    if (p.out) {
-                        const int64_t row = p.out_by_pos ? pos : p.perm[pos];
-                        *reinterpret_cast<f32x4_t*>(p.out + row * p.ldo + rk) = sum;
-                    }
-                    if (p.outT) {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            if (rk + i < r) p.outT[(int64_t)(rk + i) * p.ldT + pos] = sum[i];
-                    }
+            for (int mb = 0; mb < 4; ++mb) {
+                if (mb < nmb) {
+                    f32x4_t sum = s_red[(wave * 4 + mb) * kWave + lane];
+                    for (int q = 1; q < nsub; ++q) sum += s_red[((wave + q * nbw) * 4 + mb) * kWave + lane];
+                    const int rk = rank0 + 16 * mb + 4 * lg;  // D rows 4*(l/16)+i
+                    if (row < nrows && rk < r)
+                        *gptr(reinterpret_cast<f32x4_t*>(part + (int64_t)(pos0 + row) * p.ldp + rk)) = sum;
                 }
             }
         }
         __syncthreads();
     }
 }
+
+// Sum of the K-slice partials, in slice order, for every row with an adapter:
+//   out[row][k] (row = original row, or sorted position if out_by_pos) and,
+//   if outT is given, outT[k][sorted position], for k < r_a.
+// One workgroup per 16-row tile; thread (row n, group q) handles ranks
+// 8 q .. 8 q + 7.
+struct ReduceParams {
+    const float* part;
+    int64_t ldp;
+    int64_t slice_stride;
+    int32_t nslices;
+    const lora_adapter* adapters;
+    int32_t r_max;
+    const int32_t* perm;
+    const int32_t* sched;
+    int64_t tiles16_off;
+    float* out;
+    int64_t ldo;
+    int32_t out_by_pos;
+    float* outT;
+    int64_t ldT;
+};
+
+// shrink_reduce_kernel(ReduceParams) is defined in forward.hip.
 
 // ============================================================== expand-add
 //
@@ -320,8 +380,8 @@ void shrink_kernel(ShrinkParams p) {
 // workgroup into MFMA B-operand fragments in LDS (bf16: hi = bf16(v),
 // lo = bf16(v - hi)).  Every wave issues all of its y loads for the tile up
 // front, then runs the tile in 16-row steps.  Output columns are assigned to
-// MFMA rows so that each lane owns 16 consecutive columns of one row: 32-byte
-// (bf16) read-modify-write per lane, 128 contiguous bytes per row and wave.
+// MFMA rows so that each lane owns two runs of 8 columns of one row (see
+// expand_col): 128 contiguous bytes per row and wave.
 
 constexpr int kExpandWaves = 4;
 constexpr int kExpandCols = kExpandWaves * 64;
@@ -341,8 +401,11 @@ struct ExpandParams {
     int32_t* err;
 };
 
-// Output column of MFMA row m in column block mb (0..3) of a 64-column block.
-__device__ __forceinline__ int expand_col(int mb, int m) { return 16 * (m >> 2) + 4 * mb + (m & 3); }
+// Output column of MFMA row m in column block mb (0..3) of a 64-column block:
+// lane group g ends up owning columns 8 g + 0..7 and 32 + 8 g + 0..7, so the
+// four lane groups read and write one contiguous 64-byte half line per row
+// and instruction.
+__device__ __forceinline__ int expand_col(int mb, int m) { return 8 * (m >> 2) + 32 * (mb >> 1) + 4 * (mb & 1) + (m & 3); }
 
 template <int DT, bool TRANS_W, int KS>
 __global__ __launch_bounds__(kExpandWaves * kWave) void expand_kernel(ExpandParams p) {
@@ -368,16 +431,16 @@ __global__ __launch_bounds__(kExpandWaves * kWave) void expand_kernel(ExpandPara
     for (int64_t task = ts.begin; task < ts.end; task += ts.stride) {
         const int tile = (int)(task / ncg);
         const int cg = (int)(task % ncg);
-        const int4 rec = *reinterpret_cast<const int4*>(p.sched + p.tiles64_off + 4 * (int64_t)tile);
-        const lora_adapter ad = p.adapters[rec.x];
+        const TileRec rec = load_tile(p.sched, p.tiles64_off, tile);
+        const lora_adapter ad = load_adapter(p.adapters, rec.adapter);
         if (!adapter_ok(ad, p.r_max)) {
             if (cg == 0 && threadIdx.x == 0) atomicAdd(p.err, 1);
             continue;
         }
         const int r = ad.rank;
         const float s = ad.scale;
-        const int pos0 = rec.y;
-        const int nrows = rec.z;
+        const int pos0 = rec.pos0;
+        const int nrows = rec.rows;
         const int nsub = (nrows + 15) >> 4;
         const int c0 = cg * kExpandCols + wave * 64;
         const bool cols_ok = c0 < p.N;
@@ -412,7 +475,7 @@ __global__ __launch_bounds__(kExpandWaves * kWave) void expand_kernel(ExpandPara
             const int f = threadIdx.x + kThreads * i;
             const int kk = 32 * ((f / kWave) % KS) + 8 * ((f >> 4) & 3);
             const bool ld = vok[i] && kk < r;
-            const f32x4_t* src = reinterpret_cast<const f32x4_t*>(p.v + (ld ? vrow[i] * p.ldv + kk : 0));
+            const LORA_GLOBAL f32x4_t* src = gptr(reinterpret_cast<const f32x4_t*>(p.v + (ld ? vrow[i] * p.ldv + kk : 0)));
             vq[i][0] = src[0];
             vq[i][1] = src[1];
         }
@@ -448,16 +511,16 @@ __global__ __launch_bounds__(kExpandWaves * kWave) void expand_kernel(ExpandPara
             }
         }
 
-        // 2. All y loads of this wave for the tile: row 16 st + lr, columns c0 + 16 lg + 0..15.
+        // 2. All y loads of this wave for the tile: row 16 st + lr, columns c0 + 8 lg + 32 h + 0..7.
         u32x4_t yq[4][YQ];
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const int col = c0 + 16 * lg + 8 * h;
+                const int col = c0 + 8 * lg + 32 * h;
                 const bool ok = yok[st] && col < p.N;
-                const u32x4_t* src =
-                    reinterpret_cast<const u32x4_t*>(ybase + (ok ? yrow[st] * p.ldy + col : 0) * EB);
+                const LORA_GLOBAL u32x4_t* src =
+                    gptr(reinterpret_cast<const u32x4_t*>(ybase + (ok ? yrow[st] * p.ldy + col : 0) * EB));
 #pragma unroll
                 for (int q = 0; q < YQ / 2; ++q) yq[st][h * (YQ / 2) + q] = src[q];
             }
@@ -500,7 +563,7 @@ __global__ __launch_bounds__(kExpandWaves * kWave) void expand_kernel(ExpandPara
                 }
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    const int col = c0 + 16 * lg + 8 * h;
+                    const int col = c0 + 8 * lg + 32 * h;
                     if (yok[st] && col < p.N) {
                         float yv[8];
                         E::unpack8(&yq[st][h * (YQ / 2)], yv);
@@ -595,7 +658,7 @@ __device__ __forceinline__ void contract_load(ContractWin<DT>& W, const char* q,
 #pragma unroll
     for (int mb = 0; mb < kContractMB; ++mb) {
         const int rk = min(rank0 + 16 * mb + (lane & 15), r - 1);  // ranks past r: discarded rows
-        const f32x4_t* src = reinterpret_cast<const f32x4_t*>(PT + (int64_t)rk * ldT + pp);
+        const LORA_GLOBAL f32x4_t* src = gptr(reinterpret_cast<const f32x4_t*>(PT + (int64_t)rk * ldT + pp));
         W.pv[mb][0] = src[0];
         W.pv[mb][1] = src[1];
     }
@@ -629,7 +692,7 @@ __device__ __forceinline__ void contract_compute(const ContractWin<DT>& W, char*
 #pragma unroll
             for (int e = 0; e < 8; ++e) t[(lcol + e) * kCtPitch + lrow + j] = W.q[j].get(e);
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) qf[nb] = F::load(t + (16 * nb + lr) * kCtPitch + 8 * lg);
+        for (int nb = 0; nb < 4; ++nb) qf[nb] = F::load_lds(t + (16 * nb + lr) * kCtPitch + 8 * lg);
     }
     // 3. A operands from P^T (zero outside [lo, hi)), hi/lo split for bf16.
     const int pp = win + 8 * lg;
@@ -672,8 +735,8 @@ __global__ __launch_bounds__(kContractWaves * kWave) void contract_kernel(Contra
         const int rg = (int)((task / ncb) % p.rgroups);
         const int act = (int)(task / ((int64_t)ncb * p.rgroups));
         const int a = p.sched[p.active_off + act];
-        const lora_adapter ad = p.adapters[a];
-        const lora_adapter_grad gr = p.grads[a];
+        const lora_adapter ad = load_adapter(p.adapters, a);
+        const lora_adapter_grad gr = load_grad(p.grads, a);
         const bool is_dA = cb_all < p.ncb_in;
         if (!adapter_ok(ad, p.r_max) || gr.dA == nullptr || gr.dB == nullptr) {
             if (cb_all == 0 && rg == 0 && threadIdx.x == 0) atomicAdd(p.err, 1);
@@ -706,14 +769,19 @@ __global__ __launch_bounds__(kContractWaves * kWave) void contract_kernel(Contra
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-        for (int win = wa; win < wb; win += 64) {
-            const bool two = win + 32 < wb;
+        // Windows visited from a task-dependent start (the column blocks of one
+        // adapter read the same g / v windows); fixed order per task.
+        const int nw = (wb - wa) / 32;
+        const int rot = nw > 0 ? (int)(task % nw) : 0;
+        for (int i = 0; i < nw; i += 2) {
+            const bool two = i + 1 < nw;
+            const int wa0 = wa + 32 * (rotated(0, nw, rot, i));
+            const int wa1 = two ? wa + 32 * (rotated(0, nw, rot, i + 1)) : wa0;
             ContractWin<DT> W0, W1;
-            contract_load<DT>(W0, q, ldq, PT, p.ldT, p.perm, win, lo, hi, cq, lcol, lrow, rank0, r, lane);
-            contract_load<DT>(W1, q, ldq, PT, p.ldT, p.perm, two ? win + 32 : win, lo, hi, cq, lcol, lrow, rank0,
-                              r, lane);
-            contract_compute<DT>(W0, tileA, acc, win, lo, hi, lcol, lrow, nmb, lane);
-            if (two) contract_compute<DT>(W1, tileB, acc, win + 32, lo, hi, lcol, lrow, nmb, lane);
+            contract_load<DT>(W0, q, ldq, PT, p.ldT, p.perm, wa0, lo, hi, cq, lcol, lrow, rank0, r, lane);
+            contract_load<DT>(W1, q, ldq, PT, p.ldT, p.perm, wa1, lo, hi, cq, lcol, lrow, rank0, r, lane);
+            contract_compute<DT>(W0, tileA, acc, wa0, lo, hi, lcol, lrow, nmb, lane);
+            if (two) contract_compute<DT>(W1, tileB, acc, wa1, lo, hi, lcol, lrow, nmb, lane);
         }
 
         // Fixed-order sum of the four waves' tiles.
@@ -740,7 +808,7 @@ __global__ __launch_bounds__(kContractWaves * kWave) void contract_kernel(Contra
                             const int rk = rank0 + 16 * mb + 4 * lg + i;
                             if (rk < r) {
                                 float* dst = is_dA ? gr.dA + (int64_t)rk * p.d_in + col : gr.dB + (int64_t)col * r + rk;
-                                *dst += s * sum[i];
+                                *gptr(dst) += s * sum[i];
                             }
                         }
                     }

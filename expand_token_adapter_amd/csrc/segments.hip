@@ -4,8 +4,8 @@
 // (DeltaServe, section 2.2).  The compute kernels therefore need, for every
 // adapter, the list of its rows: a counting sort of the rows by adapter id.
 //
-// Three kernels, all deterministic (the order inside an adapter is the row
-// order, never the order in which threads happen to run):
+// General path: three kernels, all deterministic (the order inside an
+// adapter is the row order, never the order in which threads happen to run):
 //   1. seg_count   one workgroup per chunk of kChunk rows: each row's rank
 //                  among the earlier rows of its chunk with the same id, and
 //                  the per-(adapter, chunk) counts.
@@ -188,6 +188,158 @@ __global__ __launch_bounds__(kChunk) void seg_scatter_kernel(const int32_t* __re
     }
 }
 
+// ---------------------------------------------------------------- one workgroup
+//
+// For batches of up to kSmallMaxT rows and kSmallMaxA adapters the whole
+// build runs in one workgroup of 16 waves (one launch instead of three):
+//   1. wave w counts the ids of its contiguous row range into its own LDS
+//      histogram hist[w][a], one update per distinct id of each 64-row group;
+//   2. per adapter: counts = sum over w, hist[w][a] becomes the exclusive
+//      prefix over waves; a block scan over adapters gives offsets, the tile
+//      prefixes and the active list;
+//   3. wave w walks its rows in order, 64 at a time; inside a group the lanes
+//      that share an id are ranked by lane order (ballot), and the wave's
+//      cursor for that id advances by the group's count.  Every row's
+//      position is therefore its rank in row order: the same stable grouping
+//      as the three-kernel path.
+
+constexpr int kSmallMaxA = 1024;
+constexpr int kSmallMaxT = 1 << 16;
+constexpr int kSmallWaves = kScanThreads / kWave;
+
+__global__ __launch_bounds__(kScanThreads) void seg_small_kernel(const int32_t* __restrict__ ids, int32_t T,
+                                                                 int32_t A, int32_t* __restrict__ counts,
+                                                                 int32_t* __restrict__ offsets,
+                                                                 int32_t* __restrict__ perm,
+                                                                 int32_t* __restrict__ sched, int32_t* __restrict__ err,
+                                                                 int64_t active_off, int64_t tiles16_off,
+                                                                 int64_t tiles64_off) {
+    __shared__ int s_hist[kSmallWaves][kSmallMaxA];
+    __shared__ int s_off[kSmallMaxA];
+    __shared__ int s_cnt[kSmallMaxA];
+    __shared__ int s_pre16[kSmallMaxA];
+    __shared__ int s_pre64[kSmallMaxA];
+    __shared__ int s_tot[4][kSmallWaves];
+    __shared__ int s_err[kSmallWaves];
+    const int tid = threadIdx.x;
+    const int w = tid / kWave;
+    const int lane = tid & (kWave - 1);
+    const int per = (T + kSmallWaves - 1) / kSmallWaves;
+    const int r0 = min(T, w * per);
+    const int r1 = min(T, r0 + per);
+
+    for (int i = tid; i < kSmallWaves * kSmallMaxA; i += kScanThreads) (&s_hist[0][0])[i] = 0;
+    __syncthreads();
+    // Row ids are read 8 groups of 64 at a time (independent loads in flight).
+    int bad = 0;
+    for (int b = r0; b < r1; b += 8 * kWave) {
+        int idv[8];
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+            const int t = b + g * kWave + lane;
+            idv[g] = t < r1 ? ids[t] : -1;
+        }
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+            const int id = idv[g];
+            const bool valid = id >= 0 && id < A;
+            bad += (!valid && id != -1) ? 1 : 0;
+            // One pass per distinct id in the group: the lowest lane holding
+            // it adds the group's count to this wave's own histogram row.
+            uint64_t todo = __ballot(valid);
+            while (todo) {
+                const int leader = __ffsll((long long)todo) - 1;
+                const int lid = __shfl(id, leader, kWave);
+                const uint64_t m = __ballot(valid && id == lid);
+                todo &= ~m;
+                if (lane == leader) s_hist[w][lid] += __popcll(m);
+            }
+        }
+    }
+    bad = __reduce_add_sync(~0ull, bad);
+    if (lane == 0) s_err[w] = bad;
+    __syncthreads();
+
+    // per adapter: total and exclusive prefix over the waves
+    const int a = tid;
+    int c = 0;
+    if (a < A) {
+        for (int v = 0; v < kSmallWaves; ++v) {
+            const int h = s_hist[v][a];
+            s_hist[v][a] = c;
+            c += h;
+        }
+        counts[a] = c;
+        s_cnt[a] = c;
+    }
+    int tc, t16, t64, tact;
+    const int ec = block_exclusive_scan(c, s_tot[0], &tc);
+    const int e16 = block_exclusive_scan((c + 15) / 16, s_tot[1], &t16);
+    const int e64 = block_exclusive_scan((c + 63) / 64, s_tot[2], &t64);
+    const int eact = block_exclusive_scan(c > 0 ? 1 : 0, s_tot[3], &tact);
+    if (a < A) {
+        offsets[a] = ec;
+        s_off[a] = ec;
+        s_pre16[a] = e16;
+        s_pre64[a] = e64;
+        if (c > 0) sched[active_off + eact] = a;
+    }
+    if (tid == 0) {
+        offsets[A] = tc;
+        sched[0] = t16;
+        sched[1] = t64;
+        sched[2] = tact;
+        sched[3] = 0;
+        int e = 0;
+        for (int v = 0; v < kSmallWaves; ++v) e += s_err[v];
+        err[0] = e;
+    }
+    __syncthreads();
+
+    // stable scatter: wave w owns rows [r0, r1); s_hist[w][a] is its cursor for adapter a.
+    // Ids are loaded 8 groups at a time; the groups are then processed with no
+    // loads in between, so stores of one group never hold up the next.
+    for (int b = r0; b < r1; b += 8 * kWave) {
+        int idv[8];
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+            const int t = b + g * kWave + lane;
+            idv[g] = t < r1 ? ids[t] : -1;
+        }
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+            const int t = b + g * kWave + lane;
+            const int id = idv[g];
+            const bool valid = id >= 0 && id < A;
+            uint64_t todo = __ballot(valid);
+            while (todo) {
+                const int leader = __ffsll((long long)todo) - 1;
+                const int lid = __shfl(id, leader, kWave);
+                const uint64_t m = __ballot(valid && id == lid);
+                todo &= ~m;
+                if (valid && id == lid) {
+                    const int rank = __popcll(m & ((1ull << lane) - 1));
+                    const int local = s_hist[w][lid] + rank;  // position inside the adapter's group
+                    const int pos = s_off[lid] + local;
+                    perm[pos] = t;
+                    const int cnt = s_cnt[lid];
+                    if ((local & 15) == 0) {
+                        const int rows = cnt - local < 16 ? cnt - local : 16;
+                        *reinterpret_cast<int4*>(sched + tiles16_off + 4 * (int64_t)(s_pre16[lid] + local / 16)) =
+                            make_int4(lid, pos, rows, 0);
+                    }
+                    if ((local & 63) == 0) {
+                        const int rows = cnt - local < 64 ? cnt - local : 64;
+                        *reinterpret_cast<int4*>(sched + tiles64_off + 4 * (int64_t)(s_pre64[lid] + local / 64)) =
+                            make_int4(lid, pos, rows, 0);
+                    }
+                }
+                if (lane == leader) s_hist[w][lid] += __popcll(m);
+            }
+        }
+    }
+}
+
 }  // namespace lora
 
 using namespace lora;
@@ -210,6 +362,11 @@ extern "C" int lora_segments_build(const int32_t* adapter_ids, int32_t T, int32_
     const SchedLayout sl = SchedLayout::make(T, num_adapters);
     int32_t* wsi = static_cast<int32_t*>(ws);
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (T <= kSmallMaxT && num_adapters <= kSmallMaxA) {
+        hipLaunchKernelGGL(seg_small_kernel, dim3(1), dim3(kScanThreads), 0, st, adapter_ids, T, num_adapters,
+                           seg.counts, seg.offsets, seg.perm, seg.sched, seg.err, sl.active, sl.tiles16, sl.tiles64);
+        return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+    }
     hipLaunchKernelGGL(seg_count_kernel, dim3(nchunks), dim3(kChunk), 0, st, adapter_ids, T, num_adapters, nchunks,
                        wsi + w.hist, wsi + w.rank, wsi + w.errc);
     hipLaunchKernelGGL(seg_scan_kernel, dim3(1), dim3(kScanThreads), 0, st, num_adapters, nchunks, wsi + w.hist,

@@ -43,7 +43,9 @@ def _ids_case(kind, T, A, rng):
 
 
 @pytest.mark.parametrize("kind", ["random", "sorted", "reverse", "same", "none", "zipf", "bad"])
-@pytest.mark.parametrize("T,A", [(1, 1), (255, 3), (257, 64), (2048, 320), (10368, 32), (6000, 1500)])
+# (6000, 1500) and (70001, 7) take the three-kernel path; the others the one-workgroup path
+@pytest.mark.parametrize("T,A", [(1, 1), (255, 3), (257, 64), (2048, 320), (10368, 32), (65536, 1024),
+                                 (6000, 1500), (70001, 7)])
 def test_segments_bit_exact(kind, T, A):
     rng = np.random.default_rng(T * 7919 + A)
     ids = np.ascontiguousarray(_ids_case(kind, T, A, rng), dtype=np.int32)
