@@ -40,20 +40,90 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--sets", type=int, default=3, help="rotating copies of every buffer")
+    ap.add_argument("--sets", type=int, default=4, help="rotating copies of every buffer")
     ap.add_argument("--graph", action="store_true", help="replay each step from a captured HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-min-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only time a plain device copy of 256 MiB (reference for counter scaling)")
+    ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="rocprofv3 counter_collection.csv files of FETCH_SIZE / WRITE_SIZE passes over this "
+                         "bench and over --copy-calibration: write the measured HBM traffic of the expand kernel")
     return ap.parse_args()
+
+
+# HBM traffic of the dominant kernel, measured with rocprofv3 counters and
+# stored with a hash of the sources it was measured on; a stale file reads as null.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "expand_kernel_mixed-coserve-4096to14336_traffic.json")
+KERNEL_SOURCES = ["expand_token_adapter_amd/csrc/lora_kernels.h", "expand_token_adapter_amd/csrc/device_common.h",
+                  "expand_token_adapter_amd/csrc/forward.hip", "expand_token_adapter_amd/build.py"]
+EXPAND_KERNEL_PREFIX = "void lora::expand_kernel<0, false"
+COPY_BYTES = 256 << 20
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def _counter_means(path, counter):
+    """Mean per-dispatch value of one counter for every kernel in a rocprofv3 counter_collection.csv."""
+    import csv
+    from collections import defaultdict
+    vals = defaultdict(list)
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row.get("Counter_Name") == counter:
+                vals[row["Kernel_Name"]].append(float(row["Counter_Value"]))
+    return {k: (sum(v) / len(v), len(v)) for k, v in vals.items()}
+
+
+def traffic_from(fetch, write, cfetch, cwrite):
+    def pick(means, pred, what):
+        hits = [(k, m) for k, m in means.items() if pred(k)]
+        if not hits:
+            raise SystemExit(f"no {what} dispatches in the counter file")
+        return max(hits, key=lambda km: km[1][1])  # the most frequent one
+    fe = pick(_counter_means(fetch, "FETCH_SIZE"), lambda k: k.startswith(EXPAND_KERNEL_PREFIX), "expand")
+    wr = pick(_counter_means(write, "WRITE_SIZE"), lambda k: k.startswith(EXPAND_KERNEL_PREFIX), "expand")
+    cf = pick(_counter_means(cfetch, "FETCH_SIZE"), lambda k: "copy" in k.lower(), "copy")
+    cw = pick(_counter_means(cwrite, "WRITE_SIZE"), lambda k: "copy" in k.lower(), "copy")
+    f_fetch = COPY_BYTES / (cf[1][0] * 1024.0)
+    f_write = COPY_BYTES / (cw[1][0] * 1024.0)
+    rd = fe[1][0] * 1024.0 * f_fetch
+    wb = wr[1][0] * 1024.0 * f_write
+    out = {"kernel": fe[0], "fetch_kib_per_dispatch": fe[1][0], "write_kib_per_dispatch": wr[1][0],
+           "dispatches": [fe[1][1], wr[1][1]], "copy_kernel": cf[0], "copy_bytes_each_way": COPY_BYTES,
+           "copy_fetch_kib": cf[1][0], "copy_write_kib": cw[1][0], "fetch_scale": f_fetch, "write_scale": f_write,
+           "read_bytes_per_launch": rd, "write_bytes_per_launch": wb, "traffic_bytes_per_launch": rd + wb,
+           "source_sha256": kernel_source_hash(), "sources": KERNEL_SOURCES}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
+
+
+def measured_traffic():
+    """Traffic per launch from the stored counter run, or None if absent or measured on other sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != kernel_source_hash():
+        return None
+    return float(t["traffic_bytes_per_launch"])
 
 
 def copy_calibration(reps: int = 20):
     """A plain device-to-device copy of a known size: the achievable copy rate on
     this GPU, and the per-dispatch reference for scaling FETCH_SIZE / WRITE_SIZE."""
     import torch
-    n = 256 << 20
+    n = COPY_BYTES
     a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
     b = torch.empty_like(a)
     c = torch.empty_like(a)
@@ -83,7 +153,8 @@ def algorithmic(wl):
     sum_ru = int(ranks[used].sum())                  # sum over used adapters of r_a
     n_valid = int(valid.sum())
     out = {}
-    out["segments"] = dict(bytes=4 * T + 4 * T + 4 * (2 * wl.num_adapters + 1), flops=0)
+    seg_bytes = lambda n: 4 * n + 4 * n + 4 * (2 * wl.num_adapters + 1)  # ids in, perm out, counts/offsets
+    out["segments"] = dict(bytes=seg_bytes(T) + seg_bytes(wl.ft_count), flops=0)
     out["shrink"] = dict(bytes=e * n_valid * d_in + e * d_in * sum_ru + 4 * sum_rt, flops=2 * d_in * sum_rt)
     out["expand"] = dict(bytes=4 * sum_rt + e * d_out * sum_ru + 2 * e * n_valid * d_out, flops=2 * d_out * sum_rt)
     ft = wl.ft_ids
@@ -129,6 +200,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.traffic_from:
+        traffic_from(*args.traffic_from)
         return
     import torch
     import expand_token_adapter_amd as lb
@@ -263,7 +337,7 @@ def main():
         "step_algorithmic_GBps": alg["step"]["bytes"] / (ms * 1e-3) / 1e9,
         "step_algorithmic_bytes": alg["step"]["bytes"],
         "roofline": {"bound": "hbm", "kernel": "lora_expand_add (expand_kernel)", "achieved": achieved,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "algorithmic_bytes_per_launch": ex["bytes"], "avg_launch_ms": kern_ms, "timing": kern_how,
                      "mfma_frac": ex["flops"] / (kern_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
     }

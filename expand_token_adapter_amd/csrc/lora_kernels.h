@@ -33,7 +33,10 @@ namespace lora {
 
 constexpr int kShrinkWaves = 8;
 constexpr int kShrinkThreads = kShrinkWaves * kWave;
-constexpr int kSliceChunks = 16;  // K slice = 1024 elements
+#ifndef LORA_SHRINK_SLICE_CHUNKS
+#define LORA_SHRINK_SLICE_CHUNKS 16  // K slice = 1024 elements
+#endif
+constexpr int kSliceChunks = LORA_SHRINK_SLICE_CHUNKS;
 constexpr int kWPitch = 72;       // staged weight row: up to 64 ranks + 8 elements of padding
 
 __host__ __device__ constexpr int shrink_slices(int K) { return (K + 64 * kSliceChunks - 1) / (64 * kSliceChunks); }
