@@ -55,7 +55,7 @@ def parse():
 # HBM traffic of the dominant kernel, measured with rocprofv3 counters and
 # stored with a hash of the sources it was measured on; a stale file reads as null.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "expand_kernel_mixed-coserve-4096to14336_traffic.json")
-KERNEL_SOURCES = ["expand_token_adapter_amd/csrc/lora_kernels.h", "expand_token_adapter_amd/csrc/device_common.h",
+KERNEL_SOURCES = ["expand_token_adapter_amd/csrc/expand.h", "expand_token_adapter_amd/csrc/device_common.h",
                   "expand_token_adapter_amd/csrc/forward.hip", "expand_token_adapter_amd/build.py"]
 EXPAND_KERNEL_PREFIX = "void lora::expand_kernel<0, false"
 COPY_BYTES = 256 << 20

@@ -12,7 +12,9 @@
 #include <algorithm>
 
 #include "host_checks.h"
-#include "lora_kernels.h"
+#include "shrink.h"
+#include "expand.h"
+#include "contract.h"
 
 using namespace lora;
 
@@ -153,7 +155,6 @@ extern "C" int lora_backward(int dtype, const void* x, int64_t ldx, const void* 
         ep.r_max = r_max;
         ep.perm = seg_ft.perm;
         ep.sched = seg_ft.sched;
-        ep.tiles64_off = sl.tiles64;
         ep.y = dx;
         ep.ldy = lddx;
         ep.N = d_in;

@@ -274,26 +274,39 @@ struct Elem<LORA_F32> {
 // Scheduling metadata written by the segment builder (int32 offsets into
 // lora_segments.sched).  Tile records are {adapter, first sorted position,
 // rows, 0}.
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+// Four 16-bit values of one LDS column: lane i of each 16-lane group gets
+// rows row0 + 0..3 of column col0 + i, when lane 4e + c of the group passes
+// the address of (row0 + e, col0 + 4c).  (gfx950 ds_read_b64_tr_b16.)
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+    const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4_t*)((__attribute__((address_space(3))) uint16_t*)(p)));
+    return __builtin_bit_cast(uint2, v);
+}
+
 struct SchedLayout {
     int64_t active;    // [A] adapters with at least one row, ascending
     int64_t tiles16;   // [n16_max] records of up to 16 rows
     int64_t tiles64;   // [n64_max] records of up to 64 rows
+    int64_t tiles128;  // [n128_max] records of up to 128 rows
     int64_t total;     // int32 elements
     __host__ __device__ static SchedLayout make(int64_t T, int64_t A) {
         SchedLayout s;
         s.active = 4;
         s.tiles16 = s.active + ((A + 3) / 4) * 4;
-        int64_t n16 = (T + 15) / 16 + A;
-        s.tiles64 = s.tiles16 + 4 * n16;
-        int64_t n64 = (T + 63) / 64 + A;
-        s.total = s.tiles64 + 4 * n64;
+        s.tiles64 = s.tiles16 + 4 * max_tiles16(T, A);
+        s.tiles128 = s.tiles64 + 4 * max_tiles64(T, A);
+        s.total = s.tiles128 + 4 * max_tiles128(T, A);
         return s;
     }
     __host__ __device__ static int64_t max_tiles16(int64_t T, int64_t A) { return (T + 15) / 16 + A; }
     __host__ __device__ static int64_t max_tiles64(int64_t T, int64_t A) { return (T + 63) / 64 + A; }
+    __host__ __device__ static int64_t max_tiles128(int64_t T, int64_t A) { return (T + 127) / 128 + A; }
 };
 // sched[0] = number of 16-row tiles, sched[1] = number of 64-row tiles,
-// sched[2] = number of active adapters.
+// sched[2] = number of active adapters, sched[3] = number of 128-row tiles.
 
 // Contiguous slice of a task range for the calling wave group.  Workgroups
 // are handed to the 8 XCDs round-robin by index, so workgroups b with the

@@ -1,0 +1,245 @@
+// expand.h -- expand-add kernel: y += s W v for the rows of each adapter (gfx950).
+//
+// Walks the scheduling records written by the segment builder, so every
+// workgroup touches one adapter's weights and that adapter's rows only
+// (multi-LoRA batching: each row applies its own adapter, DeltaServe section
+// 2.2).  Dense work goes to 16x16 MFMA tiles; every reduction runs in a fixed
+// order, so results are bit-reproducible.
+#pragma once
+
+#include "device_common.h"
+
+namespace lora {
+
+// ============================================================== expand-add
+//
+// Y[row][c] += s_a * sum_k V[row][k] * W(c, k) for the rows of one adapter:
+//   W(c, k) = B_a[c][k]     (B_a is [N, r]; y += s B v, forward)
+//   W(c, k) = A_a[k][c]     (TRANS_W: A_a is [r, N]; dX += s A^T g, backward)
+// One workgroup = one tile record of up to ROWS rows x 256 output columns;
+// each of its four waves owns 64 columns and keeps that weight block (MFMA A
+// operand, KS x 32 ranks) in registers for the whole tile.  At the start of a
+// tile the workgroup converts the tile's fp32 V rows once into MFMA B-operand
+// fragments in LDS (bf16: hi = bf16(v), lo = bf16(v - hi)).  The tile is then
+// finished 16 rows at a time while the y rows of the next steps are already
+// in flight (a ring of kYBuf steps).  y is read and written row-contiguously:
+// lane L of a wave owns columns 8 (L % 8) .. + 7 of rows L / 8 and 8 + L / 8
+// of a 16-row step, so eight consecutive lanes cover 128 contiguous bytes of
+// a bf16 row; the MFMA accumulators are brought into that layout through a
+// small per-wave LDS buffer.
+
+constexpr int kExpandWaves = 4;
+constexpr int kExpandCols = kExpandWaves * 64;
+constexpr int kTPitch = 68;  // floats per row of the per-wave transpose buffer (16 rows x 64 columns)
+
+#ifndef LORA_EXPAND_TALL_TILES
+#define LORA_EXPAND_TALL_TILES 1
+#endif
+#ifndef LORA_EXPAND_YBUF
+#define LORA_EXPAND_YBUF 4
+#endif
+
+// Rows per tile record walked by the expand: 128 (rank <= 64) or 64 (rank <= 128).
+__host__ __device__ constexpr int expand_rows(int ks) { return (ks == 4 || !LORA_EXPAND_TALL_TILES) ? 64 : 128; }
+
+struct ExpandParams {
+    const float* v;  // [row][ldv]; row = original row, or sorted position if v_by_pos
+    int64_t ldv;
+    int32_t v_by_pos;
+    const lora_adapter* adapters;
+    int32_t r_max;
+    const int32_t* perm;
+    const int32_t* sched;
+    int64_t tiles_off;  // tile records of expand_rows(KS) rows
+    int32_t tiles_idx;  // sched[tiles_idx] = number of those records
+    void* y;            // [row][ldy], rows through perm
+    int64_t ldy;
+    int32_t N;          // output columns (d_out, or d_in for dX)
+    int32_t* err;
+};
+
+template <int DT, bool TRANS_W, int KS>
+__global__ __launch_bounds__(kExpandWaves * kWave) __attribute__((amdgpu_waves_per_eu(KS == 4 ? 2 : 3)))
+void expand_kernel(ExpandParams p) {
+    using F = Frag<DT>;
+    using E = Elem<DT>;
+    using O = F32Operand<DT>;
+    constexpr int EB = F::kBytes;
+    constexpr int YQ = EB / 2;                   // 16-byte quads per 8 elements
+    constexpr int ROWS = expand_rows(KS);
+    constexpr int STEPS = ROWS / 16;
+    constexpr int kThreads = kExpandWaves * kWave;
+    constexpr int NF = STEPS * KS * kWave / kThreads;  // V fragments converted per thread
+    constexpr int kYBuf = DT == LORA_BF16 ? LORA_EXPAND_YBUF : 2;  // y steps held in registers
+    static_assert(sizeof(O) == 32, "fragment pair is two quads");
+    __shared__ u32x4_t s_frag[STEPS * KS * kWave * 2];
+    __shared__ __attribute__((aligned(16))) float s_t[kExpandWaves][16 * kTPitch];
+    __shared__ int32_t s_row[ROWS];
+
+    const int wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int lr = lane & 15;
+    const int lg = lane >> 4;
+    const int yr = lane >> 3;       // row (and row + 8) of the step in the row-contiguous layout
+    const int yc = 8 * (lane & 7);  // first column (of the wave's 64) in that layout
+    const int ncg = (p.N + kExpandCols - 1) / kExpandCols;
+    const int64_t n_tasks = (int64_t)p.sched[p.tiles_idx] * ncg;
+    const TaskSlice ts = xcd_slice(n_tasks, 1, 0);
+    char* ybase = static_cast<char*>(p.y);
+    float* tw = &s_t[wave][0];
+
+    for (int64_t task = ts.begin; task < ts.end; task += ts.stride) {
+        const int tile = (int)(task / ncg);
+        const int cg = (int)(task % ncg);
+        const TileRec rec = load_tile(p.sched, p.tiles_off, tile);
+        const lora_adapter ad = load_adapter(p.adapters, rec.adapter);
+        if (!adapter_ok(ad, p.r_max)) {
+            if (cg == 0 && threadIdx.x == 0) atomicAdd(p.err, 1);
+            continue;
+        }
+        const int r = ad.rank;
+        const float s = ad.scale;
+        const int pos0 = rec.pos0;
+        const int nrows = rec.rows;
+        const int nst = (nrows + 15) >> 4;
+        const int c0 = cg * kExpandCols + wave * 64;
+
+        // 1. Original rows of the tile (rows past the tile repeat its first row).
+        int32_t my_row = 0;
+        if (threadIdx.x < ROWS) my_row = p.perm[pos0 + (int)threadIdx.x < pos0 + nrows ? pos0 + threadIdx.x : pos0];
+
+        // 2. Weight block: wf[mb][ks] holds W(c0 + 16 mb + lr, 32 ks + 8 lg + 0..7).
+        F wf[4][KS];
+        const char* wbase = static_cast<const char*>(TRANS_W ? ad.A : ad.B);
+        if (!TRANS_W && (r & 7) == 0) {
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) {
+                const int col = c0 + 16 * mb + lr;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int kk = 32 * ks + 8 * lg;
+                    const bool ok = col < p.N && kk < r;
+                    const F w = F::load(wbase + (ok ? (int64_t)col * r + kk : 0) * EB);
+                    wf[mb][ks] = ok ? w : F::zero();
+                }
+            }
+        } else {
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) {
+                const int col = c0 + 16 * mb + lr;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int kk = 32 * ks + 8 * lg;
+                    const int nval = (col < p.N) ? max(0, min(8, r - kk)) : 0;
+                    if (TRANS_W)
+                        wf[mb][ks] = F::load_strided(wbase + ((int64_t)(nval ? kk : 0) * p.N + (nval ? col : 0)) * EB,
+                                                     p.N, nval);
+                    else
+                        wf[mb][ks] = F::load_strided(wbase + (nval ? (int64_t)col * r + kk : 0) * EB, 1, nval);
+                }
+            }
+        }
+        if (threadIdx.x < ROWS) s_row[threadIdx.x] = my_row;
+        __syncthreads();
+
+        // 3. V rows of the whole tile (converted below), then the y rows of the
+        //    first kYBuf steps.  (The pitch of V is a multiple of 8 and >= r_max,
+        //    so 8 values from any rank group that starts below r stay inside the row.)
+        f32x4_t vq[NF][2];
+        bool vok[NF];
+#pragma unroll
+        for (int i = 0; i < NF; ++i) {
+            const int f = threadIdx.x + kThreads * i;
+            const int row = 16 * (f / (KS * kWave)) + (f & 15);
+            const int kk = 32 * ((f / kWave) % KS) + 8 * ((f >> 4) & 3);
+            vok[i] = row < nrows && kk < r;
+            const int64_t vrow = p.v_by_pos ? pos0 + (row < nrows ? row : 0) : s_row[row];
+            const LORA_GLOBAL f32x4_t* src = gptr(reinterpret_cast<const f32x4_t*>(p.v + vrow * p.ldv + (vok[i] ? kk : 0)));
+            vq[i][0] = src[0];
+            vq[i][1] = src[1];
+        }
+        const bool col_ok = c0 + yc < p.N;
+        const int ycol = col_ok ? c0 + yc : 0;
+        u32x4_t yq[kYBuf][2][YQ];
+        auto load_y = [&](u32x4_t (&dst)[2][YQ], int st) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int64_t row = s_row[16 * st + 8 * u + yr];
+                const LORA_GLOBAL u32x4_t* src =
+                    gptr(reinterpret_cast<const u32x4_t*>(ybase + (row * p.ldy + ycol) * EB));
+#pragma unroll
+                for (int q = 0; q < YQ; ++q) dst[u][q] = src[q];
+            }
+        };
+#pragma unroll
+        for (int b = 0; b < kYBuf; ++b)
+            if (b < STEPS) load_y(yq[b], b < nst ? b : 0);
+
+        // 4. V fragments of the tile -> LDS.
+#pragma unroll
+        for (int i = 0; i < NF; ++i) {
+            const int f = threadIdx.x + kThreads * i;
+            const int kk = 32 * ((f / kWave) % KS) + 8 * ((f >> 4) & 3);
+            float fv[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                fv[e] = (vok[i] && kk + e < r) ? vq[i][0][e] : 0.f;
+                fv[4 + e] = (vok[i] && kk + 4 + e < r) ? vq[i][1][e] : 0.f;
+            }
+            const O o = O::make(fv);
+            const u32x4_t* oq = reinterpret_cast<const u32x4_t*>(&o);
+            s_frag[2 * f] = oq[0];
+            s_frag[2 * f + 1] = oq[1];
+        }
+        lds_barrier();
+
+        // 5. 16 rows at a time: MFMA, accumulators to the row-contiguous layout
+        //    through LDS, y += s * acc with one rounding, then the y loads of
+        //    the step kYBuf ahead go into the freed registers.
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st) {
+            if (st < nst) {
+                f32x4_t acc[4];
+#pragma unroll
+                for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int f = (st * KS + ks) * kWave + lane;
+                    O o;
+                    u32x4_t* oq = reinterpret_cast<u32x4_t*>(&o);
+                    oq[0] = s_frag[2 * f];
+                    oq[1] = s_frag[2 * f + 1];
+#pragma unroll
+                    for (int mb = 0; mb < 4; ++mb) acc[mb] = o.mma_right(wf[mb][ks], acc[mb]);
+                }
+                // D[m][n] of block mb: column 16 mb + m, row n; this lane has m = 4 lg + i, n = lr.
+#pragma unroll
+                for (int mb = 0; mb < 4; ++mb) *reinterpret_cast<f32x4_t*>(tw + lr * kTPitch + 16 * mb + 4 * lg) = acc[mb];
+                __builtin_amdgcn_wave_barrier();
+                u32x4_t(&yb)[2][YQ] = yq[st % kYBuf];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int row_in_tile = 16 * st + 8 * u + yr;
+                    const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(tw + (8 * u + yr) * kTPitch + yc);
+                    const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(tw + (8 * u + yr) * kTPitch + yc + 4);
+                    float yv[8];
+                    E::unpack8(&yb[u][0], yv);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        yv[e] = yv[e] + s * a0[e];
+                        yv[4 + e] = yv[4 + e] + s * a1[e];
+                    }
+                    if (col_ok && row_in_tile < nrows) {
+                        const int64_t row = s_row[row_in_tile];
+                        E::store8(ybase + (row * p.ldy + ycol) * EB, yv);
+                    }
+                }
+                __builtin_amdgcn_wave_barrier();
+                if (st + kYBuf < STEPS && st + kYBuf < nst) load_y(yb, st + kYBuf);
+            }
+        }
+        __syncthreads();  // s_row / s_frag are rewritten by the next task
+    }
+}
+
+}  // namespace lora

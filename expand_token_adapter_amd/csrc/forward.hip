@@ -8,7 +8,8 @@
 #include <algorithm>
 
 #include "host_checks.h"
-#include "lora_kernels.h"
+#include "shrink.h"
+#include "expand.h"
 
 using namespace lora;
 
@@ -106,13 +107,19 @@ int64_t shrink_part_floats(int32_t T, int32_t K, int32_t r_max) {
 int run_expand(int dtype, bool trans_w, const ExpandParams& p, int32_t T, int32_t num_adapters, int32_t r_max,
                hipStream_t st) {
     const int ks = r_max <= 32 ? 1 : (r_max <= 64 ? 2 : 4);
-    const int64_t tasks = SchedLayout::max_tiles64(T, num_adapters) * ((p.N + kExpandCols - 1) / kExpandCols);
+    const SchedLayout sl = SchedLayout::make(T, num_adapters);
+    ExpandParams q = p;
+    const bool t128 = expand_rows(ks) == 128;
+    q.tiles_off = t128 ? sl.tiles128 : sl.tiles64;
+    q.tiles_idx = t128 ? 3 : 1;
+    const int64_t tiles = t128 ? SchedLayout::max_tiles128(T, num_adapters) : SchedLayout::max_tiles64(T, num_adapters);
+    const int64_t tasks = tiles * ((p.N + kExpandCols - 1) / kExpandCols);
     const unsigned grid = grid_for(tasks, 1, kMaxGrid);
     if (dtype == LORA_BF16)
-        return trans_w ? launch_expand_t<LORA_BF16, true>(ks, p, grid, st)
-                       : launch_expand_t<LORA_BF16, false>(ks, p, grid, st);
-    return trans_w ? launch_expand_t<LORA_F32, true>(ks, p, grid, st)
-                   : launch_expand_t<LORA_F32, false>(ks, p, grid, st);
+        return trans_w ? launch_expand_t<LORA_BF16, true>(ks, q, grid, st)
+                       : launch_expand_t<LORA_BF16, false>(ks, q, grid, st);
+    return trans_w ? launch_expand_t<LORA_F32, true>(ks, q, grid, st)
+                   : launch_expand_t<LORA_F32, false>(ks, q, grid, st);
 }
 
 }  // namespace lora
@@ -176,7 +183,6 @@ extern "C" int lora_expand_add(int dtype, const float* v, int64_t ldv, int32_t T
     if (T == 0) return LORA_OK;
     if ((rc = check_matrix(y, d_out, ldy)) != LORA_OK) return rc;
     if ((rc = check_f32_rows(v, ldv, r_max)) != LORA_OK) return rc;
-    const SchedLayout sl = SchedLayout::make(T, num_adapters);
     ExpandParams p{};
     p.v = v;
     p.ldv = ldv;
@@ -185,7 +191,6 @@ extern "C" int lora_expand_add(int dtype, const float* v, int64_t ldv, int32_t T
     p.r_max = r_max;
     p.perm = seg.perm;
     p.sched = seg.sched;
-    p.tiles64_off = sl.tiles64;
     p.y = y;
     p.ldy = ldy;
     p.N = d_out;
