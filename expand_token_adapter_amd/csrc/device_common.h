@@ -290,23 +290,20 @@ struct SchedLayout {
     int64_t active;    // [A] adapters with at least one row, ascending
     int64_t tiles16;   // [n16_max] records of up to 16 rows
     int64_t tiles64;   // [n64_max] records of up to 64 rows
-    int64_t tiles128;  // [n128_max] records of up to 128 rows
     int64_t total;     // int32 elements
     __host__ __device__ static SchedLayout make(int64_t T, int64_t A) {
         SchedLayout s;
         s.active = 4;
         s.tiles16 = s.active + ((A + 3) / 4) * 4;
         s.tiles64 = s.tiles16 + 4 * max_tiles16(T, A);
-        s.tiles128 = s.tiles64 + 4 * max_tiles64(T, A);
-        s.total = s.tiles128 + 4 * max_tiles128(T, A);
+        s.total = s.tiles64 + 4 * max_tiles64(T, A);
         return s;
     }
     __host__ __device__ static int64_t max_tiles16(int64_t T, int64_t A) { return (T + 15) / 16 + A; }
     __host__ __device__ static int64_t max_tiles64(int64_t T, int64_t A) { return (T + 63) / 64 + A; }
-    __host__ __device__ static int64_t max_tiles128(int64_t T, int64_t A) { return (T + 127) / 128 + A; }
 };
 // sched[0] = number of 16-row tiles, sched[1] = number of 64-row tiles,
-// sched[2] = number of active adapters, sched[3] = number of 128-row tiles.
+// sched[2] = number of active adapters.
 
 // Contiguous slice of a task range for the calling wave group.  Workgroups
 // are handed to the 8 XCDs round-robin by index, so workgroups b with the

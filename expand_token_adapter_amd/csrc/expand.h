@@ -16,13 +16,14 @@ namespace lora {
 // Y[row][c] += s_a * sum_k V[row][k] * W(c, k) for the rows of one adapter:
 //   W(c, k) = B_a[c][k]     (B_a is [N, r]; y += s B v, forward)
 //   W(c, k) = A_a[k][c]     (TRANS_W: A_a is [r, N]; dX += s A^T g, backward)
-// One workgroup = one tile record of up to ROWS rows x 256 output columns;
+// One workgroup = one tile record of up to 64 rows x 256 output columns;
 // each of its four waves owns 64 columns and keeps that weight block (MFMA A
 // operand, KS x 32 ranks) in registers for the whole tile.  At the start of a
 // tile the workgroup converts the tile's fp32 V rows once into MFMA B-operand
 // fragments in LDS (bf16: hi = bf16(v), lo = bf16(v - hi)).  The tile is then
 // finished 16 rows at a time while the y rows of the next steps are already
-// in flight (a ring of kYBuf steps).  y is read and written row-contiguously:
+// in flight (a ring of kYBuf steps; for bf16 the whole tile).  Taller tiles
+// (fewer weight-block loads) measured slower: fewer workgroups in flight.  y is read and written row-contiguously:
 // lane L of a wave owns columns 8 (L % 8) .. + 7 of rows L / 8 and 8 + L / 8
 // of a 16-row step, so eight consecutive lanes cover 128 contiguous bytes of
 // a bf16 row; the MFMA accumulators are brought into that layout through a
@@ -32,16 +33,6 @@ constexpr int kExpandWaves = 4;
 constexpr int kExpandCols = kExpandWaves * 64;
 constexpr int kTPitch = 68;  // floats per row of the per-wave transpose buffer (16 rows x 64 columns)
 
-#ifndef LORA_EXPAND_TALL_TILES
-#define LORA_EXPAND_TALL_TILES 1
-#endif
-#ifndef LORA_EXPAND_YBUF
-#define LORA_EXPAND_YBUF 4
-#endif
-
-// Rows per tile record walked by the expand: 128 (rank <= 64) or 64 (rank <= 128).
-__host__ __device__ constexpr int expand_rows(int ks) { return (ks == 4 || !LORA_EXPAND_TALL_TILES) ? 64 : 128; }
-
 struct ExpandParams {
     const float* v;  // [row][ldv]; row = original row, or sorted position if v_by_pos
     int64_t ldv;
@@ -50,8 +41,7 @@ struct ExpandParams {
     int32_t r_max;
     const int32_t* perm;
     const int32_t* sched;
-    int64_t tiles_off;  // tile records of expand_rows(KS) rows
-    int32_t tiles_idx;  // sched[tiles_idx] = number of those records
+    int64_t tiles64_off;
     void* y;            // [row][ldy], rows through perm
     int64_t ldy;
     int32_t N;          // output columns (d_out, or d_in for dX)
@@ -66,11 +56,11 @@ void expand_kernel(ExpandParams p) {
     using O = F32Operand<DT>;
     constexpr int EB = F::kBytes;
     constexpr int YQ = EB / 2;                   // 16-byte quads per 8 elements
-    constexpr int ROWS = expand_rows(KS);
+    constexpr int ROWS = 64;
     constexpr int STEPS = ROWS / 16;
     constexpr int kThreads = kExpandWaves * kWave;
     constexpr int NF = STEPS * KS * kWave / kThreads;  // V fragments converted per thread
-    constexpr int kYBuf = DT == LORA_BF16 ? LORA_EXPAND_YBUF : 2;  // y steps held in registers
+    constexpr int kYBuf = DT == LORA_BF16 ? 4 : 2;     // y steps held in registers
     static_assert(sizeof(O) == 32, "fragment pair is two quads");
     __shared__ u32x4_t s_frag[STEPS * KS * kWave * 2];
     __shared__ __attribute__((aligned(16))) float s_t[kExpandWaves][16 * kTPitch];
@@ -83,7 +73,7 @@ void expand_kernel(ExpandParams p) {
     const int yr = lane >> 3;       // row (and row + 8) of the step in the row-contiguous layout
     const int yc = 8 * (lane & 7);  // first column (of the wave's 64) in that layout
     const int ncg = (p.N + kExpandCols - 1) / kExpandCols;
-    const int64_t n_tasks = (int64_t)p.sched[p.tiles_idx] * ncg;
+    const int64_t n_tasks = (int64_t)p.sched[1] * ncg;
     const TaskSlice ts = xcd_slice(n_tasks, 1, 0);
     char* ybase = static_cast<char*>(p.y);
     float* tw = &s_t[wave][0];
@@ -91,7 +81,7 @@ void expand_kernel(ExpandParams p) {
     for (int64_t task = ts.begin; task < ts.end; task += ts.stride) {
         const int tile = (int)(task / ncg);
         const int cg = (int)(task % ncg);
-        const TileRec rec = load_tile(p.sched, p.tiles_off, tile);
+        const TileRec rec = load_tile(p.sched, p.tiles64_off, tile);
         const lora_adapter ad = load_adapter(p.adapters, rec.adapter);
         if (!adapter_ok(ad, p.r_max)) {
             if (cg == 0 && threadIdx.x == 0) atomicAdd(p.err, 1);

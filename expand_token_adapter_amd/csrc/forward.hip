@@ -107,13 +107,9 @@ int64_t shrink_part_floats(int32_t T, int32_t K, int32_t r_max) {
 int run_expand(int dtype, bool trans_w, const ExpandParams& p, int32_t T, int32_t num_adapters, int32_t r_max,
                hipStream_t st) {
     const int ks = r_max <= 32 ? 1 : (r_max <= 64 ? 2 : 4);
-    const SchedLayout sl = SchedLayout::make(T, num_adapters);
     ExpandParams q = p;
-    const bool t128 = expand_rows(ks) == 128;
-    q.tiles_off = t128 ? sl.tiles128 : sl.tiles64;
-    q.tiles_idx = t128 ? 3 : 1;
-    const int64_t tiles = t128 ? SchedLayout::max_tiles128(T, num_adapters) : SchedLayout::max_tiles64(T, num_adapters);
-    const int64_t tasks = tiles * ((p.N + kExpandCols - 1) / kExpandCols);
+    q.tiles64_off = SchedLayout::make(T, num_adapters).tiles64;
+    const int64_t tasks = SchedLayout::max_tiles64(T, num_adapters) * ((p.N + kExpandCols - 1) / kExpandCols);
     const unsigned grid = grid_for(tasks, 1, kMaxGrid);
     if (dtype == LORA_BF16)
         return trans_w ? launch_expand_t<LORA_BF16, true>(ks, q, grid, st)

@@ -22,7 +22,7 @@ constexpr int kScanThreads = 1024;
 
 // Workspace layout (int32 elements), regions aligned to 64 elements.
 struct SegWs {
-    int64_t hist, rank, errc, pre16, pre64, pre128, total;
+    int64_t hist, rank, errc, pre16, pre64, total;
     static SegWs make(int64_t T, int64_t A) {
         auto al = [](int64_t n) { return (n + 63) / 64 * 64; };
         const int64_t nchunks = (T + kChunk - 1) / kChunk;
@@ -32,8 +32,7 @@ struct SegWs {
         w.errc = w.rank + al(T);
         w.pre16 = w.errc + al(nchunks);
         w.pre64 = w.pre16 + al(A);
-        w.pre128 = w.pre64 + al(A);
-        w.total = w.pre128 + al(A);
+        w.total = w.pre64 + al(A);
         return w;
     }
 };
@@ -110,10 +109,9 @@ __global__ __launch_bounds__(kScanThreads) void seg_scan_kernel(int32_t A, int32
                                                                 int32_t* __restrict__ offsets,
                                                                 int32_t* __restrict__ sched,
                                                                 int32_t* __restrict__ pre16,
-                                                                int32_t* __restrict__ pre64,
-                                                                int32_t* __restrict__ pre128, int32_t* __restrict__ err,
+                                                                int32_t* __restrict__ pre64, int32_t* __restrict__ err,
                                                                 int64_t active_off) {
-    __shared__ int s_tot[5][kScanThreads / kWave];
+    __shared__ int s_tot[4][kScanThreads / kWave];
     const int tid = threadIdx.x;
     // Per adapter: exclusive prefix of its chunk counts (in place), total = count.
     for (int a = tid; a < A; a += kScanThreads) {
@@ -127,28 +125,25 @@ __global__ __launch_bounds__(kScanThreads) void seg_scan_kernel(int32_t A, int32
         counts[a] = run;
     }
     __syncthreads();
-    int carry_c = 0, carry16 = 0, carry64 = 0, carry128 = 0, carry_act = 0;
+    int carry_c = 0, carry16 = 0, carry64 = 0, carry_act = 0;
     int32_t* active = sched + active_off;
     for (int base = 0; base < A; base += kScanThreads) {
         const int a = base + tid;
         const int c = a < A ? counts[a] : 0;
-        int tc, t16, t64, t128, tact;
+        int tc, t16, t64, tact;
         const int ec = block_exclusive_scan(c, s_tot[0], &tc);
         const int e16 = block_exclusive_scan((c + 15) / 16, s_tot[1], &t16);
         const int e64 = block_exclusive_scan((c + 63) / 64, s_tot[2], &t64);
-        const int e128 = block_exclusive_scan((c + 127) / 128, s_tot[4], &t128);
         const int eact = block_exclusive_scan(c > 0 ? 1 : 0, s_tot[3], &tact);
         if (a < A) {
             offsets[a] = carry_c + ec;
             pre16[a] = carry16 + e16;
             pre64[a] = carry64 + e64;
-            pre128[a] = carry128 + e128;
             if (c > 0) active[carry_act + eact] = a;
         }
         carry_c += tc;
         carry16 += t16;
         carry64 += t64;
-        carry128 += t128;
         carry_act += tact;
     }
     if (tid == 0) {
@@ -156,7 +151,7 @@ __global__ __launch_bounds__(kScanThreads) void seg_scan_kernel(int32_t A, int32
         sched[0] = carry16;
         sched[1] = carry64;
         sched[2] = carry_act;
-        sched[3] = carry128;
+        sched[3] = 0;
         int e = 0;
         for (int c = 0; c < nchunks; ++c) e += errc[c];
         err[0] = e;
@@ -170,10 +165,8 @@ __global__ __launch_bounds__(kChunk) void seg_scatter_kernel(const int32_t* __re
                                                              const int32_t* __restrict__ offsets,
                                                              const int32_t* __restrict__ pre16,
                                                              const int32_t* __restrict__ pre64,
-                                                             const int32_t* __restrict__ pre128,
                                                              int32_t* __restrict__ perm, int32_t* __restrict__ sched,
-                                                             int64_t tiles16_off, int64_t tiles64_off,
-                                                             int64_t tiles128_off) {
+                                                             int64_t tiles16_off, int64_t tiles64_off) {
     const int c = blockIdx.x;
     const int64_t t = (int64_t)c * kChunk + threadIdx.x;
     if (t >= T) return;
@@ -191,11 +184,6 @@ __global__ __launch_bounds__(kChunk) void seg_scatter_kernel(const int32_t* __re
     if ((local & 63) == 0) {
         int32_t* rec = sched + tiles64_off + 4 * (int64_t)(pre64[id] + local / 64);
         const int32_t rows = cnt - local < 64 ? cnt - local : 64;
-        *reinterpret_cast<int4*>(rec) = make_int4(id, pos, rows, 0);
-    }
-    if ((local & 127) == 0) {
-        int32_t* rec = sched + tiles128_off + 4 * (int64_t)(pre128[id] + local / 128);
-        const int32_t rows = cnt - local < 128 ? cnt - local : 128;
         *reinterpret_cast<int4*>(rec) = make_int4(id, pos, rows, 0);
     }
 }
@@ -225,14 +213,13 @@ __global__ __launch_bounds__(kScanThreads) void seg_small_kernel(const int32_t* 
                                                                  int32_t* __restrict__ perm,
                                                                  int32_t* __restrict__ sched, int32_t* __restrict__ err,
                                                                  int64_t active_off, int64_t tiles16_off,
-                                                                 int64_t tiles64_off, int64_t tiles128_off) {
+                                                                 int64_t tiles64_off) {
     __shared__ int s_hist[kSmallWaves][kSmallMaxA];
     __shared__ int s_off[kSmallMaxA];
     __shared__ int s_cnt[kSmallMaxA];
     __shared__ int s_pre16[kSmallMaxA];
     __shared__ int s_pre64[kSmallMaxA];
-    __shared__ int s_pre128[kSmallMaxA];
-    __shared__ int s_tot[5][kSmallWaves];
+    __shared__ int s_tot[4][kSmallWaves];
     __shared__ int s_err[kSmallWaves];
     const int tid = threadIdx.x;
     const int w = tid / kWave;
@@ -285,18 +272,16 @@ __global__ __launch_bounds__(kScanThreads) void seg_small_kernel(const int32_t* 
         counts[a] = c;
         s_cnt[a] = c;
     }
-    int tc, t16, t64, t128, tact;
+    int tc, t16, t64, tact;
     const int ec = block_exclusive_scan(c, s_tot[0], &tc);
     const int e16 = block_exclusive_scan((c + 15) / 16, s_tot[1], &t16);
     const int e64 = block_exclusive_scan((c + 63) / 64, s_tot[2], &t64);
-    const int e128 = block_exclusive_scan((c + 127) / 128, s_tot[4], &t128);
     const int eact = block_exclusive_scan(c > 0 ? 1 : 0, s_tot[3], &tact);
     if (a < A) {
         offsets[a] = ec;
         s_off[a] = ec;
         s_pre16[a] = e16;
         s_pre64[a] = e64;
-        s_pre128[a] = e128;
         if (c > 0) sched[active_off + eact] = a;
     }
     if (tid == 0) {
@@ -304,7 +289,7 @@ __global__ __launch_bounds__(kScanThreads) void seg_small_kernel(const int32_t* 
         sched[0] = t16;
         sched[1] = t64;
         sched[2] = tact;
-        sched[3] = t128;
+        sched[3] = 0;
         int e = 0;
         for (int v = 0; v < kSmallWaves; ++v) e += s_err[v];
         err[0] = e;
@@ -348,11 +333,6 @@ __global__ __launch_bounds__(kScanThreads) void seg_small_kernel(const int32_t* 
                         *reinterpret_cast<int4*>(sched + tiles64_off + 4 * (int64_t)(s_pre64[lid] + local / 64)) =
                             make_int4(lid, pos, rows, 0);
                     }
-                    if ((local & 127) == 0) {
-                        const int rows = cnt - local < 128 ? cnt - local : 128;
-                        *reinterpret_cast<int4*>(sched + tiles128_off + 4 * (int64_t)(s_pre128[lid] + local / 128)) =
-                            make_int4(lid, pos, rows, 0);
-                    }
                 }
                 if (lane == leader) s_hist[w][lid] += __popcll(m);
             }
@@ -384,17 +364,16 @@ extern "C" int lora_segments_build(const int32_t* adapter_ids, int32_t T, int32_
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (T <= kSmallMaxT && num_adapters <= kSmallMaxA) {
         hipLaunchKernelGGL(seg_small_kernel, dim3(1), dim3(kScanThreads), 0, st, adapter_ids, T, num_adapters,
-                           seg.counts, seg.offsets, seg.perm, seg.sched, seg.err, sl.active, sl.tiles16, sl.tiles64,
-                           sl.tiles128);
+                           seg.counts, seg.offsets, seg.perm, seg.sched, seg.err, sl.active, sl.tiles16, sl.tiles64);
         return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
     }
     hipLaunchKernelGGL(seg_count_kernel, dim3(nchunks), dim3(kChunk), 0, st, adapter_ids, T, num_adapters, nchunks,
                        wsi + w.hist, wsi + w.rank, wsi + w.errc);
     hipLaunchKernelGGL(seg_scan_kernel, dim3(1), dim3(kScanThreads), 0, st, num_adapters, nchunks, wsi + w.hist,
-                       wsi + w.errc, seg.counts, seg.offsets, seg.sched, wsi + w.pre16, wsi + w.pre64, wsi + w.pre128,
-                       seg.err, sl.active);
+                       wsi + w.errc, seg.counts, seg.offsets, seg.sched, wsi + w.pre16, wsi + w.pre64, seg.err,
+                       sl.active);
     hipLaunchKernelGGL(seg_scatter_kernel, dim3(nchunks), dim3(kChunk), 0, st, adapter_ids, T, num_adapters, nchunks,
-                       wsi + w.hist, wsi + w.rank, seg.counts, seg.offsets, wsi + w.pre16, wsi + w.pre64,
-                       wsi + w.pre128, seg.perm, seg.sched, sl.tiles16, sl.tiles64, sl.tiles128);
+                       wsi + w.hist, wsi + w.rank, seg.counts, seg.offsets, wsi + w.pre16, wsi + w.pre64, seg.perm,
+                       seg.sched, sl.tiles16, sl.tiles64);
     return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
