@@ -235,9 +235,9 @@ def main():
         st["grads"] = lb.GradTable(st["dA"], st["dB"])
         st["seg"] = lb.Segments(T, wl.num_adapters, dev)
         st["seg_ft"] = lb.Segments(n, wl.num_adapters, dev)
-        st["ws"] = torch.empty(lb.lora_backward_workspace_bytes(n, wl.d_in, wl.d_out, st["table"].r_max),
+        st["ws"] = torch.empty(lb.lora_backward_workspace_bytes(torch.bfloat16, n, wl.d_in, wl.d_out, st["table"].r_max),
                                dtype=torch.uint8, device=dev)
-        st["ws_shrink"] = torch.empty(lb.lora_shrink_workspace_bytes(T, wl.d_in, st["table"].r_max),
+        st["ws_shrink"] = torch.empty(lb.lora_shrink_workspace_bytes(torch.bfloat16, T, wl.d_in, st["table"].r_max),
                                       dtype=torch.uint8, device=dev)
         sets.append(st)
     torch.cuda.synchronize()

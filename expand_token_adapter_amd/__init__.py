@@ -67,12 +67,12 @@ def lora_segments_workspace_bytes(T: int, num_adapters: int) -> int:
     return _abi.load().lora_segments_workspace_bytes(T, num_adapters)
 
 
-def lora_shrink_workspace_bytes(T: int, d_in: int, r_max: int) -> int:
-    return _abi.load().lora_shrink_workspace_bytes(T, d_in, r_max)
+def lora_shrink_workspace_bytes(dtype: torch.dtype, T: int, d_in: int, r_max: int) -> int:
+    return _abi.load().lora_shrink_workspace_bytes(_DTYPES[dtype], T, d_in, r_max)
 
 
-def lora_backward_workspace_bytes(T_ft: int, d_in: int, d_out: int, r_max: int) -> int:
-    return _abi.load().lora_backward_workspace_bytes(T_ft, d_in, d_out, r_max)
+def lora_backward_workspace_bytes(dtype: torch.dtype, T_ft: int, d_in: int, d_out: int, r_max: int) -> int:
+    return _abi.load().lora_backward_workspace_bytes(_DTYPES[dtype], T_ft, d_in, d_out, r_max)
 
 
 def lora_segments_sched_elems(T: int, num_adapters: int) -> int:
@@ -201,7 +201,7 @@ def lora_shrink(x: torch.Tensor, adapters: AdapterTable, seg: Segments, v: Optio
         v = torch.zeros((T, (r_max + 7) // 8 * 8), dtype=torch.float32, device=x.device)
     pv, _, _, ldv = _rows(v, "v")
     lib = _abi.load()
-    need = lib.lora_shrink_workspace_bytes(T, d_in, r_max)
+    need = lib.lora_shrink_workspace_bytes(_dtype_code(x), T, d_in, r_max)
     if ws is None or ws.numel() < need:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     st = lib.lora_shrink(_dtype_code(x), px, ldx, T, d_in, adapters.ptr, len(adapters), r_max, seg.c,
@@ -246,7 +246,7 @@ def lora_backward(x: torch.Tensor, dy: torch.Tensor, adapters: AdapterTable, gra
         raise ValueError("the gradient table must have one entry per adapter")
     r_max = adapters.r_max if r_max is None else r_max
     lib = _abi.load()
-    need = lib.lora_backward_workspace_bytes(T, d_in, d_out, r_max)
+    need = lib.lora_backward_workspace_bytes(_dtype_code(x), T, d_in, d_out, r_max)
     if ws is None or ws.numel() < need:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     st = lib.lora_backward(_dtype_code(x), px, ldx, pdy, lddy, pdx or None, lddx, T, d_in, d_out, adapters.ptr,

@@ -45,8 +45,8 @@ SIGNATURES = {
     "lora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "lora_segments_sched_elems": (_sz, [_i32, _i32]),
     "lora_segments_workspace_bytes": (_sz, [_i32, _i32]),
-    "lora_shrink_workspace_bytes": (_sz, [_i32, _i32, _i32]),
-    "lora_backward_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
+    "lora_shrink_workspace_bytes": (_sz, [ctypes.c_int, _i32, _i32, _i32]),
+    "lora_backward_workspace_bytes": (_sz, [ctypes.c_int, _i32, _i32, _i32, _i32]),
     "lora_segments_build": (ctypes.c_int, [_vp, _i32, _i32, LoraSegments, _vp, _sz, _vp]),
     "lora_shrink": (ctypes.c_int, [ctypes.c_int, _vp, _i64, _i32, _i32, _vp, _i32, _i32, LoraSegments,
                                    _vp, _i64, _vp, _sz, _vp]),

@@ -22,7 +22,7 @@ namespace lora {
 int run_shrink(int dtype, bool trans_w, const ShrinkParams& p, const ReduceParams& rp, int32_t T, int32_t num_adapters,
                hipStream_t st);
 int64_t shrink_part_ld(int32_t r_max);
-int64_t shrink_part_floats(int32_t T, int32_t K, int32_t r_max);
+int64_t shrink_part_floats(int dtype, int32_t T, int32_t K, int32_t r_max);
 int run_expand(int dtype, bool trans_w, const ExpandParams& p, int32_t T, int32_t num_adapters, int32_t r_max,
                hipStream_t st);
 
@@ -32,7 +32,7 @@ int run_expand(int dtype, bool trans_w, const ExpandParams& p, int32_t T, int32_
 struct BwdWs {
     int64_t ldg, ldT;               // pitch of g rows; pitch of the rank-major arrays
     int64_t g, gT, vT, part, total; // offsets
-    static BwdWs make(int64_t T, int64_t d_in, int64_t d_out, int64_t r_max) {
+    static BwdWs make(int dtype, int64_t T, int64_t d_in, int64_t d_out, int64_t r_max) {
         BwdWs w;
         w.ldg = round_up(r_max, 8);
         w.ldT = round_up(T > 0 ? T : 1, 32);
@@ -40,8 +40,8 @@ struct BwdWs {
         w.gT = round_up(w.g + T * w.ldg, 64);
         w.vT = round_up(w.gT + r_max * w.ldT, 64);
         w.part = round_up(w.vT + r_max * w.ldT, 64);
-        const int64_t np = std::max(shrink_part_floats((int32_t)T, (int32_t)d_in, (int32_t)r_max),
-                                    shrink_part_floats((int32_t)T, (int32_t)d_out, (int32_t)r_max));
+        const int64_t np = std::max(shrink_part_floats(dtype, (int32_t)T, (int32_t)d_in, (int32_t)r_max),
+                                    shrink_part_floats(dtype, (int32_t)T, (int32_t)d_out, (int32_t)r_max));
         w.total = round_up(w.part + np, 64);
         return w;
     }
@@ -64,9 +64,9 @@ __global__ void transpose_v_kernel(const float* __restrict__ v, int64_t ldv, con
 }
 }  // namespace
 
-extern "C" size_t lora_backward_workspace_bytes(int32_t T_ft, int32_t d_in, int32_t d_out, int32_t r_max) {
-    if (T_ft < 0 || d_in < 1 || d_out < 1 || r_max < 1 || r_max > LORA_MAX_RANK) return 0;
-    return (size_t)BwdWs::make(T_ft, d_in, d_out, r_max).total * sizeof(float);
+extern "C" size_t lora_backward_workspace_bytes(int dtype, int32_t T_ft, int32_t d_in, int32_t d_out, int32_t r_max) {
+    if (!valid_dtype(dtype) || T_ft < 0 || d_in < 1 || d_out < 1 || r_max < 1 || r_max > LORA_MAX_RANK) return 0;
+    return (size_t)BwdWs::make(dtype, T_ft, d_in, d_out, r_max).total * sizeof(float);
 }
 
 extern "C" int lora_backward(int dtype, const void* x, int64_t ldx, const void* dy, int64_t lddy, void* dx,
@@ -83,7 +83,7 @@ extern "C" int lora_backward(int dtype, const void* x, int64_t ldx, const void* 
     if (dx && (rc = check_matrix(dx, d_in, lddx)) != LORA_OK) return rc;
     if (v_saved && (rc = check_f32_rows(v_saved, ldv, r_max)) != LORA_OK) return rc;
     if (!seg_ft.offsets) return LORA_ERR_INVALID_ARG;
-    const BwdWs w = BwdWs::make(T_ft, d_in, d_out, r_max);
+    const BwdWs w = BwdWs::make(dtype, T_ft, d_in, d_out, r_max);
     if (!ws || !aligned16(ws) || ws_bytes < (size_t)w.total * sizeof(float)) return LORA_ERR_WORKSPACE;
 
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -106,7 +106,7 @@ extern "C" int lora_backward(int dtype, const void* x, int64_t ldx, const void* 
     sp.part = wsf + w.part;
     sp.ldp = shrink_part_ld(r_max);
     sp.slice_stride = (int64_t)T_ft * sp.ldp;
-    sp.nslices = shrink_slices(d_out);
+    sp.nslices = shrink_slices(dtype, d_out);
     sp.err = seg_ft.err;
     sp.rgroups = rank_groups(r_max);
     ReduceParams rp{};
@@ -137,7 +137,7 @@ extern "C" int lora_backward(int dtype, const void* x, int64_t ldx, const void* 
         vp.x = x;
         vp.ldx = ldx;
         vp.K = d_in;
-        vp.nslices = shrink_slices(d_in);
+        vp.nslices = shrink_slices(dtype, d_in);
         ReduceParams vr = rp;
         vr.nslices = vp.nslices;
         vr.out = nullptr;

@@ -11,6 +11,15 @@
 
 namespace lora {
 
+// Window i (0 <= i < n) of a wave's range, visited from a per-workgroup
+// starting point so that concurrent workgroups do not all read the same
+// lines at the same time.  The order is fixed per task, so results stay
+// bit-reproducible.
+__device__ __forceinline__ int rotated(int kc0, int n, int rot, int i) {
+    const int j = i + rot;
+    return kc0 + (j < n ? j : j - n);
+}
+
 // ============================================================== token contraction
 //
 // For each adapter a with fine-tuning rows, each group of 32 ranks and each

@@ -286,6 +286,21 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
     return __builtin_bit_cast(uint2, v);
 }
 
+// 16 bytes per lane from global memory straight into LDS: lane L's bytes
+// land at lds_row + 16 L (gfx950 global_load_lds_dwordx4; counted in vmcnt).
+__device__ __forceinline__ void lds_dma16(const void* src, void* lds_row) {
+    __builtin_amdgcn_global_load_lds((const LORA_GLOBAL void*)src,
+                                     (__attribute__((address_space(3))) void*)lds_row, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding:
+// vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_le() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 struct SchedLayout {
     int64_t active;    // [A] adapters with at least one row, ascending
     int64_t tiles16;   // [n16_max] records of up to 16 rows

@@ -43,42 +43,45 @@ int launch_expand_t(int ks, const ExpandParams& p, unsigned grid, hipStream_t st
 namespace lora {
 
 __global__ __launch_bounds__(256) void shrink_reduce_kernel(ReduceParams p) {
-    const int n = threadIdx.x >> 4;  // row of the tile
-    const int q = threadIdx.x & 15;  // rank group of 8
-    const int64_t n_tasks = p.sched[0];
-    for (int64_t tile = blockIdx.x; tile < n_tasks; tile += gridDim.x) {
+    const int wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int n = lane & 15;  // row of the tile
+    const int g = lane >> 4;  // first rank group of 8
+    const int64_t ntiles = p.sched[0];
+    for (int64_t tile = (int64_t)blockIdx.x * 4 + wave; tile < ntiles; tile += (int64_t)gridDim.x * 4) {
         const TileRec rec = load_tile(p.sched, p.tiles16_off, tile);
+        const int pos = rec.pos0 + (n < rec.rows ? n : 0);
+        const int64_t orow = p.out_by_pos ? pos : p.perm[pos];
         const lora_adapter ad = load_adapter(p.adapters, rec.adapter);
-        if (!adapter_ok(ad, p.r_max)) continue;  // counted by the shrink kernel
+        if (!adapter_ok(ad, p.r_max) || n >= rec.rows) continue;  // bad entries are counted by the shrink
         const int r = ad.rank;
-        const int k = 8 * q;
-        if (n >= rec.rows || k >= r) continue;
-        const int pos = rec.pos0 + n;
-        const float* src = p.part + (int64_t)pos * p.ldp + k;
-        f32x4_t a = f32x4_t{0.f, 0.f, 0.f, 0.f}, b = a;
-        for (int s = 0; s < p.nslices; ++s) {
-            const LORA_GLOBAL f32x4_t* v = gptr(reinterpret_cast<const f32x4_t*>(src + (int64_t)s * p.slice_stride));
-            a += v[0];
-            b += v[1];
-        }
-        // ranks r .. 8q+7 of the last group hold no partial: write zeros there
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (k + i >= r) a[i] = 0.f;
-            if (k + 4 + i >= r) b[i] = 0.f;
-        }
-        if (p.out) {
-            // k + 8 <= round_up(r_max, 8) <= ldo (a multiple of 8)
-            const int64_t row = p.out_by_pos ? pos : p.perm[pos];
-            float* dst = p.out + row * p.ldo + k;
-            *gptr(reinterpret_cast<f32x4_t*>(dst)) = a;
-            *gptr(reinterpret_cast<f32x4_t*>(dst + 4)) = b;
-        }
-        if (p.outT) {
+        for (int k = 8 * g; k < r; k += 32) {
+            const float* src = p.part + (int64_t)pos * p.ldp + k;
+            f32x4_t a = f32x4_t{0.f, 0.f, 0.f, 0.f}, b = a;
+#pragma unroll 4
+            for (int sl = 0; sl < p.nslices; ++sl) {
+                const LORA_GLOBAL f32x4_t* v = gptr(reinterpret_cast<const f32x4_t*>(src + (int64_t)sl * p.slice_stride));
+                a += v[0];
+                b += v[1];
+            }
+            // ranks r .. k + 7 of the last group hold no partial: zeros there
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                if (k + i < r) gptr(p.outT)[(int64_t)(k + i) * p.ldT + pos] = a[i];
-                if (k + 4 + i < r) gptr(p.outT)[(int64_t)(k + 4 + i) * p.ldT + pos] = b[i];
+                if (k + i >= r) a[i] = 0.f;
+                if (k + 4 + i >= r) b[i] = 0.f;
+            }
+            if (p.out) {
+                // k + 8 <= round_up(r_max, 8) <= ldo (a multiple of 8)
+                float* dst = p.out + orow * p.ldo + k;
+                *gptr(reinterpret_cast<f32x4_t*>(dst)) = a;
+                *gptr(reinterpret_cast<f32x4_t*>(dst + 4)) = b;
+            }
+            if (p.outT) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (k + i < r) gptr(p.outT)[(int64_t)(k + i) * p.ldT + pos] = a[i];
+                    if (k + 4 + i < r) gptr(p.outT)[(int64_t)(k + 4 + i) * p.ldT + pos] = b[i];
+                }
             }
         }
     }
@@ -93,15 +96,15 @@ int run_shrink(int dtype, bool trans_w, const ShrinkParams& p, const ReduceParam
     const int rc = dtype == LORA_BF16 ? launch_shrink_t<LORA_BF16>(trans_w, p, grid, st)
                                       : launch_shrink_t<LORA_F32>(trans_w, p, grid, st);
     if (rc != LORA_OK) return rc;
-    const unsigned rgrid = (unsigned)std::min<int64_t>(SchedLayout::max_tiles16(T, num_adapters), 4096);
+    const unsigned rgrid = (unsigned)std::min<int64_t>((SchedLayout::max_tiles16(T, num_adapters) + 3) / 4, 4096);
     hipLaunchKernelGGL(shrink_reduce_kernel, dim3(rgrid), dim3(256), 0, st, rp);
     return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
 // Workspace of the split-K partials: [slices][T][round_up(r_max, 8)] fp32.
 int64_t shrink_part_ld(int32_t r_max) { return round_up(r_max, 8); }
-int64_t shrink_part_floats(int32_t T, int32_t K, int32_t r_max) {
-    return (int64_t)shrink_slices(K) * (T > 0 ? T : 1) * shrink_part_ld(r_max);
+int64_t shrink_part_floats(int dtype, int32_t T, int32_t K, int32_t r_max) {
+    return (int64_t)shrink_slices(dtype, K) * (T > 0 ? T : 1) * shrink_part_ld(r_max);
 }
 
 int run_expand(int dtype, bool trans_w, const ExpandParams& p, int32_t T, int32_t num_adapters, int32_t r_max,
@@ -120,9 +123,9 @@ int run_expand(int dtype, bool trans_w, const ExpandParams& p, int32_t T, int32_
 
 }  // namespace lora
 
-extern "C" size_t lora_shrink_workspace_bytes(int32_t T, int32_t d_in, int32_t r_max) {
-    if (T < 0 || d_in < 1 || r_max < 1 || r_max > LORA_MAX_RANK) return 0;
-    return (size_t)shrink_part_floats(T, d_in, r_max) * sizeof(float);
+extern "C" size_t lora_shrink_workspace_bytes(int dtype, int32_t T, int32_t d_in, int32_t r_max) {
+    if (!valid_dtype(dtype) || T < 0 || d_in < 1 || r_max < 1 || r_max > LORA_MAX_RANK) return 0;
+    return (size_t)shrink_part_floats(dtype, T, d_in, r_max) * sizeof(float);
 }
 
 extern "C" int lora_shrink(int dtype, const void* x, int64_t ldx, int32_t T, int32_t d_in,
@@ -134,7 +137,7 @@ extern "C" int lora_shrink(int dtype, const void* x, int64_t ldx, int32_t T, int
     if (T == 0) return LORA_OK;
     if ((rc = check_matrix(x, d_in, ldx)) != LORA_OK) return rc;
     if ((rc = check_f32_rows(v, ldv, r_max)) != LORA_OK) return rc;
-    if (!ws || !aligned16(ws) || ws_bytes < (size_t)shrink_part_floats(T, d_in, r_max) * sizeof(float))
+    if (!ws || !aligned16(ws) || ws_bytes < (size_t)shrink_part_floats(dtype, T, d_in, r_max) * sizeof(float))
         return LORA_ERR_WORKSPACE;
     const SchedLayout sl = SchedLayout::make(T, num_adapters);
     ShrinkParams p{};
@@ -149,7 +152,7 @@ extern "C" int lora_shrink(int dtype, const void* x, int64_t ldx, int32_t T, int
     p.part = static_cast<float*>(ws);
     p.ldp = shrink_part_ld(r_max);
     p.slice_stride = (int64_t)T * p.ldp;
-    p.nslices = shrink_slices(d_in);
+    p.nslices = shrink_slices(dtype, d_in);
     p.err = seg.err;
     p.rgroups = rank_groups(r_max);
     ReduceParams rp{};

@@ -136,10 +136,10 @@ size_t lora_segments_sched_elems(int32_t T, int32_t num_adapters);
 size_t lora_segments_workspace_bytes(int32_t T, int32_t num_adapters);
 
 /* Workspace bytes of lora_shrink (host, pure). */
-size_t lora_shrink_workspace_bytes(int32_t T, int32_t d_in, int32_t r_max);
+size_t lora_shrink_workspace_bytes(int dtype, int32_t T, int32_t d_in, int32_t r_max);
 
 /* Workspace bytes of lora_backward for T_ft rows (host, pure). */
-size_t lora_backward_workspace_bytes(int32_t T_ft, int32_t d_in, int32_t d_out, int32_t r_max);
+size_t lora_backward_workspace_bytes(int dtype, int32_t T_ft, int32_t d_in, int32_t d_out, int32_t r_max);
 
 /*
  * Group the rows of a batch by adapter: which weights each row applies
@@ -161,9 +161,10 @@ int lora_segments_build(const int32_t* adapter_ids, int32_t T, int32_t num_adapt
  *   lora_segments_build over the same T rows, v [T, ldv] fp32 output
  *   (ldv >= r_max, multiple of 8).  Row t of v receives columns 0..r_a-1
  *   and zeros in columns r_a..round_up(r_a, 8)-1; rows without an adapter
- *   are left unchanged.  ws: lora_shrink_workspace_bytes(T, d_in, r_max) bytes of
- *   device memory (the sum over d_in is split into 1024-wide slices whose
- *   partials are added in slice order).  Two kernels.
+ *   are left unchanged.  ws: lora_shrink_workspace_bytes(dtype, T, d_in, r_max)
+ *   bytes of device memory (the sum over d_in is split into slices of 512
+ *   (bf16) or 256 (fp32) elements whose partials are added in slice order).
+ *   Two kernels.
  */
 int lora_shrink(int dtype, const void* x, int64_t ldx, int32_t T, int32_t d_in,
                 const lora_adapter* adapters, int32_t num_adapters, int32_t r_max,
@@ -193,8 +194,8 @@ int lora_expand_add(int dtype, const float* v, int64_t ldv, int32_t T, int32_t d
  *         0..T_ft-1 refer to x, dy, dx)
  *   v_saved [T_ft, ldv] fp32: v = A x of these rows as lora_shrink wrote it,
  *         or NULL to recompute it from x
- *   ws: lora_backward_workspace_bytes(T_ft, d_in, d_out, r_max) bytes of
- *         device memory.
+ *   ws: lora_backward_workspace_bytes(dtype, T_ft, d_in, d_out, r_max) bytes
+ *         of device memory.
  * The caller passes a compact view of the fine-tuning rows; a contiguous
  * fine-tuning tail of a mixed batch is passed by pointer offset, no copy.
  */

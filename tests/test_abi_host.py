@@ -51,13 +51,17 @@ def test_workspace_queries(lib):
     a = lib.lora_segments_workspace_bytes(1000, 32)
     b = lib.lora_segments_workspace_bytes(5000, 32)
     assert b > a >= 4 * 1000
-    assert lib.lora_backward_workspace_bytes(2048, 4096, 14336, 64) >= 3 * 2048 * 64 * 4
-    assert lib.lora_backward_workspace_bytes(16, 256, 256, 0) == 0
-    assert lib.lora_backward_workspace_bytes(16, 256, 256, 129) == 0
-    # split-K partials: one 1024-wide slice of d_in per [T, round_up(r_max, 8)] fp32 block
-    assert lib.lora_shrink_workspace_bytes(100, 4096, 20) == 4 * 100 * 24 * 4
-    assert lib.lora_shrink_workspace_bytes(100, 1000, 8) == 1 * 100 * 8 * 4
-    assert lib.lora_shrink_workspace_bytes(100, 0, 8) == 0
+    assert lib.lora_backward_workspace_bytes(0, 2048, 4096, 14336, 64) >= 3 * 2048 * 64 * 4
+    assert lib.lora_backward_workspace_bytes(0, 16, 256, 256, 0) == 0
+    assert lib.lora_backward_workspace_bytes(0, 16, 256, 256, 129) == 0
+    assert lib.lora_backward_workspace_bytes(7, 16, 256, 256, 8) == 0
+    # split-K partials: one [T, round_up(r_max, 8)] fp32 block per slice of d_in
+    # (512 elements for bf16, 256 for fp32)
+    assert lib.lora_shrink_workspace_bytes(0, 100, 4096, 20) == 8 * 100 * 24 * 4
+    assert lib.lora_shrink_workspace_bytes(1, 100, 4096, 20) == 16 * 100 * 24 * 4
+    assert lib.lora_shrink_workspace_bytes(0, 100, 1000, 8) == 2 * 100 * 8 * 4
+    assert lib.lora_shrink_workspace_bytes(0, 100, 0, 8) == 0
+    assert lib.lora_shrink_workspace_bytes(3, 100, 256, 8) == 0
     # 16-row and 64-row tile records for every row plus one partial tile per adapter
     n = lib.lora_segments_sched_elems(1000, 10)
     assert n >= 4 * ((1000 + 15) // 16 + 10) + 4 * ((1000 + 63) // 64 + 10)
@@ -92,7 +96,7 @@ def _seg(ok=True):
 def test_shrink_and_expand_reject_bad_arguments(lib, kw, code):
     a = dict(dtype=0, T=64, A=4, r_max=8, adapters=FAKE, seg_ok=True, x=FAKE, ld=256, d=256, v=FAKE, ldv=8)
     a.update(kw)
-    need = lib.lora_shrink_workspace_bytes(max(a["T"], 0), max(a["d"], 1), min(max(a["r_max"], 1), 128))
+    need = lib.lora_shrink_workspace_bytes(0, max(a["T"], 0), max(a["d"], 1), min(max(a["r_max"], 1), 128))
     st = lib.lora_shrink(a["dtype"], a["x"], a["ld"], a["T"], a["d"], a["adapters"], a["A"], a["r_max"],
                          _seg(a["seg_ok"]), a["v"], a["ldv"], FAKE, need, None)
     assert st == code
@@ -123,7 +127,7 @@ def test_segments_build_rejects(lib):
 
 
 def test_shrink_workspace_rejected(lib):
-    need = lib.lora_shrink_workspace_bytes(64, 256, 8)
+    need = lib.lora_shrink_workspace_bytes(0, 64, 256, 8)
     args = (0, FAKE, 256, 64, 256, FAKE, 4, 8, _seg(), FAKE, 8)
     assert lib.lora_shrink(*args, FAKE, need - 1, None) == _abi.LORA_ERR_WORKSPACE
     assert lib.lora_shrink(*args, 0, need, None) == _abi.LORA_ERR_WORKSPACE
@@ -131,7 +135,7 @@ def test_shrink_workspace_rejected(lib):
 
 
 def test_backward_rejects(lib):
-    need = lib.lora_backward_workspace_bytes(16, 256, 256, 8)
+    need = lib.lora_backward_workspace_bytes(0, 16, 256, 256, 8)
 
     def call(**kw):
         a = dict(dtype=0, x=FAKE, ldx=256, dy=FAKE, lddy=256, dx=FAKE, lddx=256, T=16, d_in=256, d_out=256,
