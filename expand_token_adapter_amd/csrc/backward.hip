@@ -49,7 +49,7 @@ struct BwdWs {
 }  // namespace lora
 
 namespace {
-constexpr int64_t kMaxContractGrid = 4096;
+constexpr int64_t kMaxContractGrid = 512;  // two resident workgroups per CU
 
 // vT[k][pos] = v[perm[pos]][k] for pos < n_valid, k < r_max: the caller's saved v,
 // rank-major by sorted position as the token contraction reads it.
@@ -187,10 +187,9 @@ extern "C" int lora_backward(int dtype, const void* x, int64_t ldx, const void* 
     const int64_t max_active = num_adapters < T_ft ? num_adapters : T_ft;
     const int64_t tasks = max_active * cp.rgroups * (cp.ncb_in + cp.ncb_out);
     const unsigned grid = grid_for(tasks, 1, kMaxContractGrid);
-    const dim3 block(kContractWaves * kWave);
     if (dtype == LORA_BF16)
-        hipLaunchKernelGGL(contract_kernel<LORA_BF16>, dim3(grid), block, 0, st, cp);
+        hipLaunchKernelGGL(contract_kernel<LORA_BF16>, dim3(grid), dim3(contract_waves<LORA_BF16>() * kWave), 0, st, cp);
     else
-        hipLaunchKernelGGL(contract_kernel<LORA_F32>, dim3(grid), block, 0, st, cp);
+        hipLaunchKernelGGL(contract_kernel<LORA_F32>, dim3(grid), dim3(contract_waves<LORA_F32>() * kWave), 0, st, cp);
     return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }

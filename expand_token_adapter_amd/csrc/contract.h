@@ -22,7 +22,7 @@ __device__ __forceinline__ int rotated(int kc0, int n, int rot, int i) {
 
 // ============================================================== token contraction
 //
-// For each adapter a with fine-tuning rows, each group of 32 ranks and each
+// For each adapter a with fine-tuning rows, each group of 16 ranks and each
 // block of 64 columns:
 //   dA_a[k][c] += s_a * sum_rows g[row][k] * x[row][c]      (c < d_in)
 //   dB_a[c][k] += s_a * sum_rows dy[row][c] * v[row][k]     (c < d_out)
@@ -31,13 +31,17 @@ __device__ __forceinline__ int rotated(int kc0, int n, int rot, int i) {
 // tiles are stored as loaded and read back transposed with
 // ds_read_b64_tr_b16; fp32 tiles are written transposed element by element.
 // g and v come rank-major ([k][sorted position]) from the shrink kernel.
-// Four waves split the adapter's rows into contiguous ranges, two 32-row
-// windows per iteration with all loads issued first; their partial tiles
-// are summed in wave order through LDS and added to dA / dB, which no other
+// The waves (eight for bf16, four for fp32) split the adapter's rows into
+// contiguous ranges of 32-row windows.  Each wave runs two interleaved
+// streams of windows: while one window is multiplied, the next window of
+// the other stream is in flight, and the row indices (perm) of each stream
+// are fetched one window ahead of its data.  The waves' partial tiles are
+// summed in wave order through LDS and added to dA / dB, which no other
 // workgroup touches.
 
-constexpr int kContractWaves = 4;
-constexpr int kContractMB = 2;    // 16-rank blocks per task (32 ranks)
+template <int DT>
+__host__ __device__ constexpr int contract_waves() { return DT == LORA_BF16 ? 8 : 4; }
+constexpr int kContractMB = 1;    // 16-rank blocks per task
 constexpr int kCtPitch = 32 + 8;  // fp32 path: LDS pitch (elements) of a transposed column
 constexpr int kQPitch = 64 + 8;   // bf16 path: LDS pitch (elements) of a staged row
 
@@ -67,8 +71,8 @@ struct ContractLds {
     static constexpr int EB = Frag<DT>::kBytes;
     // per wave: two window tiles
     static constexpr int kTileBytes = DT == LORA_BF16 ? 32 * kQPitch * 2 : 64 * kCtPitch * 4;
-    static constexpr int kTransBytes = kContractWaves * 2 * kTileBytes;
-    static constexpr int kRedBytes = kContractWaves * kContractMB * 4 * kWave * 16;
+    static constexpr int kTransBytes = contract_waves<DT>() * 2 * kTileBytes;
+    static constexpr int kRedBytes = contract_waves<DT>() * kContractMB * 4 * kWave * 16;
     static constexpr int kBytes = kTransBytes > kRedBytes ? kTransBytes : kRedBytes;
 };
 
@@ -80,19 +84,23 @@ struct ContractWin {
     f32x4_t pv[kContractMB][2];
 };
 
-template <int DT>
-__device__ __forceinline__ void contract_load(ContractWin<DT>& W, const char* q, int64_t ldq, const float* PT,
-                                              int64_t ldT, const int32_t* perm, int win, int lo, int hi, int c0,
-                                              int lcol, int lrow, int rank0, int r, int lane) {
-    constexpr int EB = Frag<DT>::kBytes;
-    int64_t rows[4];
+// Row indices of this lane's 4 rows of a window (positions outside [lo, hi)
+// read row lo: finite data, P is zero there).
+__device__ __forceinline__ void contract_rows(int32_t* rows, const int32_t* perm, int win, int lo, int hi, int lrow) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int pos = win + lrow + j;
-        rows[j] = perm[pos >= lo && pos < hi ? pos : lo];  // outside the range: row lo (finite, P is zero there)
+        rows[j] = perm[pos >= lo && pos < hi ? pos : lo];
     }
+}
+
+template <int DT>
+__device__ __forceinline__ void contract_load(ContractWin<DT>& W, const char* q, int64_t ldq, const float* PT,
+                                              int64_t ldT, const int32_t* rows, int win, int c0, int lcol, int rank0,
+                                              int r, int lane) {
+    constexpr int EB = Frag<DT>::kBytes;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) W.q[j] = Frag<DT>::load(q + (rows[j] * ldq + c0 + lcol) * EB);
+    for (int j = 0; j < 4; ++j) W.q[j] = Frag<DT>::load(q + ((int64_t)rows[j] * ldq + c0 + lcol) * EB);
     const int pp = win + 8 * (lane >> 4);
 #pragma unroll
     for (int mb = 0; mb < kContractMB; ++mb) {
@@ -152,8 +160,10 @@ __device__ __forceinline__ void contract_compute(const ContractWin<DT>& W, char*
 }
 
 template <int DT>
-__global__ __launch_bounds__(kContractWaves * kWave) void contract_kernel(ContractParams p) {
+__global__ __launch_bounds__(contract_waves<DT>() * kWave) __attribute__((amdgpu_waves_per_eu(DT == LORA_BF16 ? 4 : 2)))
+void contract_kernel(ContractParams p) {
     using F = Frag<DT>;
+    constexpr int NW = contract_waves<DT>();
     __shared__ __attribute__((aligned(16))) char s_mem[ContractLds<DT>::kBytes];
 
     const int wave = threadIdx.x / kWave;
@@ -161,7 +171,16 @@ __global__ __launch_bounds__(kContractWaves * kWave) void contract_kernel(Contra
     const int lr = lane & 15;
     const int lg = lane >> 4;
     const int ncb = p.ncb_in + p.ncb_out;
-    const int64_t n_tasks = (int64_t)p.sched[2] * p.rgroups * ncb;
+    // Rank groups: enough for the largest rank among the adapters with rows
+    // (bad table entries count as r_max; they are reported per task below).
+    const int n_act = p.sched[2];
+    int rmax_act = 1;
+    for (int i = 0; i < n_act; ++i) {
+        const int rk = p.adapters[p.sched[p.active_off + i]].rank;
+        rmax_act = max(rmax_act, rk >= 1 && rk <= p.r_max ? rk : p.r_max);
+    }
+    const int rgroups = min(p.rgroups, (rmax_act + 16 * kContractMB - 1) / (16 * kContractMB));
+    const int64_t n_tasks = (int64_t)n_act * rgroups * ncb;
     const TaskSlice ts = xcd_slice(n_tasks, 1, 0);
     char* tileA = s_mem + (2 * wave) * ContractLds<DT>::kTileBytes;
     char* tileB = s_mem + (2 * wave + 1) * ContractLds<DT>::kTileBytes;
@@ -170,9 +189,11 @@ __global__ __launch_bounds__(kContractWaves * kWave) void contract_kernel(Contra
     const int lcol = 8 * (lane & 7);
 
     for (int64_t task = ts.begin; task < ts.end; task += ts.stride) {
-        const int cb_all = (int)(task % ncb);
-        const int rg = (int)((task / ncb) % p.rgroups);
-        const int act = (int)(task / ((int64_t)ncb * p.rgroups));
+        // rank group fastest: groups past an adapter's rank exit at once, and
+        // the remaining tasks spread evenly over the XCDs' contiguous ranges
+        const int rg = (int)(task % rgroups);
+        const int cb_all = (int)((task / rgroups) % ncb);
+        const int act = (int)(task / ((int64_t)ncb * rgroups));
         const int a = p.sched[p.active_off + act];
         const lora_adapter ad = load_adapter(p.adapters, a);
         const lora_adapter_grad gr = load_grad(p.grads, a);
@@ -199,8 +220,8 @@ __global__ __launch_bounds__(kContractWaves * kWave) void contract_kernel(Contra
         // 32-aligned windows of sorted positions covering [lo, hi), split over the waves.
         const int w0 = lo & ~31;
         const int nwin = (hi - w0 + 31) / 32;
-        const int wa = w0 + 32 * (int)((int64_t)wave * nwin / kContractWaves);
-        const int wb = w0 + 32 * (int)((int64_t)(wave + 1) * nwin / kContractWaves);
+        const int wa = w0 + 32 * (int)((int64_t)wave * nwin / NW);
+        const int wb = w0 + 32 * (int)((int64_t)(wave + 1) * nwin / NW);
 
         f32x4_t acc[kContractMB][4];
 #pragma unroll
@@ -209,21 +230,32 @@ __global__ __launch_bounds__(kContractWaves * kWave) void contract_kernel(Contra
             for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
         // Windows visited from a task-dependent start (the column blocks of one
-        // adapter read the same g / v windows); fixed order per task.
+        // adapter read the same g / v windows); fixed order per task.  Two
+        // streams: A takes windows 0, 2, 4, ..., B takes 1, 3, 5, ...; indices
+        // past the range repeat the last window (loaded, never multiplied).
         const int nw = (wb - wa) / 32;
-        const int rot = nw > 0 ? (int)(task % nw) : 0;
-        for (int i = 0; i < nw; i += 2) {
-            const bool two = i + 1 < nw;
-            const int wa0 = wa + 32 * (rotated(0, nw, rot, i));
-            const int wa1 = two ? wa + 32 * (rotated(0, nw, rot, i + 1)) : wa0;
-            ContractWin<DT> W0, W1;
-            contract_load<DT>(W0, q, ldq, PT, p.ldT, p.perm, wa0, lo, hi, cq, lcol, lrow, rank0, r, lane);
-            contract_load<DT>(W1, q, ldq, PT, p.ldT, p.perm, wa1, lo, hi, cq, lcol, lrow, rank0, r, lane);
-            contract_compute<DT>(W0, tileA, acc, wa0, lo, hi, lcol, lrow, nmb, lane);
-            if (two) contract_compute<DT>(W1, tileB, acc, wa1, lo, hi, lcol, lrow, nmb, lane);
+        if (nw > 0) {
+            const int rot = (int)(task % nw);
+            auto win_at = [&](int i) { return wa + 32 * rotated(0, nw, rot, i < nw ? i : nw - 1); };
+            int32_t rowsA[4], rowsB[4];
+            ContractWin<DT> WA, WB;
+            contract_rows(rowsA, p.perm, win_at(0), lo, hi, lrow);
+            contract_rows(rowsB, p.perm, win_at(1), lo, hi, lrow);
+            contract_load<DT>(WA, q, ldq, PT, p.ldT, rowsA, win_at(0), cq, lcol, rank0, r, lane);
+            contract_rows(rowsA, p.perm, win_at(2), lo, hi, lrow);
+            contract_load<DT>(WB, q, ldq, PT, p.ldT, rowsB, win_at(1), cq, lcol, rank0, r, lane);
+            contract_rows(rowsB, p.perm, win_at(3), lo, hi, lrow);
+            for (int i = 0; i < nw; i += 2) {
+                contract_compute<DT>(WA, tileA, acc, win_at(i), lo, hi, lcol, lrow, nmb, lane);
+                contract_load<DT>(WA, q, ldq, PT, p.ldT, rowsA, win_at(i + 2), cq, lcol, rank0, r, lane);
+                contract_rows(rowsA, p.perm, win_at(i + 4), lo, hi, lrow);
+                if (i + 1 < nw) contract_compute<DT>(WB, tileB, acc, win_at(i + 1), lo, hi, lcol, lrow, nmb, lane);
+                contract_load<DT>(WB, q, ldq, PT, p.ldT, rowsB, win_at(i + 3), cq, lcol, rank0, r, lane);
+                contract_rows(rowsB, p.perm, win_at(i + 5), lo, hi, lrow);
+            }
         }
 
-        // Fixed-order sum of the four waves' tiles.
+        // Fixed-order sum of the waves' tiles; wave nb (< 4) finishes column block nb.
         __syncthreads();
         f32x4_t* red = reinterpret_cast<f32x4_t*>(s_mem);
 #pragma unroll
@@ -231,15 +263,15 @@ __global__ __launch_bounds__(kContractWaves * kWave) void contract_kernel(Contra
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb) red[((wave * kContractMB + mb) * 4 + nb) * kWave + lane] = acc[mb][nb];
         __syncthreads();
-        {
-            const int nb = wave;  // this wave finishes column block nb
+        if (wave < 4) {
+            const int nb = wave;
             const float s = ad.scale;
 #pragma unroll
             for (int mb = 0; mb < kContractMB; ++mb) {
                 if (mb < nmb) {
                     f32x4_t sum = red[(mb * 4 + nb) * kWave + lane];
 #pragma unroll
-                    for (int w = 1; w < kContractWaves; ++w) sum += red[((w * kContractMB + mb) * 4 + nb) * kWave + lane];
+                    for (int w = 1; w < NW; ++w) sum += red[((w * kContractMB + mb) * 4 + nb) * kWave + lane];
                     const int col = c0 + 16 * nb + lr;
                     if (col < N) {
 #pragma unroll

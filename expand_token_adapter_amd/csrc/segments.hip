@@ -193,15 +193,29 @@ __global__ __launch_bounds__(kChunk) void seg_scatter_kernel(const int32_t* __re
 // For batches of up to kSmallMaxT rows and kSmallMaxA adapters the whole
 // build runs in one workgroup of 16 waves (one launch instead of three):
 //   1. wave w counts the ids of its contiguous row range into its own LDS
-//      histogram hist[w][a], one update per distinct id of each 64-row group;
+//      histogram hist[w][a], one update per distinct id of each 64-row group
+//      (lanes with equal ids are matched by one ballot per id bit);
 //   2. per adapter: counts = sum over w, hist[w][a] becomes the exclusive
 //      prefix over waves; a block scan over adapters gives offsets, the tile
 //      prefixes and the active list;
 //   3. wave w walks its rows in order, 64 at a time; inside a group the lanes
-//      that share an id are ranked by lane order (ballot), and the wave's
-//      cursor for that id advances by the group's count.  Every row's
+//      that share an id are ranked by lane order (the same ballot match), and
+//      the wave's cursor for that id advances by the group's count.  Every row's
 //      position is therefore its rank in row order: the same stable grouping
 //      as the three-kernel path.
+
+// Lanes of this wave holding the same valid id as the calling lane (0 for an
+// invalid one), from one ballot per bit of the ids (ids < 2^nbits): a lane
+// matches when it agrees on every bit.
+__device__ __forceinline__ uint64_t same_id_lanes(int id, bool valid, int nbits) {
+    uint64_t m = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+        const bool bit = (id >> b) & 1;
+        const uint64_t set = __ballot(valid && bit);
+        m &= bit ? set : ~set;
+    }
+    return valid ? m : 0ull;
+}
 
 constexpr int kSmallMaxA = 1024;
 constexpr int kSmallMaxT = 1 << 16;
@@ -227,6 +241,7 @@ __global__ __launch_bounds__(kScanThreads) void seg_small_kernel(const int32_t* 
     const int per = (T + kSmallWaves - 1) / kSmallWaves;
     const int r0 = min(T, w * per);
     const int r1 = min(T, r0 + per);
+    const int nbits = A > 1 ? 32 - __clz(A - 1) : 1;  // bits of the largest id
 
     for (int i = tid; i < kSmallWaves * kSmallMaxA; i += kScanThreads) (&s_hist[0][0])[i] = 0;
     __syncthreads();
@@ -244,16 +259,10 @@ __global__ __launch_bounds__(kScanThreads) void seg_small_kernel(const int32_t* 
             const int id = idv[g];
             const bool valid = id >= 0 && id < A;
             bad += (!valid && id != -1) ? 1 : 0;
-            // One pass per distinct id in the group: the lowest lane holding
-            // it adds the group's count to this wave's own histogram row.
-            uint64_t todo = __ballot(valid);
-            while (todo) {
-                const int leader = __ffsll((long long)todo) - 1;
-                const int lid = __shfl(id, leader, kWave);
-                const uint64_t m = __ballot(valid && id == lid);
-                todo &= ~m;
-                if (lane == leader) s_hist[w][lid] += __popcll(m);
-            }
+            // The lowest lane holding each id adds the group's count of that
+            // id to this wave's own histogram row.
+            const uint64_t m = same_id_lanes(id, valid, nbits);
+            if (valid && lane == __ffsll((long long)m) - 1) s_hist[w][id] += __popcll(m);
         }
     }
     bad = __reduce_add_sync(~0ull, bad);
@@ -311,31 +320,29 @@ __global__ __launch_bounds__(kScanThreads) void seg_small_kernel(const int32_t* 
             const int t = b + g * kWave + lane;
             const int id = idv[g];
             const bool valid = id >= 0 && id < A;
-            uint64_t todo = __ballot(valid);
-            while (todo) {
-                const int leader = __ffsll((long long)todo) - 1;
-                const int lid = __shfl(id, leader, kWave);
-                const uint64_t m = __ballot(valid && id == lid);
-                todo &= ~m;
-                if (valid && id == lid) {
-                    const int rank = __popcll(m & ((1ull << lane) - 1));
-                    const int local = s_hist[w][lid] + rank;  // position inside the adapter's group
-                    const int pos = s_off[lid] + local;
-                    perm[pos] = t;
-                    const int cnt = s_cnt[lid];
-                    if ((local & 15) == 0) {
-                        const int rows = cnt - local < 16 ? cnt - local : 16;
-                        *reinterpret_cast<int4*>(sched + tiles16_off + 4 * (int64_t)(s_pre16[lid] + local / 16)) =
-                            make_int4(lid, pos, rows, 0);
-                    }
-                    if ((local & 63) == 0) {
-                        const int rows = cnt - local < 64 ? cnt - local : 64;
-                        *reinterpret_cast<int4*>(sched + tiles64_off + 4 * (int64_t)(s_pre64[lid] + local / 64)) =
-                            make_int4(lid, pos, rows, 0);
-                    }
+            const uint64_t m = same_id_lanes(id, valid, nbits);
+            int cur = 0;
+            if (valid) cur = s_hist[w][id];
+            if (valid) {
+                const int rank = __popcll(m & ((1ull << lane) - 1));
+                const int local = cur + rank;  // position inside the adapter's group
+                const int pos = s_off[id] + local;
+                perm[pos] = t;
+                const int cnt = s_cnt[id];
+                if ((local & 15) == 0) {
+                    const int rows = cnt - local < 16 ? cnt - local : 16;
+                    *reinterpret_cast<int4*>(sched + tiles16_off + 4 * (int64_t)(s_pre16[id] + local / 16)) =
+                        make_int4(id, pos, rows, 0);
                 }
-                if (lane == leader) s_hist[w][lid] += __popcll(m);
+                if ((local & 63) == 0) {
+                    const int rows = cnt - local < 64 ? cnt - local : 64;
+                    *reinterpret_cast<int4*>(sched + tiles64_off + 4 * (int64_t)(s_pre64[id] + local / 64)) =
+                        make_int4(id, pos, rows, 0);
+                }
             }
+            // every lane has read its cursor: the lowest lane of each id advances it
+            __builtin_amdgcn_wave_barrier();
+            if (valid && lane == __ffsll((long long)m) - 1) s_hist[w][id] = cur + __popcll(m);
         }
     }
 }
