@@ -4,7 +4,8 @@ One step = the whole hot path over one mixed co-serving batch (seed 0):
   lora_segments_build (all rows) -> lora_shrink -> lora_expand_add
   -> lora_segments_build (fine-tuning rows) -> lora_backward (dX, dA, dB),
 with the forward's v of the fine-tuning rows passed to the backward as the
-saved v.  Workload: 128 decode rows, 8 prefill segments of U[128, 1024]
+saved v.  `--workload` selects another of the synthetic workloads (the
+backward runs only where the workload has fine-tuning rows).  Workload: 128 decode rows, 8 prefill segments of U[128, 1024]
 rows, 2 fine-tuning segments of 1024 rows on the reserved adapter; 32
 adapters with ranks drawn from {8, 16, 32, 64}, scale 2.0; d_in 4096 ->
 d_out 14336; bf16 elements (DeltaServe section 3.2, "Mixed forward batch").
@@ -32,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
+RANKS_DESC = {2: "16", 3: "U{8,16,32,64}", 4: "16", 5: "U{8,16,32,64,128}"}
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 
 
@@ -41,6 +43,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--sets", type=int, default=4, help="rotating copies of every buffer")
+    ap.add_argument("--workload", type=int, default=3, choices=(2, 3, 4, 5),
+                    help="synthetic workload (workloads.config index); 3 = the mixed co-serving batch")
     ap.add_argument("--graph", action="store_true", help="replay each step from a captured HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-min-seconds", type=float, default=10.0)
@@ -181,8 +185,9 @@ def cpu_baseline(wl, min_seconds):
     t0 = time.perf_counter()
     while True:
         oracle.forward(ref["x"], ref["ids"], ref["ranks"], ref["scales"], ref["A"], ref["B"], ref["y0"])
-        oracle.backward(ref["x"][s:s + n], ref["dy"], ref["ids"][s:s + n], ref["ranks"], ref["scales"],
-                        ref["A"], ref["B"])
+        if n > 0:
+            oracle.backward(ref["x"][s:s + n], ref["dy"], ref["ids"][s:s + n], ref["ranks"], ref["scales"],
+                            ref["A"], ref["B"])
         reps += 1
         el = time.perf_counter() - t0
         if el >= min_seconds or reps >= 50:
@@ -209,34 +214,38 @@ def main():
     import workloads
 
     dev = torch.device("cuda:0")
-    wl = workloads.config(3, seed=0)
+    wl = workloads.config(args.workload, seed=0)
     T, s, n = wl.T, wl.ft_start, wl.ft_count
+    has_ft = n > 0
     alg = algorithmic(wl)
 
     def dev_bf16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
 
     base = dict(A=[dev_bf16(a) for a in wl.A], B=[dev_bf16(b) for b in wl.B], x=dev_bf16(wl.x),
-                y=dev_bf16(wl.y0), dy=dev_bf16(wl.dy))
+                y=dev_bf16(wl.y0), dy=dev_bf16(wl.dy) if has_ft else None)
     ids = torch.from_numpy(wl.ids).to(dev)
     ft_ids = ids[s:s + n].contiguous()
-    r_ft = int(wl.ranks[0])
+    r_ft = int(wl.ranks[wl.ft_ids[0]]) if has_ft else None
     sets = []
     for k in range(args.sets):
         c = (lambda t: t) if k == 0 else (lambda t: t.clone())
         A = [c(a) for a in base["A"]]
         B = [c(b) for b in base["B"]]
         st = dict(A=A, B=B, table=lb.AdapterTable(A, B, wl.scales.tolist()), x=c(base["x"]), y=c(base["y"]),
-                  dy=c(base["dy"]), ids=ids.clone(), ft_ids=ft_ids.clone())
-        st["dx"] = torch.zeros((n, wl.d_in), dtype=torch.bfloat16, device=dev)
+                  ids=ids.clone())
         st["v"] = torch.zeros((T, (st["table"].r_max + 7) // 8 * 8), dtype=torch.float32, device=dev)
-        st["dA"] = [torch.zeros(a.shape, dtype=torch.float32, device=dev) for a in A]
-        st["dB"] = [torch.zeros(b.shape, dtype=torch.float32, device=dev) for b in B]
-        st["grads"] = lb.GradTable(st["dA"], st["dB"])
         st["seg"] = lb.Segments(T, wl.num_adapters, dev)
-        st["seg_ft"] = lb.Segments(n, wl.num_adapters, dev)
-        st["ws"] = torch.empty(lb.lora_backward_workspace_bytes(torch.bfloat16, n, wl.d_in, wl.d_out, st["table"].r_max),
-                               dtype=torch.uint8, device=dev)
+        if has_ft:
+            st["dy"] = c(base["dy"])
+            st["ft_ids"] = ft_ids.clone()
+            st["dx"] = torch.zeros((n, wl.d_in), dtype=torch.bfloat16, device=dev)
+            st["dA"] = [torch.zeros(a.shape, dtype=torch.float32, device=dev) for a in A]
+            st["dB"] = [torch.zeros(b.shape, dtype=torch.float32, device=dev) for b in B]
+            st["grads"] = lb.GradTable(st["dA"], st["dB"])
+            st["seg_ft"] = lb.Segments(n, wl.num_adapters, dev)
+            st["ws"] = torch.empty(lb.lora_backward_workspace_bytes(torch.bfloat16, n, wl.d_in, wl.d_out,
+                                                                    st["table"].r_max), dtype=torch.uint8, device=dev)
         st["ws_shrink"] = torch.empty(lb.lora_shrink_workspace_bytes(torch.bfloat16, T, wl.d_in, st["table"].r_max),
                                       dtype=torch.uint8, device=dev)
         sets.append(st)
@@ -250,9 +259,10 @@ def main():
         lb.lora_expand_add(st["v"], st["table"], st["seg"], st["y"])
         if ev is not None:
             ev[1].record()
-        lb.lora_segments_build(st["ft_ids"], wl.num_adapters, out=st["seg_ft"])
-        lb.lora_backward(st["x"][s:s + n], st["dy"], st["table"], st["grads"], st["seg_ft"], dx=st["dx"],
-                         v_saved=st["v"][s:s + n], ws=st["ws"])
+        if has_ft:
+            lb.lora_segments_build(st["ft_ids"], wl.num_adapters, out=st["seg_ft"])
+            lb.lora_backward(st["x"][s:s + n], st["dy"], st["table"], st["grads"], st["seg_ft"], dx=st["dx"],
+                             v_saved=st["v"][s:s + n], ws=st["ws"])
 
     graphs = None
     if args.graph:
@@ -311,7 +321,7 @@ def main():
         torch.cuda.synchronize()
         kern_ms = e0.elapsed_time(e1) / K
         kern_how = "events around back-to-back launches"
-    errs = [int(st["seg"].err.item()) + int(st["seg_ft"].err.item()) for st in sets]
+    errs = [int(st["seg"].err.item()) + (int(st["seg_ft"].err.item()) if has_ft else 0) for st in sets]
     if any(errs):
         raise RuntimeError(f"device-side data errors reported: {errs}")
 
@@ -330,14 +340,15 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "mixed-coserve-32x-4096to14336", "rows": T, "ft_rows": n, "d_in": wl.d_in,
-                   "d_out": wl.d_out, "adapters": wl.num_adapters, "ranks": "U{8,16,32,64}",
+        "config": {"workload": workloads.CONFIG_NAMES[args.workload], "rows": T, "ft_rows": n, "d_in": wl.d_in,
+                   "d_out": wl.d_out, "adapters": wl.num_adapters, "ranks": RANKS_DESC[args.workload],
                    "ft_adapter_rank": r_ft, "seed": 0, "input_sets": args.sets,
                    "launch": "graph" if graphs is not None else "eager"},
         "step_algorithmic_GBps": alg["step"]["bytes"] / (ms * 1e-3) / 1e9,
         "step_algorithmic_bytes": alg["step"]["bytes"],
         "roofline": {"bound": "hbm", "kernel": "lora_expand_add (expand_kernel)", "achieved": achieved,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic() if args.workload == 3 else None,
                      "algorithmic_bytes_per_launch": ex["bytes"], "avg_launch_ms": kern_ms, "timing": kern_how,
                      "mfma_frac": ex["flops"] / (kern_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
     }

@@ -339,10 +339,20 @@ __device__ __forceinline__ TaskSlice xcd_slice(int64_t n, int units_per_wg, int 
 }
 
 // Table entries and tile records, read with global loads.
+// Tables and tile records are read-only while a kernel runs and are indexed
+// with wave-uniform values: read through the constant address space, so
+// they become scalar loads whose waits (lgkmcnt) do not hold up the vector
+// memory pipeline.
+#define LORA_CONST __attribute__((address_space(4)))
+template <class T>
+__device__ __forceinline__ const LORA_CONST T* cptr(const T* p) {
+    return (const LORA_CONST T*)(p);
+}
+
 __device__ __forceinline__ lora_adapter load_adapter(const lora_adapter* table, int a) {
     // One 16-byte and one 8-byte load, issued together.
-    const LORA_GLOBAL u32x4_t* q4 = gptr(reinterpret_cast<const u32x4_t*>(table + a));
-    const LORA_GLOBAL uint64_t* q = gptr(reinterpret_cast<const uint64_t*>(table + a));
+    const LORA_CONST u32x4_t* q4 = cptr(reinterpret_cast<const u32x4_t*>(table + a));
+    const LORA_CONST uint64_t* q = cptr(reinterpret_cast<const uint64_t*>(table + a));
     const u32x4_t ab = q4[0];
     const uint64_t w2 = q[2];
     const uint64_t w0 = (uint64_t)ab[0] | ((uint64_t)ab[1] << 32);
@@ -355,7 +365,7 @@ __device__ __forceinline__ lora_adapter load_adapter(const lora_adapter* table, 
     return ad;
 }
 __device__ __forceinline__ lora_adapter_grad load_grad(const lora_adapter_grad* table, int a) {
-    const LORA_GLOBAL uint64_t* q = gptr(reinterpret_cast<const uint64_t*>(table + a));
+    const LORA_CONST uint64_t* q = cptr(reinterpret_cast<const uint64_t*>(table + a));
     lora_adapter_grad g;
     g.dA = reinterpret_cast<float*>(q[0]);
     g.dB = reinterpret_cast<float*>(q[1]);
@@ -365,7 +375,7 @@ struct TileRec {
     int adapter, pos0, rows;
 };
 __device__ __forceinline__ TileRec load_tile(const int32_t* sched, int64_t off, int64_t tile) {
-    const u32x4_t v = *gptr(reinterpret_cast<const u32x4_t*>(sched + off + 4 * tile));
+    const u32x4_t v = *cptr(reinterpret_cast<const u32x4_t*>(sched + off + 4 * tile));
     return TileRec{(int)v[0], (int)v[1], (int)v[2]};
 }
 
