@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--workload", type=int, default=3, choices=(2, 3, 4, 5),
                     help="synthetic workload (workloads.config index); 3 = the mixed co-serving batch")
     ap.add_argument("--graph", action="store_true", help="replay each step from a captured HIP graph")
+    ap.add_argument("--overlap", action="store_true",
+                    help="run the fine-tuning backward (v recomputed) on a second stream, concurrently with the "
+                         "forward, joining at the end of each step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-min-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -251,7 +254,18 @@ def main():
         sets.append(st)
     torch.cuda.synchronize()
 
+    side = torch.cuda.Stream(device=dev) if args.overlap else None  # default priority
+
+    def backward(st, v_saved):
+        lb.lora_segments_build(st["ft_ids"], wl.num_adapters, out=st["seg_ft"])
+        lb.lora_backward(st["x"][s:s + n], st["dy"], st["table"], st["grads"], st["seg_ft"], dx=st["dx"],
+                         v_saved=v_saved, ws=st["ws"])
+
     def step(st, ev=None):
+        if side is not None and has_ft:
+            side.wait_stream(torch.cuda.current_stream(dev))
+            with torch.cuda.stream(side):
+                backward(st, None)
         lb.lora_segments_build(st["ids"], wl.num_adapters, out=st["seg"])
         lb.lora_shrink(st["x"], st["table"], st["seg"], v=st["v"], ws=st["ws_shrink"])
         if ev is not None:
@@ -259,19 +273,19 @@ def main():
         lb.lora_expand_add(st["v"], st["table"], st["seg"], st["y"])
         if ev is not None:
             ev[1].record()
-        if has_ft:
-            lb.lora_segments_build(st["ft_ids"], wl.num_adapters, out=st["seg_ft"])
-            lb.lora_backward(st["x"][s:s + n], st["dy"], st["table"], st["grads"], st["seg_ft"], dx=st["dx"],
-                             v_saved=st["v"][s:s + n], ws=st["ws"])
+        if side is not None and has_ft:
+            torch.cuda.current_stream(dev).wait_stream(side)
+        elif has_ft:
+            backward(st, st["v"][s:s + n])
 
     graphs = None
     if args.graph:
-        side = torch.cuda.Stream(device=dev)
-        side.wait_stream(torch.cuda.current_stream(dev))
-        with torch.cuda.stream(side):
+        warm = torch.cuda.Stream(device=dev)
+        warm.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(warm):
             for st in sets:
                 step(st)
-        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.current_stream(dev).wait_stream(warm)
         torch.cuda.synchronize()
         graphs = []
         for st in sets:
@@ -343,7 +357,8 @@ def main():
         "config": {"workload": workloads.CONFIG_NAMES[args.workload], "rows": T, "ft_rows": n, "d_in": wl.d_in,
                    "d_out": wl.d_out, "adapters": wl.num_adapters, "ranks": RANKS_DESC[args.workload],
                    "ft_adapter_rank": r_ft, "seed": 0, "input_sets": args.sets,
-                   "launch": "graph" if graphs is not None else "eager"},
+                   "launch": "graph" if graphs is not None else "eager",
+                   "streams": 2 if args.overlap else 1},
         "step_algorithmic_GBps": alg["step"]["bytes"] / (ms * 1e-3) / 1e9,
         "step_algorithmic_bytes": alg["step"]["bytes"],
         "roofline": {"bound": "hbm", "kernel": "lora_expand_add (expand_kernel)", "achieved": achieved,

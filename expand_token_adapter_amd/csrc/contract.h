@@ -166,7 +166,7 @@ void contract_kernel(ContractParams p) {
     constexpr int NW = contract_waves<DT>();
     __shared__ __attribute__((aligned(16))) char s_mem[ContractLds<DT>::kBytes];
 
-    const int wave = threadIdx.x / kWave;
+    const int wave = wave_id();
     const int lane = threadIdx.x & (kWave - 1);
     const int lr = lane & 15;
     const int lg = lane >> 4;

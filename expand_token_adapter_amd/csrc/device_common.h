@@ -56,6 +56,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // drains them).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Index of the calling wave in its workgroup, as a wave-uniform (scalar)
+// value: branches on it stay scalar branches instead of exec-masked ones.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave)); }
+
 // ---------------------------------------------------------------- MFMA
 
 __device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {

@@ -66,7 +66,7 @@ void expand_kernel(ExpandParams p) {
     __shared__ __attribute__((aligned(16))) float s_t[kExpandWaves][16 * kTPitch];
     __shared__ int32_t s_row[ROWS];
 
-    const int wave = threadIdx.x / kWave;
+    const int wave = wave_id();
     const int lane = threadIdx.x & (kWave - 1);
     const int lr = lane & 15;
     const int lg = lane >> 4;

@@ -43,7 +43,7 @@ int launch_expand_t(int ks, const ExpandParams& p, unsigned grid, hipStream_t st
 namespace lora {
 
 __global__ __launch_bounds__(256) void shrink_reduce_kernel(ReduceParams p) {
-    const int wave = threadIdx.x / kWave;
+    const int wave = wave_id();
     const int lane = threadIdx.x & (kWave - 1);
     const int n = lane & 15;  // row of the tile
     const int g = lane >> 4;  // first rank group of 8

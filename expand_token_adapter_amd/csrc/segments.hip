@@ -87,7 +87,7 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
 // exclusive prefix and writes the workgroup total to *total.
 __device__ __forceinline__ int block_exclusive_scan(int v, int* s_tot, int* total) {
     constexpr int kWaves = kScanThreads / kWave;
-    const int w = threadIdx.x / kWave;
+    const int w = wave_id();
     const int lane = threadIdx.x & (kWave - 1);
     const int incl = wave_inclusive_scan(v);
     if (lane == kWave - 1) s_tot[w] = incl;
@@ -236,7 +236,7 @@ __global__ __launch_bounds__(kScanThreads) void seg_small_kernel(const int32_t* 
     __shared__ int s_tot[4][kSmallWaves];
     __shared__ int s_err[kSmallWaves];
     const int tid = threadIdx.x;
-    const int w = tid / kWave;
+    const int w = wave_id();
     const int lane = tid & (kWave - 1);
     const int per = (T + kSmallWaves - 1) / kSmallWaves;
     const int r0 = min(T, w * per);

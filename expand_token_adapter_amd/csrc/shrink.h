@@ -106,7 +106,7 @@ void shrink_kernel(ShrinkParams p) {
     char* s_wb = reinterpret_cast<char*>(s_w);
     f32x4_t* s_red = reinterpret_cast<f32x4_t*>(s_w);  // reused after the MFMA pass
 
-    const int wave = threadIdx.x / kWave;
+    const int wave = wave_id();
     const int lane = threadIdx.x & (kWave - 1);
     const int lr = lane & 15;  // MFMA row / column within the 16x16 tile
     const int lg = lane >> 4;  // K group of this lane
