@@ -191,18 +191,24 @@ __global__ __launch_bounds__(kChunk) void seg_scatter_kernel(const int32_t* __re
 // ---------------------------------------------------------------- one workgroup
 //
 // For batches of up to kSmallMaxT rows and kSmallMaxA adapters the whole
-// build runs in one workgroup of 16 waves (one launch instead of three):
-//   1. wave w counts the ids of its contiguous row range into its own LDS
-//      histogram hist[w][a], one update per distinct id of each 64-row group
-//      (lanes with equal ids are matched by one ballot per id bit);
+// build runs in one workgroup of 16 waves (one launch instead of three).
+// Wave w owns a contiguous range of rows; its first 512 ids are loaded once,
+// before anything else, and stay in registers for both passes together with
+// each lane's match inside its group (longer ranges load and match the rest
+// again in the second pass; the matching is most of the kernel's ALU work):
+//   1. wave w counts its ids into its own LDS histogram row hist[w][a], one
+//      update per distinct id of each 64-row group (lanes with equal ids are
+//      matched by one ballot per id bit);
 //   2. per adapter: counts = sum over w, hist[w][a] becomes the exclusive
-//      prefix over waves; a block scan over adapters gives offsets, the tile
-//      prefixes and the active list;
+//      prefix over waves; one block scan of four values per adapter gives
+//      offsets, both tile prefixes and the active list;
 //   3. wave w walks its rows in order, 64 at a time; inside a group the lanes
 //      that share an id are ranked by lane order (the same ballot match), and
 //      the wave's cursor for that id advances by the group's count.  Every row's
 //      position is therefore its rank in row order: the same stable grouping
 //      as the three-kernel path.
+// Only LDS is waited on at the barriers; the global stores of one phase
+// never hold up the next.
 
 // Lanes of this wave holding the same valid id as the calling lane (0 for an
 // invalid one), from one ballot per bit of the ids (ids < 2^nbits): a lane
@@ -217,9 +223,38 @@ __device__ __forceinline__ uint64_t same_id_lanes(int id, bool valid, int nbits)
     return valid ? m : 0ull;
 }
 
+
+// Exclusive scan of four ints per thread across the workgroup (one LDS
+// barrier; s_tot is used once).  Returns the exclusive prefixes and writes
+// the workgroup totals to *total.
+__device__ __forceinline__ int4 block_exclusive_scan4(int4 v, int4* s_tot, int4* total) {
+    constexpr int kWaves = kScanThreads / kWave;
+    const int w = wave_id();
+    const int lane = threadIdx.x & (kWave - 1);
+    int4 incl = v;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int4 o = make_int4(__shfl_up(incl.x, d, kWave), __shfl_up(incl.y, d, kWave),
+                                 __shfl_up(incl.z, d, kWave), __shfl_up(incl.w, d, kWave));
+        if (lane >= d) incl = incl + o;
+    }
+    if (lane == kWave - 1) s_tot[w] = incl;
+    lds_barrier();
+    int4 before = make_int4(0, 0, 0, 0), all = make_int4(0, 0, 0, 0);
+#pragma unroll 4
+    for (int i = 0; i < kWaves; ++i) {
+        const int4 x = s_tot[i];
+        if (i < w) before = before + x;
+        all = all + x;
+    }
+    *total = all;
+    return before + incl - v;
+}
+
 constexpr int kSmallMaxA = 1024;
 constexpr int kSmallMaxT = 1 << 16;
 constexpr int kSmallWaves = kScanThreads / kWave;
+constexpr int kSmallBatch = 8;  // 64-row groups per load batch
 
 __global__ __launch_bounds__(kScanThreads) void seg_small_kernel(const int32_t* __restrict__ ids, int32_t T,
                                                                  int32_t A, int32_t* __restrict__ counts,
@@ -229,11 +264,8 @@ __global__ __launch_bounds__(kScanThreads) void seg_small_kernel(const int32_t* 
                                                                  int64_t active_off, int64_t tiles16_off,
                                                                  int64_t tiles64_off) {
     __shared__ int s_hist[kSmallWaves][kSmallMaxA];
-    __shared__ int s_off[kSmallMaxA];
-    __shared__ int s_cnt[kSmallMaxA];
-    __shared__ int s_pre16[kSmallMaxA];
-    __shared__ int s_pre64[kSmallMaxA];
-    __shared__ int s_tot[4][kSmallWaves];
+    __shared__ int4 s_info[kSmallMaxA];  // offset, count, 16-row tile prefix, 64-row tile prefix
+    __shared__ int4 s_tot[kSmallWaves];
     __shared__ int s_err[kSmallWaves];
     const int tid = threadIdx.x;
     const int w = wave_id();
@@ -242,34 +274,55 @@ __global__ __launch_bounds__(kScanThreads) void seg_small_kernel(const int32_t* 
     const int r0 = min(T, w * per);
     const int r1 = min(T, r0 + per);
     const int nbits = A > 1 ? 32 - __clz(A - 1) : 1;  // bits of the largest id
+    constexpr int kStep = kSmallBatch * kWave;
 
-    for (int i = tid; i < kSmallWaves * kSmallMaxA; i += kScanThreads) (&s_hist[0][0])[i] = 0;
-    __syncthreads();
-    // Row ids are read 8 groups of 64 at a time (independent loads in flight).
-    int bad = 0;
-    for (int b = r0; b < r1; b += 8 * kWave) {
-        int idv[8];
+    auto load_batch = [&](int b, int* idv) {
 #pragma unroll
-        for (int g = 0; g < 8; ++g) {
+        for (int g = 0; g < kSmallBatch; ++g) {
             const int t = b + g * kWave + lane;
             idv[g] = t < r1 ? ids[t] : -1;
         }
+    };
+    int id0[kSmallBatch];
+    load_batch(r0, id0);
+    // Each wave clears its own histogram row (no other wave touches it before the barrier).
+    for (int a = lane; a < A; a += kWave) s_hist[w][a] = 0;
+
+    // A lane's match inside its 64-row group: rank among the lanes with its id
+    // (bits 0-7), their number (bits 8-15), bit 16 set on the lowest of them;
+    // 0 for a lane without a valid id.
+    auto match = [&](int id, bool valid) {
+        const uint64_t m = same_id_lanes(id, valid, nbits);
+        const int rank = __popcll(m & ((1ull << lane) - 1));
+        return valid ? rank | (__popcll(m) << 8) | (rank == 0 ? 1 << 16 : 0) : 0;
+    };
+    // 1. count: the lowest lane holding each id adds the group's count of that id.
+    int bad = 0;
+    int mt0[kSmallBatch];
+    auto count_batch = [&](int b, const int* idv, int* mt) {
 #pragma unroll
-        for (int g = 0; g < 8; ++g) {
-            const int id = idv[g];
-            const bool valid = id >= 0 && id < A;
-            bad += (!valid && id != -1) ? 1 : 0;
-            // The lowest lane holding each id adds the group's count of that
-            // id to this wave's own histogram row.
-            const uint64_t m = same_id_lanes(id, valid, nbits);
-            if (valid && lane == __ffsll((long long)m) - 1) s_hist[w][id] += __popcll(m);
+        for (int g = 0; g < kSmallBatch; ++g) {
+            mt[g] = 0;
+            if (b + g * kWave < r1) {  // wave-uniform: skip empty groups
+                const int id = idv[g];
+                const bool valid = id >= 0 && id < A;
+                bad += (!valid && id != -1) ? 1 : 0;
+                mt[g] = match(id, valid);
+                if (mt[g] & (1 << 16)) s_hist[w][id] += mt[g] >> 8 & 0xff;
+            }
         }
+    };
+    count_batch(r0, id0, mt0);
+    for (int b = r0 + kStep; b < r1; b += kStep) {
+        int idv[kSmallBatch], mt[kSmallBatch];
+        load_batch(b, idv);
+        count_batch(b, idv, mt);
     }
     bad = __reduce_add_sync(~0ull, bad);
     if (lane == 0) s_err[w] = bad;
-    __syncthreads();
+    lds_barrier();
 
-    // per adapter: total and exclusive prefix over the waves
+    // 2. per adapter: total and exclusive prefix over the waves, then the scans over adapters
     const int a = tid;
     int c = 0;
     if (a < A) {
@@ -278,72 +331,67 @@ __global__ __launch_bounds__(kScanThreads) void seg_small_kernel(const int32_t* 
             s_hist[v][a] = c;
             c += h;
         }
-        counts[a] = c;
-        s_cnt[a] = c;
     }
-    int tc, t16, t64, tact;
-    const int ec = block_exclusive_scan(c, s_tot[0], &tc);
-    const int e16 = block_exclusive_scan((c + 15) / 16, s_tot[1], &t16);
-    const int e64 = block_exclusive_scan((c + 63) / 64, s_tot[2], &t64);
-    const int eact = block_exclusive_scan(c > 0 ? 1 : 0, s_tot[3], &tact);
+    int4 tot;
+    const int4 ex = block_exclusive_scan4(make_int4(c, (c + 15) / 16, (c + 63) / 64, c > 0 ? 1 : 0), s_tot, &tot);
+    if (a < A) s_info[a] = make_int4(ex.x, c, ex.y, ex.z);
+    lds_barrier();
     if (a < A) {
-        offsets[a] = ec;
-        s_off[a] = ec;
-        s_pre16[a] = e16;
-        s_pre64[a] = e64;
-        if (c > 0) sched[active_off + eact] = a;
+        counts[a] = c;
+        offsets[a] = ex.x;
+        if (c > 0) sched[active_off + ex.w] = a;
     }
     if (tid == 0) {
-        offsets[A] = tc;
-        sched[0] = t16;
-        sched[1] = t64;
-        sched[2] = tact;
-        sched[3] = 0;
+        offsets[A] = tot.x;
+        *reinterpret_cast<int4*>(sched) = make_int4(tot.y, tot.z, tot.w, 0);
         int e = 0;
         for (int v = 0; v < kSmallWaves; ++v) e += s_err[v];
         err[0] = e;
     }
-    __syncthreads();
 
-    // stable scatter: wave w owns rows [r0, r1); s_hist[w][a] is its cursor for adapter a.
-    // Ids are loaded 8 groups at a time; the groups are then processed with no
-    // loads in between, so stores of one group never hold up the next.
-    for (int b = r0; b < r1; b += 8 * kWave) {
-        int idv[8];
+    // 3. stable scatter: s_hist[w][a] is wave w's cursor for adapter a.
+    auto scatter_batch = [&](int b, const int* idv, const int* mt) {
 #pragma unroll
-        for (int g = 0; g < 8; ++g) {
-            const int t = b + g * kWave + lane;
-            idv[g] = t < r1 ? ids[t] : -1;
-        }
-#pragma unroll
-        for (int g = 0; g < 8; ++g) {
+        for (int g = 0; g < kSmallBatch; ++g) {
+            if (b + g * kWave >= r1) break;  // wave-uniform
             const int t = b + g * kWave + lane;
             const int id = idv[g];
-            const bool valid = id >= 0 && id < A;
-            const uint64_t m = same_id_lanes(id, valid, nbits);
+            const bool valid = mt[g] != 0;
             int cur = 0;
-            if (valid) cur = s_hist[w][id];
             if (valid) {
-                const int rank = __popcll(m & ((1ull << lane) - 1));
+                cur = s_hist[w][id];
+                const int4 info = s_info[id];
+                const int rank = mt[g] & 0xff;
                 const int local = cur + rank;  // position inside the adapter's group
-                const int pos = s_off[id] + local;
+                const int pos = info.x + local;
+                const int cnt = info.y;
                 perm[pos] = t;
-                const int cnt = s_cnt[id];
                 if ((local & 15) == 0) {
                     const int rows = cnt - local < 16 ? cnt - local : 16;
-                    *reinterpret_cast<int4*>(sched + tiles16_off + 4 * (int64_t)(s_pre16[id] + local / 16)) =
+                    *reinterpret_cast<int4*>(sched + tiles16_off + 4 * (int64_t)(info.z + local / 16)) =
                         make_int4(id, pos, rows, 0);
                 }
                 if ((local & 63) == 0) {
                     const int rows = cnt - local < 64 ? cnt - local : 64;
-                    *reinterpret_cast<int4*>(sched + tiles64_off + 4 * (int64_t)(s_pre64[id] + local / 64)) =
+                    *reinterpret_cast<int4*>(sched + tiles64_off + 4 * (int64_t)(info.w + local / 64)) =
                         make_int4(id, pos, rows, 0);
                 }
             }
             // every lane has read its cursor: the lowest lane of each id advances it
             __builtin_amdgcn_wave_barrier();
-            if (valid && lane == __ffsll((long long)m) - 1) s_hist[w][id] = cur + __popcll(m);
+            if (mt[g] & (1 << 16)) s_hist[w][id] = cur + (mt[g] >> 8 & 0xff);
         }
+    };
+    scatter_batch(r0, id0, mt0);
+    for (int b = r0 + kStep; b < r1; b += kStep) {
+        int idv[kSmallBatch], mt[kSmallBatch];
+        load_batch(b, idv);
+#pragma unroll
+        for (int g = 0; g < kSmallBatch; ++g) {
+            const bool valid = idv[g] >= 0 && idv[g] < A;
+            mt[g] = b + g * kWave < r1 ? match(idv[g], valid) : 0;
+        }
+        scatter_batch(b, idv, mt);
     }
 }
 
