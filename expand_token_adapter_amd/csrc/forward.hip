@@ -16,6 +16,7 @@ using namespace lora;
 namespace {
 
 constexpr int64_t kMaxGrid = 8192;
+constexpr int64_t kShrinkMaxGrid = 1024;
 
 template <int DT>
 int launch_shrink_t(bool trans_w, const ShrinkParams& p, unsigned grid, hipStream_t st) {
@@ -42,48 +43,73 @@ int launch_expand_t(int ks, const ExpandParams& p, unsigned grid, hipStream_t st
 
 namespace lora {
 
-__global__ __launch_bounds__(256) void shrink_reduce_kernel(ReduceParams p) {
+// Fixed-order sum of the K-slice partials of one 16-row tile per workgroup.
+// Lane (n, q) = (lane % 16, lane / 16) holds ranks 16 j + 4 q .. + 3 of row
+// n; wave w sums the slices [w ns / 4, (w + 1) ns / 4) in slice order with
+// all its loads in flight, and wave 0 adds the four wave sums in wave order,
+// so the result does not depend on timing.
+constexpr int kReduceWaves = 4;
+constexpr int kReduceJ = LORA_MAX_RANK / 16;
+
+__global__ __launch_bounds__(kReduceWaves * kWave) void shrink_reduce_kernel(ReduceParams p) {
+    __shared__ f32x4_t s_acc[kReduceWaves - 1][kReduceJ][kWave];
     const int wave = wave_id();
     const int lane = threadIdx.x & (kWave - 1);
-    const int n = lane & 15;  // row of the tile
-    const int g = lane >> 4;  // first rank group of 8
+    const int n = lane & 15;
+    const int q = lane >> 4;
     const int64_t ntiles = p.sched[0];
-    for (int64_t tile = (int64_t)blockIdx.x * 4 + wave; tile < ntiles; tile += (int64_t)gridDim.x * 4) {
+    const int s0 = wave * p.nslices / kReduceWaves;
+    const int s1 = (wave + 1) * p.nslices / kReduceWaves;
+    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
         const TileRec rec = load_tile(p.sched, p.tiles16_off, tile);
-        const int pos = rec.pos0 + (n < rec.rows ? n : 0);
-        const int64_t orow = p.out_by_pos ? pos : p.perm[pos];
         const lora_adapter ad = load_adapter(p.adapters, rec.adapter);
-        if (!adapter_ok(ad, p.r_max) || n >= rec.rows) continue;  // bad entries are counted by the shrink
+        if (!adapter_ok(ad, p.r_max)) continue;  // bad entries are counted by the shrink
         const int r = ad.rank;
-        for (int k = 8 * g; k < r; k += 32) {
-            const float* src = p.part + (int64_t)pos * p.ldp + k;
-            f32x4_t a = f32x4_t{0.f, 0.f, 0.f, 0.f}, b = a;
-#pragma unroll 4
-            for (int sl = 0; sl < p.nslices; ++sl) {
-                const LORA_GLOBAL f32x4_t* v = gptr(reinterpret_cast<const f32x4_t*>(src + (int64_t)sl * p.slice_stride));
-                a += v[0];
-                b += v[1];
-            }
-            // ranks r .. k + 7 of the last group hold no partial: zeros there
+        const int nj = (r + 15) / 16;
+        const bool row_ok = n < rec.rows;
+        const int pos = rec.pos0 + (row_ok ? n : 0);
+        const int64_t orow = wave == 0 && p.out && !p.out_by_pos ? p.perm[pos] : pos;
+        // quads at or past r hold no partial (and may lie past the workspace): not read
+        const float* src = p.part + (int64_t)pos * p.ldp + 4 * q;
+        f32x4_t acc[kReduceJ];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (k + i >= r) a[i] = 0.f;
-                if (k + 4 + i >= r) b[i] = 0.f;
-            }
-            if (p.out) {
-                // k + 8 <= round_up(r_max, 8) <= ldo (a multiple of 8)
-                float* dst = p.out + orow * p.ldo + k;
-                *gptr(reinterpret_cast<f32x4_t*>(dst)) = a;
-                *gptr(reinterpret_cast<f32x4_t*>(dst + 4)) = b;
-            }
-            if (p.outT) {
+        for (int j = 0; j < kReduceJ; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+        for (int sl = s0; sl < s1; ++sl) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    if (k + i < r) gptr(p.outT)[(int64_t)(k + i) * p.ldT + pos] = a[i];
-                    if (k + 4 + i < r) gptr(p.outT)[(int64_t)(k + 4 + i) * p.ldT + pos] = b[i];
+            for (int j = 0; j < kReduceJ; ++j)
+                if (j < nj && 16 * j + 4 * q < r)
+                    acc[j] += *gptr(reinterpret_cast<const f32x4_t*>(src + (int64_t)sl * p.slice_stride + 16 * j));
+        }
+        if (wave > 0) {
+#pragma unroll
+            for (int j = 0; j < kReduceJ; ++j)
+                if (j < nj) s_acc[wave - 1][j][lane] = acc[j];
+        }
+        lds_barrier();
+        if (wave == 0 && row_ok) {
+#pragma unroll
+            for (int j = 0; j < kReduceJ; ++j) {
+                if (j < nj) {
+                    f32x4_t sum = acc[j];
+#pragma unroll
+                    for (int w = 0; w < kReduceWaves - 1; ++w) sum += s_acc[w][j][lane];
+                    const int k = 16 * j + 4 * q;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (k + i >= r) sum[i] = 0.f;
+                    // quads below round_up(r, 8) <= round_up(r_max, 8) <= ldo
+                    if (p.out && k < (r + 7) / 8 * 8)
+                        *gptr(reinterpret_cast<f32x4_t*>(p.out + orow * p.ldo + k)) = sum;
+                    if (p.outT) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (k + i < r) gptr(p.outT)[(int64_t)(k + i) * p.ldT + pos] = sum[i];
+                    }
                 }
             }
         }
+        lds_barrier();  // s_acc is reused by the next tile
     }
 }
 
@@ -91,13 +117,15 @@ __global__ __launch_bounds__(256) void shrink_reduce_kernel(ReduceParams p) {
 // split-K shrink into partials, then their fixed-order sum.
 int run_shrink(int dtype, bool trans_w, const ShrinkParams& p, const ReduceParams& rp, int32_t T, int32_t num_adapters,
                hipStream_t st) {
+    // at most four workgroups per CU: the later tasks of a workgroup overlap
+    // their metadata loads with the current task's data
     const int64_t tasks = SchedLayout::max_tiles64(T, num_adapters) * p.rgroups * p.nslices;
-    const unsigned grid = grid_for(tasks, 1, kMaxGrid);
+    const unsigned grid = grid_for(tasks, 1, kShrinkMaxGrid);
     const int rc = dtype == LORA_BF16 ? launch_shrink_t<LORA_BF16>(trans_w, p, grid, st)
                                       : launch_shrink_t<LORA_F32>(trans_w, p, grid, st);
     if (rc != LORA_OK) return rc;
-    const unsigned rgrid = (unsigned)std::min<int64_t>((SchedLayout::max_tiles16(T, num_adapters) + 3) / 4, 4096);
-    hipLaunchKernelGGL(shrink_reduce_kernel, dim3(rgrid), dim3(256), 0, st, rp);
+    const unsigned rgrid = (unsigned)std::min<int64_t>(SchedLayout::max_tiles16(T, num_adapters), kMaxGrid);
+    hipLaunchKernelGGL(shrink_reduce_kernel, dim3(rgrid), dim3(kReduceWaves * kWave), 0, st, rp);
     return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
