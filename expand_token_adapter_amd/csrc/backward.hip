@@ -7,8 +7,9 @@
 //   v  = A x                         shrink kernel (or the caller's saved v)
 //   dX += s A^T g                    expand kernel, weights read transposed
 //   dA += s sum g x^T, dB += s sum dy v^T   token-contraction kernel
-// Four launches; the workspace holds g (by sorted position, row- and
-// rank-major) and v (rank-major).
+// The workspace holds g (by sorted position, row- and rank-major), v
+// (rank-major), the shrinks' split-K partials and the contraction's partial
+// tiles of tiles cut between workgroups.
 #include <algorithm>
 
 #include "host_checks.h"
@@ -31,7 +32,7 @@ int run_expand(int dtype, bool trans_w, const ExpandParams& p, int32_t T, int32_
 // shrinks (reused by the g and v passes, which run one after the other).
 struct BwdWs {
     int64_t ldg, ldT;               // pitch of g rows; pitch of the rank-major arrays
-    int64_t g, gT, vT, part, total; // offsets
+    int64_t g, gT, vT, part, fix, fix_meta, total; // offsets
     static BwdWs make(int dtype, int64_t T, int64_t d_in, int64_t d_out, int64_t r_max) {
         BwdWs w;
         w.ldg = round_up(r_max, 8);
@@ -42,14 +43,15 @@ struct BwdWs {
         w.part = round_up(w.vT + r_max * w.ldT, 64);
         const int64_t np = std::max(shrink_part_floats(dtype, (int32_t)T, (int32_t)d_in, (int32_t)r_max),
                                     shrink_part_floats(dtype, (int32_t)T, (int32_t)d_out, (int32_t)r_max));
-        w.total = round_up(w.part + np, 64);
+        w.fix = round_up(w.part + np, 64);
+        w.fix_meta = w.fix + (int64_t)kContractGrid * 2 * kFixFloats;
+        w.total = round_up(w.fix_meta + (int64_t)kContractGrid * 2 * kFixMeta, 64);
         return w;
     }
 };
 }  // namespace lora
 
 namespace {
-constexpr int64_t kMaxContractGrid = 512;  // two resident workgroups per CU
 
 // vT[k][pos] = v[perm[pos]][k] for pos < n_valid, k < r_max: the caller's saved v,
 // rank-major by sorted position as the token contraction reads it.
@@ -184,12 +186,15 @@ extern "C" int lora_backward(int dtype, const void* x, int64_t ldx, const void* 
     cp.ncb_out = (d_out + 63) / 64;
     cp.rgroups = (r_max + 16 * kContractMB - 1) / (16 * kContractMB);
     cp.err = seg_ft.err;
-    const int64_t max_active = num_adapters < T_ft ? num_adapters : T_ft;
-    const int64_t tasks = max_active * cp.rgroups * (cp.ncb_in + cp.ncb_out);
-    const unsigned grid = grid_for(tasks, 1, kMaxContractGrid);
+    cp.fix = wsf + w.fix;
+    cp.fix_meta = reinterpret_cast<int32_t*>(wsf + w.fix_meta);
+    // kContractGrid workgroups (a multiple of the 8 XCDs) split the work evenly
     if (dtype == LORA_BF16)
-        hipLaunchKernelGGL(contract_kernel<LORA_BF16>, dim3(grid), dim3(contract_waves<LORA_BF16>() * kWave), 0, st, cp);
+        hipLaunchKernelGGL(contract_kernel<LORA_BF16>, dim3(kContractGrid), dim3(contract_waves<LORA_BF16>() * kWave),
+                           0, st, cp);
     else
-        hipLaunchKernelGGL(contract_kernel<LORA_F32>, dim3(grid), dim3(contract_waves<LORA_F32>() * kWave), 0, st, cp);
+        hipLaunchKernelGGL(contract_kernel<LORA_F32>, dim3(kContractGrid), dim3(contract_waves<LORA_F32>() * kWave), 0,
+                           st, cp);
+    hipLaunchKernelGGL(contract_fixup_kernel, dim3(kContractGrid), dim3(4 * kWave), 0, st, cp, (int)kContractGrid);
     return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }

@@ -23,7 +23,7 @@ __device__ __forceinline__ int rotated(int kc0, int n, int rot, int i) {
 // ============================================================== token contraction
 //
 // For each adapter a with fine-tuning rows, each group of 16 ranks and each
-// block of 64 columns:
+// block of 64 columns (a "tile"):
 //   dA_a[k][c] += s_a * sum_rows g[row][k] * x[row][c]      (c < d_in)
 //   dB_a[c][k] += s_a * sum_rows dy[row][c] * v[row][k]     (c < d_out)
 // The contraction runs over rows, so the row-major x / dy tiles (32 rows x
@@ -31,13 +31,20 @@ __device__ __forceinline__ int rotated(int kc0, int n, int rot, int i) {
 // tiles are stored as loaded and read back transposed with
 // ds_read_b64_tr_b16; fp32 tiles are written transposed element by element.
 // g and v come rank-major ([k][sorted position]) from the shrink kernel.
-// The waves (eight for bf16, four for fp32) split the adapter's rows into
-// contiguous ranges of 32-row windows.  Each wave runs two interleaved
-// streams of windows: while one window is multiplied, the next window of
-// the other stream is in flight, and the row indices (perm) of each stream
-// are fetched one window ahead of its data.  The waves' partial tiles are
-// summed in wave order through LDS and added to dA / dB, which no other
-// workgroup touches.
+//
+// Work split ("stream-K"): the work is the list of (tile, 32-row window)
+// units, ordered by active adapter, rank group, column block, window; the
+// grid's workgroups (one per CU) take equal contiguous ranges of it, so no
+// CU waits on another's second tile.  Inside a workgroup the waves (eight
+// for bf16, four for fp32) split the windows of each tile they meet into
+// contiguous ranges.  Each wave runs two interleaved streams of windows:
+// while one window is multiplied, the next window of the other stream is in
+// flight, and the row indices (perm) of each stream are fetched one window
+// ahead of its data.  The waves' partial tiles are summed in wave order
+// through LDS.  A tile whose windows all fall in one workgroup is added to
+// dA / dB there; a tile cut by workgroup boundaries leaves one partial tile
+// per workgroup, and contract_fixup_kernel adds those in workgroup order.
+// Every sum therefore runs in an order fixed by the shapes alone.
 
 template <int DT>
 __host__ __device__ constexpr int contract_waves() { return DT == LORA_BF16 ? 8 : 4; }
@@ -62,9 +69,54 @@ struct ContractParams {
     int64_t active_off;
     int32_t d_in, d_out;
     int32_t ncb_in, ncb_out;
-    int32_t rgroups;  // ceil(r_max / 32)
+    int32_t rgroups;  // ceil(r_max / 16)
     int32_t* err;
+    float* fix;       // [grid][2] partial tiles of cut tiles (kFixFloats floats each)
+    int32_t* fix_meta;  // [grid][2][kFixMeta]: first unit of the tile (lo, hi; -1: none, -2: empty
+                        // range), adapter, rank group, column block, owner
 };
+
+constexpr int kContractGrid = 256;  // one workgroup per CU
+constexpr int kFixFloats = kContractMB * 4 * kWave * 4;
+constexpr int kFixMeta = 8;
+
+// One active adapter's share of the contraction: rank groups x column blocks
+// x 32-row windows of its sorted rows (no units for an invalid entry).
+struct ContractAct {
+    int a, rgroups, nwin, lo, hi;
+    int64_t units;
+};
+__device__ __forceinline__ ContractAct contract_act(const ContractParams& p, int i, int ncb) {
+    ContractAct c;
+    c.a = p.sched[p.active_off + i];
+    const lora_adapter ad = load_adapter(p.adapters, c.a);
+    const lora_adapter_grad gr = load_grad(p.grads, c.a);
+    const bool ok = adapter_ok(ad, p.r_max) && gr.dA != nullptr && gr.dB != nullptr;
+    c.rgroups = ok ? min(p.rgroups, (ad.rank + 16 * kContractMB - 1) / (16 * kContractMB)) : 0;
+    c.lo = p.offsets[c.a];
+    c.hi = p.offsets[c.a + 1];
+    c.nwin = (c.hi - (c.lo & ~31) + 31) / 32;
+    c.units = (int64_t)c.rgroups * ncb * c.nwin;
+    return c;
+}
+
+// The same, for a wave-uniform index: every field wave-uniform (scalar).
+__device__ __forceinline__ ContractAct contract_act_uniform(const ContractParams& p, int i, int ncb) {
+    ContractAct c = contract_act(p, i, ncb);
+    c.a = __builtin_amdgcn_readfirstlane(c.a);
+    c.rgroups = __builtin_amdgcn_readfirstlane(c.rgroups);
+    c.nwin = __builtin_amdgcn_readfirstlane(c.nwin);
+    c.lo = __builtin_amdgcn_readfirstlane(c.lo);
+    c.hi = __builtin_amdgcn_readfirstlane(c.hi);
+    c.units = uniform64(c.units);
+    return c;
+}
+
+__device__ __forceinline__ int64_t wave_sum64(int64_t v) {
+#pragma unroll
+    for (int d = kWave / 2; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
+    return v;
+}
 
 template <int DT>
 struct ContractLds {
@@ -160,9 +212,8 @@ __device__ __forceinline__ void contract_compute(const ContractWin<DT>& W, char*
 }
 
 template <int DT>
-__global__ __launch_bounds__(contract_waves<DT>() * kWave) __attribute__((amdgpu_waves_per_eu(DT == LORA_BF16 ? 4 : 2)))
+__global__ __launch_bounds__(contract_waves<DT>() * kWave) __attribute__((amdgpu_waves_per_eu(DT == LORA_BF16 ? 2 : 1)))
 void contract_kernel(ContractParams p) {
-    using F = Frag<DT>;
     constexpr int NW = contract_waves<DT>();
     __shared__ __attribute__((aligned(16))) char s_mem[ContractLds<DT>::kBytes];
 
@@ -171,40 +222,79 @@ void contract_kernel(ContractParams p) {
     const int lr = lane & 15;
     const int lg = lane >> 4;
     const int ncb = p.ncb_in + p.ncb_out;
-    // Rank groups: enough for the largest rank among the adapters with rows
-    // (bad table entries count as r_max; they are reported per task below).
     const int n_act = p.sched[2];
-    int rmax_act = 1;
-    for (int i = 0; i < n_act; ++i) {
-        const int rk = p.adapters[p.sched[p.active_off + i]].rank;
-        rmax_act = max(rmax_act, rk >= 1 && rk <= p.r_max ? rk : p.r_max);
+    // Workgroups of one XCD take neighbouring ranges (workgroup b runs on XCD b % 8).
+    const int G = gridDim.x;
+    const int vg = (int)(blockIdx.x % kNumXcd) * (G / kNumXcd) + (int)(blockIdx.x / kNumXcd);
+    int32_t* meta = p.fix_meta + (int64_t)vg * 2 * kFixMeta;
+    if (threadIdx.x == 0) {
+        meta[0] = -1;
+        meta[kFixMeta] = -1;
     }
-    const int rgroups = min(p.rgroups, (rmax_act + 16 * kContractMB - 1) / (16 * kContractMB));
-    const int64_t n_tasks = (int64_t)n_act * rgroups * ncb;
-    const TaskSlice ts = xcd_slice(n_tasks, 1, 0);
+
+    // Total units (every wave, 64 adapters per pass); workgroup 0 counts the bad entries.
+    int64_t U = 0;
+    for (int b = 0; b < n_act; b += kWave) {
+        const int i = b + lane;
+        ContractAct c{};
+        if (i < n_act) c = contract_act(p, i, ncb);
+        U += uniform64(wave_sum64(c.units));
+        if (blockIdx.x == 0 && wave == 0 && i < n_act && c.rgroups == 0) atomicAdd(p.err, 1);
+    }
+    const int64_t begin = U * vg / G;
+    const int64_t end = U * (vg + 1) / G;
+    if (begin >= end) {  // (fewer units than workgroups) the fix-up steps over this one
+        if (threadIdx.x == 0) meta[0] = -2;
+        return;
+    }
+    // The active adapter holding unit `begin` and the units before it.
+    int act = 0;
+    int64_t abase = 0;
+    for (int b = 0; b < n_act; b += kWave) {
+        const int i = b + lane;
+        const int64_t un = i < n_act ? contract_act(p, i, ncb).units : 0;
+        int64_t incl = un;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int64_t o = __shfl_up(incl, d, kWave);
+            if (lane >= d) incl += o;
+        }
+        const uint64_t hit = __ballot(i < n_act && abase + incl - un <= begin && begin < abase + incl);
+        if (hit) {
+            const int l = __ffsll((long long)hit) - 1;
+            act = b + l;
+            abase += uniform64(__shfl(incl - un, l, kWave));
+            break;
+        }
+        abase += uniform64(__shfl(incl, kWave - 1, kWave));
+    }
+
     char* tileA = s_mem + (2 * wave) * ContractLds<DT>::kTileBytes;
     char* tileB = s_mem + (2 * wave + 1) * ContractLds<DT>::kTileBytes;
     // Loader role: lane covers window rows 4*(lane/8)+j (j < 4), columns 8*(lane%8)+e (e < 8).
     const int lrow = 4 * (lane >> 3);
     const int lcol = 8 * (lane & 7);
 
-    for (int64_t task = ts.begin; task < ts.end; task += ts.stride) {
-        // rank group fastest: groups past an adapter's rank exit at once, and
-        // the remaining tasks spread evenly over the XCDs' contiguous ranges
-        const int rg = (int)(task % rgroups);
-        const int cb_all = (int)((task / rgroups) % ncb);
-        const int act = (int)(task / ((int64_t)ncb * rgroups));
-        const int a = p.sched[p.active_off + act];
+    ContractAct c = contract_act_uniform(p, act, ncb);
+    int slot = 0;
+    for (int64_t u = begin; u < end;) {
+        if (u >= abase + c.units) {  // next adapter (u < end <= U: one exists)
+            abase += c.units;
+            c = contract_act_uniform(p, ++act, ncb);
+            continue;
+        }
+        const int64_t local = u - abase;
+        const int tile_in = (int)(local / c.nwin);  // rank group major, then column block
+        const int w0 = (int)(local - (int64_t)tile_in * c.nwin);
+        const int w1 = (int)min((int64_t)c.nwin, w0 + (end - u));
+        const int rg = tile_in / ncb;
+        const int cb_all = tile_in - rg * ncb;
+        const int a = c.a;
         const lora_adapter ad = load_adapter(p.adapters, a);
         const lora_adapter_grad gr = load_grad(p.grads, a);
         const bool is_dA = cb_all < p.ncb_in;
-        if (!adapter_ok(ad, p.r_max) || gr.dA == nullptr || gr.dB == nullptr) {
-            if (cb_all == 0 && rg == 0 && threadIdx.x == 0) atomicAdd(p.err, 1);
-            continue;
-        }
         const int r = ad.rank;
         const int rank0 = rg * 16 * kContractMB;
-        if (rank0 >= r) continue;
         const int nmb = min(kContractMB, (r - rank0 + 15) / 16);
         const int cb = is_dA ? cb_all : cb_all - p.ncb_in;
         const int c0 = cb * 64;
@@ -214,14 +304,14 @@ void contract_kernel(ContractParams p) {
         const float* PT = is_dA ? p.gT : p.vT;
         // Columns past N (N is a multiple of 8) read column block 0 of the row; never written back.
         const int cq = c0 + lcol < N ? c0 : -lcol;
-
-        const int lo = p.offsets[a];
-        const int hi = p.offsets[a + 1];
-        // 32-aligned windows of sorted positions covering [lo, hi), split over the waves.
-        const int w0 = lo & ~31;
-        const int nwin = (hi - w0 + 31) / 32;
-        const int wa = w0 + 32 * (int)((int64_t)wave * nwin / NW);
-        const int wb = w0 + 32 * (int)((int64_t)(wave + 1) * nwin / NW);
+        const int lo = c.lo;
+        const int hi = c.hi;
+        // This wave's windows: a contiguous share of [w0, w1) of the 32-aligned
+        // windows of sorted positions covering [lo, hi).
+        const int wbase = lo & ~31;
+        const int nwt = w1 - w0;
+        const int wa = wbase + 32 * (w0 + nwt * wave / NW);
+        const int wb = wbase + 32 * (w0 + nwt * (wave + 1) / NW);
 
         f32x4_t acc[kContractMB][4];
 #pragma unroll
@@ -229,13 +319,13 @@ void contract_kernel(ContractParams p) {
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-        // Windows visited from a task-dependent start (the column blocks of one
-        // adapter read the same g / v windows); fixed order per task.  Two
+        // Windows visited from a tile-dependent start (the column blocks of one
+        // adapter read the same g / v windows); fixed order per tile.  Two
         // streams: A takes windows 0, 2, 4, ..., B takes 1, 3, 5, ...; indices
         // past the range repeat the last window (loaded, never multiplied).
         const int nw = (wb - wa) / 32;
         if (nw > 0) {
-            const int rot = (int)(task % nw);
+            const int rot = cb_all % nw;
             auto win_at = [&](int i) { return wa + 32 * rotated(0, nw, rot, i < nw ? i : nw - 1); };
             int32_t rowsA[4], rowsB[4];
             ContractWin<DT> WA, WB;
@@ -245,14 +335,18 @@ void contract_kernel(ContractParams p) {
             contract_rows(rowsA, p.perm, win_at(2), lo, hi, lrow);
             contract_load<DT>(WB, q, ldq, PT, p.ldT, rowsB, win_at(1), cq, lcol, rank0, r, lane);
             contract_rows(rowsB, p.perm, win_at(3), lo, hi, lrow);
-            for (int i = 0; i < nw; i += 2) {
+            // (B's multiply is unconditional inside the loop, so the compiler
+            // keeps B's loads where they are issued, a window ahead)
+            int i = 0;
+            for (; i + 1 < nw; i += 2) {
                 contract_compute<DT>(WA, tileA, acc, win_at(i), lo, hi, lcol, lrow, nmb, lane);
                 contract_load<DT>(WA, q, ldq, PT, p.ldT, rowsA, win_at(i + 2), cq, lcol, rank0, r, lane);
                 contract_rows(rowsA, p.perm, win_at(i + 4), lo, hi, lrow);
-                if (i + 1 < nw) contract_compute<DT>(WB, tileB, acc, win_at(i + 1), lo, hi, lcol, lrow, nmb, lane);
+                contract_compute<DT>(WB, tileB, acc, win_at(i + 1), lo, hi, lcol, lrow, nmb, lane);
                 contract_load<DT>(WB, q, ldq, PT, p.ldT, rowsB, win_at(i + 3), cq, lcol, rank0, r, lane);
                 contract_rows(rowsB, p.perm, win_at(i + 5), lo, hi, lrow);
             }
+            if (i < nw) contract_compute<DT>(WA, tileA, acc, win_at(i), lo, hi, lcol, lrow, nmb, lane);
         }
 
         // Fixed-order sum of the waves' tiles; wave nb (< 4) finishes column block nb.
@@ -263,30 +357,112 @@ void contract_kernel(ContractParams p) {
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb) red[((wave * kContractMB + mb) * 4 + nb) * kWave + lane] = acc[mb][nb];
         __syncthreads();
+        const bool whole = w0 == 0 && w1 == c.nwin;
         if (wave < 4) {
             const int nb = wave;
             const float s = ad.scale;
 #pragma unroll
             for (int mb = 0; mb < kContractMB; ++mb) {
-                if (mb < nmb) {
-                    f32x4_t sum = red[(mb * 4 + nb) * kWave + lane];
-#pragma unroll
-                    for (int w = 1; w < NW; ++w) sum += red[((w * kContractMB + mb) * 4 + nb) * kWave + lane];
+                f32x4_t sum = red[(mb * 4 + nb) * kWave + lane];
+#pragma unroll 4
+                for (int w = 1; w < NW; ++w) sum += red[((w * kContractMB + mb) * 4 + nb) * kWave + lane];
+                if (!whole) {
+                    // partial tile for contract_fixup_kernel
+                    float* f = p.fix + ((int64_t)vg * 2 + slot) * kFixFloats;
+                    *gptr(reinterpret_cast<f32x4_t*>(f) + (mb * 4 + nb) * kWave + lane) = sum;
+                } else if (mb < nmb) {
+                    // the four read-modify-writes of a lane: loads first (entries
+                    // outside [0, r) x [0, N) read the tile's first entry and are
+                    // not written), then the stores
                     const int col = c0 + 16 * nb + lr;
-                    if (col < N) {
+                    float* dst[4];
+                    bool ok[4];
+                    float old[4];
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int rk = rank0 + 16 * mb + 4 * lg + i;
-                            if (rk < r) {
-                                float* dst = is_dA ? gr.dA + (int64_t)rk * p.d_in + col : gr.dB + (int64_t)col * r + rk;
-                                *gptr(dst) += s * sum[i];
-                            }
-                        }
+                    for (int i = 0; i < 4; ++i) {
+                        const int rk = rank0 + 16 * mb + 4 * lg + i;
+                        ok[i] = col < N && rk < r;
+                        const int rk_ = ok[i] ? rk : rank0;
+                        const int col_ = ok[i] ? col : c0;
+                        dst[i] = is_dA ? gr.dA + (int64_t)rk_ * p.d_in + col_ : gr.dB + (int64_t)col_ * r + rk_;
+                        old[i] = *gptr(dst[i]);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (ok[i]) *gptr(dst[i]) = old[i] + s * sum[i];
+                }
+            }
+        }
+        if (!whole) {
+            if (threadIdx.x == 0) {
+                const int64_t tile_u = abase + (int64_t)tile_in * c.nwin;  // first unit: the tile's id
+                int32_t* m = meta + slot * kFixMeta;
+                m[0] = (int32_t)(tile_u & 0x7fffffff);
+                m[1] = (int32_t)(tile_u >> 31);
+                m[2] = a;
+                m[3] = rg;
+                m[4] = cb_all;
+                m[5] = w0 == 0;  // owner: holds the tile's first window, runs its fix-up
+            }
+            slot = 1;  // only a workgroup's first and last tiles can be cut
+        } else {
+            slot = 1;
+        }
+        u += w1 - w0;
+        __syncthreads();
+    }
+}
+
+// Adds the partial tiles of each cut tile in workgroup order, then s times
+// the sum to dA / dB.  Workgroup g handles the tile it owns (if any); the
+// later workgroups that hold the same tile follow g in order.
+__global__ __launch_bounds__(4 * kWave) void contract_fixup_kernel(ContractParams p, int G) {
+    const int g0 = blockIdx.x;
+    const int nb = wave_id();
+    const int lane = threadIdx.x & (kWave - 1);
+    const int lr = lane & 15;
+    const int lg = lane >> 4;
+    for (int sl = 0; sl < 2; ++sl) {
+        const int32_t* m = p.fix_meta + ((int64_t)g0 * 2 + sl) * kFixMeta;
+        if (m[0] < 0 || !m[5]) continue;
+        const int32_t id0 = m[0], id1 = m[1];
+        const int a = m[2], rg = m[3], cb_all = m[4];
+        f32x4_t sum[kContractMB];
+#pragma unroll
+        for (int mb = 0; mb < kContractMB; ++mb)
+            sum[mb] = *gptr(reinterpret_cast<const f32x4_t*>(p.fix + ((int64_t)g0 * 2 + sl) * kFixFloats) +
+                            (mb * 4 + nb) * kWave + lane);
+        for (int g = g0 + 1; g < G; ++g) {
+            const int32_t* mg = p.fix_meta + (int64_t)g * 2 * kFixMeta;  // its first tile
+            if (mg[0] == -2) continue;  // no units
+            if (mg[0] != id0 || mg[1] != id1) break;
+#pragma unroll
+            for (int mb = 0; mb < kContractMB; ++mb)
+                sum[mb] += *gptr(reinterpret_cast<const f32x4_t*>(p.fix + (int64_t)g * 2 * kFixFloats) +
+                                 (mb * 4 + nb) * kWave + lane);
+        }
+        const lora_adapter ad = load_adapter(p.adapters, a);
+        const lora_adapter_grad gr = load_grad(p.grads, a);
+        const bool is_dA = cb_all < p.ncb_in;
+        const int r = ad.rank;
+        const int rank0 = rg * 16 * kContractMB;
+        const int nmb = min(kContractMB, (r - rank0 + 15) / 16);
+        const int c0 = (is_dA ? cb_all : cb_all - p.ncb_in) * 64;
+        const int N = is_dA ? p.d_in : p.d_out;
+        const int col = c0 + 16 * nb + lr;
+#pragma unroll
+        for (int mb = 0; mb < kContractMB; ++mb) {
+            if (mb < nmb) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int rk = rank0 + 16 * mb + 4 * lg + i;
+                    if (col < N && rk < r) {
+                        float* dst = is_dA ? gr.dA + (int64_t)rk * p.d_in + col : gr.dB + (int64_t)col * r + rk;
+                        *gptr(dst) += ad.scale * sum[mb][i];
                     }
                 }
             }
         }
-        __syncthreads();
     }
 }
 
