@@ -303,6 +303,20 @@ __device__ __forceinline__ void lds_dma16(const void* src, void* lds_row) {
                                      (__attribute__((address_space(3))) void*)lds_row, 16, 0, 0);
 }
 
+// The same load issued from inline assembly: the compiler does not track it,
+// so it does not order consecutive such loads behind one another (its waits
+// for LDS writes it cannot tell apart).  The caller waits (vmcnt) before any
+// wave reads the bytes; lds_row must be wave-uniform.
+__device__ __forceinline__ void lds_dma16_async(const void* src, void* lds_row) {
+    const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_row;
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "global_load_lds_dwordx4 %1, off"
+        :
+        : "s"(m0), "v"(src)
+        : "memory", "m0");
+}
+
 // s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding:
 // vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 template <int N>

@@ -189,27 +189,10 @@ void shrink_kernel(ShrinkParams p) {
             }
         };
 
-        // 1. Weight slice loads (16-byte units), then this wave's x half-slice
-        //    (chunk c, half h; chunks past the slice re-read its start).
+        // 1. This wave's x half-slice (chunk c, half h; chunks past the slice
+        //    re-read its start), then the weight slice loads (16-byte units).
         F xr[SCH][2];
         if (work) {
-            if constexpr (!TRANS_W) {
-                // Straight into LDS: rank row j = wave + 8 i; lane L fetches unit
-                // L ^ (j % 16) of the row, which lands in slot L of the LDS row.
-                // Rows past the group are not loaded (their MFMA outputs are discarded).
-#pragma unroll
-                for (int i = 0; i < NU; ++i) {
-                    const int j = wave + kShrinkWaves * i;
-                    if (j < nr) {
-                        const int q = lane ^ (j & 15);
-                        const int kq = q * EPU < klen ? q * EPU : 0;
-                        lds_dma16(wbase + ((int64_t)(rank0 + j) * p.K + k0 + kq) * EB, s_w + j * 64);
-                    }
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            } else {
-                if (trans_units) load_tbatch(0);
-            }
             const char* xp = static_cast<const char*>(p.x) + xrow * p.ldx * EB;
 #pragma unroll
             for (int c = 0; c < SCH; ++c)
@@ -219,6 +202,24 @@ void shrink_kernel(ShrinkParams p) {
                     const int kk = (cc < nch ? cc * 64 : 0) + 8 * lg + 32 * h;
                     xr[c][h] = F::load(xp + (int64_t)(k0 + (kk < klen ? kk : 0)) * EB);
                 }
+            if constexpr (!TRANS_W) {
+                // Straight into LDS, issued last (the compiler does not track
+                // these loads; the barrier below waits for them): rank row
+                // j = wave + 8 i; lane L fetches unit L ^ (j % 16) of the row,
+                // which lands in slot L of the LDS row.  Rows past the group are
+                // not loaded (their MFMA outputs are discarded).
+#pragma unroll
+                for (int i = 0; i < NU; ++i) {
+                    const int j = wave + kShrinkWaves * i;
+                    if (j < nr) {
+                        const int q = lane ^ (j & 15);
+                        const int kq = q * EPU < klen ? q * EPU : 0;
+                        lds_dma16_async(wbase + ((int64_t)(rank0 + j) * p.K + k0 + kq) * EB, s_w + j * 64);
+                    }
+                }
+            } else {
+                if (trans_units) load_tbatch(0);
+            }
         }
 
         // 2. Next task's metadata, while this task's loads are in flight.
@@ -227,9 +228,9 @@ void shrink_kernel(ShrinkParams p) {
 
         // 3. Weight slice -> LDS (swizzled rows), then one barrier.
         if constexpr (!TRANS_W) {
-            // this wave's LDS loads were issued before its x loads: wait for all but those
-            __builtin_amdgcn_sched_barrier(0);
-            wait_vmcnt_le<SCH * 2 * (EB / 2)>();
+            // this wave's weight loads into LDS (and its x loads) have landed
+            // before the barrier; a barrier alone does not wait for them
+            wait_vmcnt_le<0>();
         } else if (trans_units) {
             store_tbatch(0);
             for (int b = 1; kShrinkThreads * kTB * b < tunits; ++b) {
