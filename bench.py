@@ -317,6 +317,7 @@ def main():
     t0 = time.perf_counter()
     for i in range(K):
         run(args.warmup + i, None if graphs is not None else evs.get(i))
+    t_enq = time.perf_counter()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / K
@@ -365,6 +366,7 @@ def main():
                    "ft_adapter_rank": r_ft, "seed": 0, "input_sets": args.sets,
                    "launch": "graph" if graphs is not None else "eager",
                    "streams": 2 if args.overlap else 1},
+        "host_enqueue_ms_per_step": (t_enq - t0) * 1e3 / K,
         "step_algorithmic_GBps": alg["step"]["bytes"] / (ms * 1e-3) / 1e9,
         "step_algorithmic_bytes": alg["step"]["bytes"],
         "roofline": {"bound": "hbm", "kernel": "lora_expand_add (expand_kernel)", "achieved": achieved,
