@@ -248,6 +248,13 @@ struct Elem<LORA_BF16> {
         for (int i = 0; i < 4; ++i) q[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
         *gptr(reinterpret_cast<u32x4_t*>(p)) = q;
     }
+    // The same as a nontemporal (streaming) store.
+    __device__ __forceinline__ static void store8_nt(void* p, const float* f) {
+        u32x4_t q;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+        __builtin_nontemporal_store(q, gptr(reinterpret_cast<u32x4_t*>(p)));
+    }
 };
 
 template <>
@@ -276,6 +283,11 @@ struct Elem<LORA_F32> {
         LORA_GLOBAL f32x4_t* v = gptr(reinterpret_cast<f32x4_t*>(p));
         v[0] = f32x4_t{f[0], f[1], f[2], f[3]};
         v[1] = f32x4_t{f[4], f[5], f[6], f[7]};
+    }
+    __device__ __forceinline__ static void store8_nt(void* p, const float* f) {
+        LORA_GLOBAL f32x4_t* v = gptr(reinterpret_cast<f32x4_t*>(p));
+        __builtin_nontemporal_store(f32x4_t{f[0], f[1], f[2], f[3]}, v);
+        __builtin_nontemporal_store(f32x4_t{f[4], f[5], f[6], f[7]}, v + 1);
     }
 };
 

@@ -157,8 +157,9 @@ void expand_kernel(ExpandParams p) {
                 const int64_t row = s_row[16 * st + 8 * u + yr];
                 const LORA_GLOBAL u32x4_t* src =
                     gptr(reinterpret_cast<const u32x4_t*>(ybase + (row * p.ldy + ycol) * EB));
+                // y is read once and written once: streaming (nontemporal) accesses
 #pragma unroll
-                for (int q = 0; q < YQ; ++q) dst[u][q] = src[q];
+                for (int q = 0; q < YQ; ++q) dst[u][q] = __builtin_nontemporal_load(src + q);
             }
         };
 #pragma unroll
@@ -221,7 +222,7 @@ void expand_kernel(ExpandParams p) {
                     }
                     if (col_ok && row_in_tile < nrows) {
                         const int64_t row = s_row[row_in_tile];
-                        E::store8(ybase + (row * p.ldy + ycol) * EB, yv);
+                        E::store8_nt(ybase + (row * p.ldy + ycol) * EB, yv);
                     }
                 }
                 __builtin_amdgcn_wave_barrier();
