@@ -51,21 +51,6 @@ struct BwdWs {
 };
 }  // namespace lora
 
-namespace {
-
-// vT[k][pos] = v[perm[pos]][k] for pos < n_valid, k < r_max: the caller's saved v,
-// rank-major by sorted position as the token contraction reads it.
-__global__ void transpose_v_kernel(const float* __restrict__ v, int64_t ldv, const int32_t* __restrict__ perm,
-                                   const int32_t* __restrict__ n_valid, int32_t r_max, float* __restrict__ vT,
-                                   int64_t ldT, int32_t T) {
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t pos = idx % T;
-    const int64_t k = idx / T;
-    if (k >= r_max || pos >= *n_valid) return;
-    vT[k * ldT + pos] = v[(int64_t)perm[pos] * ldv + k];
-}
-}  // namespace
-
 extern "C" size_t lora_backward_workspace_bytes(int dtype, int32_t T_ft, int32_t d_in, int32_t d_out, int32_t r_max) {
     if (!valid_dtype(dtype) || T_ft < 0 || d_in < 1 || d_out < 1 || r_max < 1 || r_max > LORA_MAX_RANK) return 0;
     return (size_t)BwdWs::make(dtype, T_ft, d_in, d_out, r_max).total * sizeof(float);
@@ -126,15 +111,15 @@ extern "C" int lora_backward(int dtype, const void* x, int64_t ldx, const void* 
     rp.out_by_pos = 1;
     rp.outT = gT;
     rp.ldT = w.ldT;
-    if ((rc = run_shrink(dtype, true, sp, rp, T_ft, num_adapters, st)) != LORA_OK) return rc;
-
-    // 2. v = A x, rank-major by sorted position.
+    // 2. v = A x, rank-major by sorted position: the caller's v, copied by the
+    //    reduce of g, or a second shrink.
     if (v_saved) {
-        const int64_t n = (int64_t)T_ft * r_max;
-        hipLaunchKernelGGL(transpose_v_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, v_saved, ldv,
-                           seg_ft.perm, seg_ft.offsets + num_adapters, r_max, vT, w.ldT, T_ft);
-        if (hipGetLastError() != hipSuccess) return LORA_ERR_HIP;
-    } else {
+        rp.vsrc = v_saved;
+        rp.ldvsrc = ldv;
+        rp.vT = vT;
+    }
+    if ((rc = run_shrink(dtype, true, sp, rp, T_ft, num_adapters, st)) != LORA_OK) return rc;
+    if (!v_saved) {
         ShrinkParams vp = sp;
         vp.x = x;
         vp.ldx = ldx;
@@ -144,6 +129,7 @@ extern "C" int lora_backward(int dtype, const void* x, int64_t ldx, const void* 
         vr.nslices = vp.nslices;
         vr.out = nullptr;
         vr.outT = vT;
+        vr.vsrc = nullptr;
         if ((rc = run_shrink(dtype, false, vp, vr, T_ft, num_adapters, st)) != LORA_OK) return rc;
     }
 

@@ -69,6 +69,7 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void shrink_reduce_kernel(Red
         const bool row_ok = n < rec.rows;
         const int pos = rec.pos0 + (row_ok ? n : 0);
         const int64_t orow = wave == 0 && p.out && !p.out_by_pos ? p.perm[pos] : pos;
+        const int64_t vrow = wave == 1 && p.vsrc ? p.perm[pos] : 0;
         // quads at or past r hold no partial (and may lie past the workspace): not read
         const float* src = p.part + (int64_t)pos * p.ldp + 4 * q;
         f32x4_t acc[kReduceJ];
@@ -87,6 +88,20 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void shrink_reduce_kernel(Red
                 if (j < nj) s_acc[wave - 1][j][lane] = acc[j];
         }
         lds_barrier();
+        if (wave == 1 && p.vsrc && row_ok) {
+            // rank-major copy of the caller's v rows of this tile (quads below
+            // round_up(r, 4) <= the caller's pitch)
+#pragma unroll
+            for (int j = 0; j < kReduceJ; ++j) {
+                const int k = 16 * j + 4 * q;
+                if (j < nj && k < r) {
+                    const f32x4_t vv = *gptr(reinterpret_cast<const f32x4_t*>(p.vsrc + vrow * p.ldvsrc + k));
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (k + i < r) gptr(p.vT)[(int64_t)(k + i) * p.ldT + pos] = vv[i];
+                }
+            }
+        }
         if (wave == 0 && row_ok) {
 #pragma unroll
             for (int j = 0; j < kReduceJ; ++j) {

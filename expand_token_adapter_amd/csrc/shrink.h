@@ -308,6 +308,11 @@ struct ReduceParams {
     int32_t out_by_pos;
     float* outT;
     int64_t ldT;
+    // optional rank-major copy of a caller's v: vT[k][pos] = vsrc[perm[pos]][k]
+    // for k < r_a (pitch ldT), written alongside the sum of the same tile
+    const float* vsrc;
+    int64_t ldvsrc;
+    float* vT;
 };
 
 // shrink_reduce_kernel(ReduceParams) is defined in forward.hip.
