@@ -1,8 +1,8 @@
 """Throughput of the multi-LoRA batched adapter path on one MI355X.
 
 One step = the whole hot path over one mixed co-serving batch (seed 0):
-  lora_segments_build (all rows) -> lora_shrink -> lora_expand_add
-  -> lora_segments_build (fine-tuning rows) -> lora_backward (dX, dA, dB),
+  lora_segments_build_batch (all rows, and the fine-tuning rows) ->
+  lora_shrink -> lora_expand_add -> lora_backward (dX, dA, dB),
 with the forward's v of the fine-tuning rows passed to the backward as the
 saved v.  `--workload` selects another of the synthetic workloads (the
 backward runs only where the workload has fine-tuning rows).  Workload: 128 decode rows, 8 prefill segments of U[128, 1024]
@@ -258,7 +258,6 @@ def main():
     side = torch.cuda.Stream(device=dev) if args.overlap else None  # default priority
 
     def backward(st, v_saved):
-        lb.lora_segments_build(st["ft_ids"], wl.num_adapters, out=st["seg_ft"])
         lb.lora_backward(st["x"][s:s + n], st["dy"], st["table"], st["grads"], st["seg_ft"], dx=st["dx"],
                          v_saved=v_saved, ws=st["ws"])
 
@@ -266,8 +265,13 @@ def main():
         if side is not None and has_ft:
             side.wait_stream(torch.cuda.current_stream(dev))
             with torch.cuda.stream(side):
+                lb.lora_segments_build(st["ft_ids"], wl.num_adapters, out=st["seg_ft"])
                 backward(st, None)
-        lb.lora_segments_build(st["ids"], wl.num_adapters, out=st["seg"])
+        if has_ft and side is None:
+            # the batch's rows and its fine-tuning rows grouped in one launch
+            lb.lora_segments_build_batch([(st["ids"], st["seg"]), (st["ft_ids"], st["seg_ft"])], wl.num_adapters)
+        else:
+            lb.lora_segments_build(st["ids"], wl.num_adapters, out=st["seg"])
         lb.lora_shrink(st["x"], st["table"], st["seg"], v=st["v"], ws=st["ws_shrink"])
         if ev is not None:
             ev[0].record()

@@ -23,7 +23,7 @@ from ._abi import LORA_BF16, LORA_F32, LORA_MAX_RANK, LoraError
 
 __all__ = [
     "AdapterTable", "GradTable", "Segments", "LoraError",
-    "lora_segments_build", "lora_shrink", "lora_expand_add", "lora_backward",
+    "lora_segments_build", "lora_segments_build_batch", "lora_shrink", "lora_expand_add", "lora_backward",
     "lora_abi_version", "lora_status_string",
     "lora_segments_workspace_bytes", "lora_shrink_workspace_bytes", "lora_backward_workspace_bytes",
     "lora_segments_sched_elems",
@@ -189,6 +189,29 @@ def lora_segments_build(adapter_ids: torch.Tensor, num_adapters: int, out: Optio
                                          seg.ws.numel(), _stream(adapter_ids.device))
     _abi.check("lora_segments_build", st)
     return seg
+
+
+def lora_segments_build_batch(jobs, num_adapters: int) -> list:
+    """Several lora_segments_build calls in one enqueue: jobs = [(adapter_ids, out Segments or None), ...]
+    on one device; the one-workgroup builds share launches.  Returns the Segments, in order."""
+    segs, raw = [], []
+    for ids, out in jobs:
+        _on_gpu(ids)
+        if ids.dtype != torch.int32 or ids.dim() != 1 or not ids.is_contiguous():
+            raise ValueError("adapter_ids must be a contiguous 1-D int32 tensor")
+        T = int(ids.shape[0])
+        seg = out if out is not None else Segments(T, num_adapters, ids.device)
+        if seg.T != T or seg.num_adapters != num_adapters:
+            raise ValueError("Segments buffers were sized for another batch")
+        segs.append(seg)
+        raw.append(_abi.LoraSegmentsJob(ids.data_ptr(), T, seg.c, seg.ws.data_ptr(), seg.ws.numel()))
+    if not segs:
+        return segs
+    arr = (_abi.LoraSegmentsJob * len(raw))(*raw)
+    st = _abi.load().lora_segments_build_batch(ctypes.addressof(arr), len(raw), num_adapters,
+                                               _stream(jobs[0][0].device))
+    _abi.check("lora_segments_build_batch", st)
+    return segs
 
 
 def lora_shrink(x: torch.Tensor, adapters: AdapterTable, seg: Segments, v: Optional[torch.Tensor] = None,

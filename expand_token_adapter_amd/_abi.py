@@ -40,6 +40,10 @@ class LoraSegments(ctypes.Structure):
     _fields_ = [("counts", _vp), ("offsets", _vp), ("perm", _vp), ("err", _vp), ("sched", _vp)]
 
 
+class LoraSegmentsJob(ctypes.Structure):
+    _fields_ = [("adapter_ids", _vp), ("T", _i32), ("seg", LoraSegments), ("ws", _vp), ("ws_bytes", _sz)]
+
+
 SIGNATURES = {
     "lora_abi_version": (ctypes.c_int, []),
     "lora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -48,6 +52,7 @@ SIGNATURES = {
     "lora_shrink_workspace_bytes": (_sz, [ctypes.c_int, _i32, _i32, _i32]),
     "lora_backward_workspace_bytes": (_sz, [ctypes.c_int, _i32, _i32, _i32, _i32]),
     "lora_segments_build": (ctypes.c_int, [_vp, _i32, _i32, LoraSegments, _vp, _sz, _vp]),
+    "lora_segments_build_batch": (ctypes.c_int, [_vp, _i32, _i32, _vp]),
     "lora_shrink": (ctypes.c_int, [ctypes.c_int, _vp, _i64, _i32, _i32, _vp, _i32, _i32, LoraSegments,
                                    _vp, _i64, _vp, _sz, _vp]),
     "lora_expand_add": (ctypes.c_int, [ctypes.c_int, _vp, _i64, _i32, _i32, _vp, _i32, _i32, LoraSegments,

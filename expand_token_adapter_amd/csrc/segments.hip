@@ -256,13 +256,33 @@ constexpr int kSmallMaxT = 1 << 16;
 constexpr int kSmallWaves = kScanThreads / kWave;
 constexpr int kSmallBatch = 8;  // 64-row groups per load batch
 
-__global__ __launch_bounds__(kScanThreads) void seg_small_kernel(const int32_t* __restrict__ ids, int32_t T,
-                                                                 int32_t A, int32_t* __restrict__ counts,
-                                                                 int32_t* __restrict__ offsets,
-                                                                 int32_t* __restrict__ perm,
-                                                                 int32_t* __restrict__ sched, int32_t* __restrict__ err,
-                                                                 int64_t active_off, int64_t tiles16_off,
-                                                                 int64_t tiles64_off) {
+// One build of the one-workgroup path; a launch carries up to kSegBatchMax
+// independent builds, one workgroup each (blockIdx.x selects the build).
+struct SegSmallJob {
+    const int32_t* ids;
+    int32_t T;
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* perm;
+    int32_t* sched;
+    int32_t* err;
+    int64_t active_off, tiles16_off, tiles64_off;
+};
+constexpr int kSegBatchMax = LORA_SEG_BATCH_MAX;
+struct SegSmallJobs {
+    SegSmallJob job[kSegBatchMax];
+};
+
+__global__ __launch_bounds__(kScanThreads) void seg_small_kernel(SegSmallJobs jobs, int32_t A) {
+    const SegSmallJob& job = jobs.job[blockIdx.x];
+    const int32_t* __restrict__ ids = job.ids;
+    const int32_t T = job.T;
+    int32_t* __restrict__ counts = job.counts;
+    int32_t* __restrict__ offsets = job.offsets;
+    int32_t* __restrict__ perm = job.perm;
+    int32_t* __restrict__ sched = job.sched;
+    int32_t* __restrict__ err = job.err;
+    const int64_t active_off = job.active_off, tiles16_off = job.tiles16_off, tiles64_off = job.tiles64_off;
     __shared__ int s_hist[kSmallWaves][kSmallMaxA];
     __shared__ int4 s_info[kSmallMaxA];  // offset, count, 16-row tile prefix, 64-row tile prefix
     __shared__ int4 s_tot[kSmallWaves];
@@ -404,24 +424,30 @@ extern "C" size_t lora_segments_workspace_bytes(int32_t T, int32_t num_adapters)
     return (size_t)SegWs::make(T, num_adapters).total * sizeof(int32_t);
 }
 
-extern "C" int lora_segments_build(const int32_t* adapter_ids, int32_t T, int32_t num_adapters, lora_segments seg,
-                                   void* ws, size_t ws_bytes, void* stream) {
+namespace {
+// Host-side checks of one build (nothing enqueued on failure).
+int seg_check(const int32_t* adapter_ids, int32_t T, int32_t num_adapters, const lora_segments& seg, const void* ws,
+              size_t ws_bytes) {
     if (T < 0 || num_adapters < 1) return LORA_ERR_INVALID_ARG;
     if (T == 0) return LORA_OK;
     if (!adapter_ids || !seg.counts || !seg.offsets || !seg.perm || !seg.err || !seg.sched) return LORA_ERR_INVALID_ARG;
     if (((uintptr_t)seg.sched & 15u) != 0) return LORA_ERR_INVALID_ARG;
+    if (!ws || ws_bytes < (size_t)SegWs::make(T, num_adapters).total * sizeof(int32_t)) return LORA_ERR_WORKSPACE;
+    return LORA_OK;
+}
+bool seg_small(int32_t T, int32_t num_adapters) { return T <= kSmallMaxT && num_adapters <= kSmallMaxA; }
+SegSmallJob small_job(const int32_t* adapter_ids, int32_t T, int32_t num_adapters, const lora_segments& seg) {
+    const SchedLayout sl = SchedLayout::make(T, num_adapters);
+    return SegSmallJob{adapter_ids, T, seg.counts, seg.offsets, seg.perm, seg.sched, seg.err,
+                       sl.active, sl.tiles16, sl.tiles64};
+}
+// The three-kernel path for batches beyond the one-workgroup limits.
+void seg_large(const int32_t* adapter_ids, int32_t T, int32_t num_adapters, const lora_segments& seg, void* ws,
+               hipStream_t st) {
     const SegWs w = SegWs::make(T, num_adapters);
-    if (!ws || ws_bytes < (size_t)w.total * sizeof(int32_t)) return LORA_ERR_WORKSPACE;
-    const int64_t nchunks64 = ((int64_t)T + kChunk - 1) / kChunk;
-    const int32_t nchunks = (int32_t)nchunks64;
+    const int32_t nchunks = (int32_t)(((int64_t)T + kChunk - 1) / kChunk);
     const SchedLayout sl = SchedLayout::make(T, num_adapters);
     int32_t* wsi = static_cast<int32_t*>(ws);
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    if (T <= kSmallMaxT && num_adapters <= kSmallMaxA) {
-        hipLaunchKernelGGL(seg_small_kernel, dim3(1), dim3(kScanThreads), 0, st, adapter_ids, T, num_adapters,
-                           seg.counts, seg.offsets, seg.perm, seg.sched, seg.err, sl.active, sl.tiles16, sl.tiles64);
-        return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
-    }
     hipLaunchKernelGGL(seg_count_kernel, dim3(nchunks), dim3(kChunk), 0, st, adapter_ids, T, num_adapters, nchunks,
                        wsi + w.hist, wsi + w.rank, wsi + w.errc);
     hipLaunchKernelGGL(seg_scan_kernel, dim3(1), dim3(kScanThreads), 0, st, num_adapters, nchunks, wsi + w.hist,
@@ -430,5 +456,50 @@ extern "C" int lora_segments_build(const int32_t* adapter_ids, int32_t T, int32_
     hipLaunchKernelGGL(seg_scatter_kernel, dim3(nchunks), dim3(kChunk), 0, st, adapter_ids, T, num_adapters, nchunks,
                        wsi + w.hist, wsi + w.rank, seg.counts, seg.offsets, wsi + w.pre16, wsi + w.pre64, seg.perm,
                        seg.sched, sl.tiles16, sl.tiles64);
+}
+}  // namespace
+
+extern "C" int lora_segments_build(const int32_t* adapter_ids, int32_t T, int32_t num_adapters, lora_segments seg,
+                                   void* ws, size_t ws_bytes, void* stream) {
+    const int rc = seg_check(adapter_ids, T, num_adapters, seg, ws, ws_bytes);
+    if (rc != LORA_OK || T == 0) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (seg_small(T, num_adapters)) {
+        SegSmallJobs jobs{};
+        jobs.job[0] = small_job(adapter_ids, T, num_adapters, seg);
+        hipLaunchKernelGGL(seg_small_kernel, dim3(1), dim3(kScanThreads), 0, st, jobs, num_adapters);
+    } else {
+        seg_large(adapter_ids, T, num_adapters, seg, ws, st);
+    }
+    return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
+extern "C" int lora_segments_build_batch(const lora_segments_job* jobs, int32_t n_jobs, int32_t num_adapters,
+                                         void* stream) {
+    if (n_jobs < 0 || (n_jobs > 0 && !jobs)) return LORA_ERR_INVALID_ARG;
+    if (n_jobs == 0) return LORA_OK;
+    for (int32_t i = 0; i < n_jobs; ++i) {
+        const lora_segments_job& j = jobs[i];
+        const int rc = seg_check(j.adapter_ids, j.T, num_adapters, j.seg, j.ws, j.ws_bytes);
+        if (rc != LORA_OK) return rc;
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    SegSmallJobs batch{};
+    int nb = 0;
+    auto flush = [&]() {
+        if (nb > 0) hipLaunchKernelGGL(seg_small_kernel, dim3(nb), dim3(kScanThreads), 0, st, batch, num_adapters);
+        nb = 0;
+    };
+    for (int32_t i = 0; i < n_jobs; ++i) {
+        const lora_segments_job& j = jobs[i];
+        if (j.T == 0) continue;
+        if (seg_small(j.T, num_adapters)) {
+            batch.job[nb++] = small_job(j.adapter_ids, j.T, num_adapters, j.seg);
+            if (nb == kSegBatchMax) flush();
+        } else {
+            seg_large(j.adapter_ids, j.T, num_adapters, j.seg, j.ws, st);
+        }
+    }
+    flush();
     return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }

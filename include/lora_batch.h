@@ -154,6 +154,34 @@ size_t lora_backward_workspace_bytes(int dtype, int32_t T_ft, int32_t d_in, int3
 int lora_segments_build(const int32_t* adapter_ids, int32_t T, int32_t num_adapters,
                         lora_segments seg, void* ws, size_t ws_bytes, void* stream);
 
+/* One build of lora_segments_build_batch (all pointers device, as in
+ * lora_segments_build; the struct array itself lives in host memory). */
+typedef struct lora_segments_job {
+    const int32_t* adapter_ids; /* [T] */
+    int32_t T;
+    lora_segments seg;
+    void* ws;                   /* lora_segments_workspace_bytes(T, num_adapters) bytes */
+    size_t ws_bytes;
+} lora_segments_job;
+
+/* Builds per launch of lora_segments_build_batch's one-workgroup path. */
+#define LORA_SEG_BATCH_MAX 8
+
+/*
+ * Several independent lora_segments_build calls over the same adapter table
+ * size, enqueued together: builds of up to 65536 rows (and num_adapters <=
+ * 1024) share one launch, one workgroup each, LORA_SEG_BATCH_MAX per launch;
+ * larger ones take the three-kernel path one after the other.  Typical use:
+ * the whole mixed batch and its fine-tuning rows (the rows the backward
+ * reads), which multi-LoRA co-serving groups separately (DeltaServe, sections
+ * 2.2 and 3.2).  Outputs are identical to one lora_segments_build per job.
+ * Every job is checked on the host first; if any check fails nothing is
+ * enqueued and its status is returned.  jobs: host array of n_jobs >= 0
+ * entries (NULL allowed when n_jobs == 0); jobs with T == 0 are skipped.
+ * The jobs must not share output or workspace buffers.
+ */
+int lora_segments_build_batch(const lora_segments_job* jobs, int32_t n_jobs, int32_t num_adapters, void* stream);
+
 /*
  * Shrink: v_t = A_{a(t)} x_t with fp32 accumulation, for every row with an
  * adapter (the "A x" of h(x) = W x + B A x, MOLT section 2.1).

@@ -42,6 +42,8 @@ def test_struct_sizes_match_header():
     assert ctypes.sizeof(_abi.LoraAdapter) == 24
     assert ctypes.sizeof(_abi.LoraAdapterGrad) == 16
     assert ctypes.sizeof(_abi.LoraSegments) == 40
+    assert ctypes.sizeof(_abi.LoraSegmentsJob) == 72
+    assert _abi.LoraSegmentsJob.seg.offset == 16 and _abi.LoraSegmentsJob.ws_bytes.offset == 64
 
 
 def test_workspace_queries(lib):
@@ -124,6 +126,28 @@ def test_segments_build_rejects(lib):
     assert lib.lora_segments_build(FAKE, 100, 4, _seg(False), FAKE, need, None) == _abi.LORA_ERR_INVALID_ARG
     assert lib.lora_segments_build(FAKE, 100, 4, _seg(), FAKE, need - 1, None) == _abi.LORA_ERR_WORKSPACE
     assert lib.lora_segments_build(FAKE, 100, 4, _seg(), 0, need, None) == _abi.LORA_ERR_WORKSPACE
+
+
+def test_segments_build_batch_rejects(lib):
+    need = lib.lora_segments_workspace_bytes(100, 4)
+
+    def jobs(*js):
+        arr = (_abi.LoraSegmentsJob * len(js))(*js)
+        return ctypes.addressof(arr), arr
+
+    good = _abi.LoraSegmentsJob(FAKE, 100, _seg(), FAKE, need)
+    assert lib.lora_segments_build_batch(None, 0, 4, None) == _abi.LORA_OK  # nothing to do
+    assert lib.lora_segments_build_batch(None, -1, 4, None) == _abi.LORA_ERR_INVALID_ARG
+    assert lib.lora_segments_build_batch(None, 2, 4, None) == _abi.LORA_ERR_INVALID_ARG
+    # any bad job rejects the whole call before anything is enqueued
+    for bad, code in [(_abi.LoraSegmentsJob(FAKE, -1, _seg(), FAKE, need), _abi.LORA_ERR_INVALID_ARG),
+                      (_abi.LoraSegmentsJob(0, 100, _seg(), FAKE, need), _abi.LORA_ERR_INVALID_ARG),
+                      (_abi.LoraSegmentsJob(FAKE, 100, _seg(False), FAKE, need), _abi.LORA_ERR_INVALID_ARG),
+                      (_abi.LoraSegmentsJob(FAKE, 100, _seg(), FAKE, need - 1), _abi.LORA_ERR_WORKSPACE)]:
+        ptr, _keep = jobs(good, bad)
+        assert lib.lora_segments_build_batch(ptr, 2, 4, None) == code
+    ptr, _keep = jobs(good)
+    assert lib.lora_segments_build_batch(ptr, 1, 0, None) == _abi.LORA_ERR_INVALID_ARG
 
 
 def test_shrink_workspace_rejected(lib):

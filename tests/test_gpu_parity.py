@@ -59,6 +59,32 @@ def test_segments_bit_exact(kind, T, A):
     assert int(seg.err.item()) == err
 
 
+def test_segments_build_batch_matches_single_builds():
+    """One batched call == one lora_segments_build per job, bit for bit, and the oracle;
+    covers a three-kernel job, an empty job, bad ids and more jobs than one launch holds."""
+    rng = np.random.default_rng(5)
+    A = 32
+    cases = [rng.integers(-1, A, size=8185), rng.integers(0, A, size=2048), rng.integers(-1, A, size=70001),
+             np.zeros(0), rng.integers(-4, A + 4, size=300)]
+    cases += [rng.integers(-1, A, size=int(n)) for n in rng.integers(1, 3000, size=6)]
+    ids = [torch.from_numpy(np.ascontiguousarray(c, dtype=np.int32)).cuda() for c in cases]
+    batch = lb.lora_segments_build_batch([(t, None) for t in ids], A)
+    singles = [lb.lora_segments_build(t, A) for t in ids]
+    torch.cuda.synchronize()
+    assert len(batch) == len(cases)
+    for c, b, one in zip(cases, batch, singles):
+        for name in ("counts", "offsets", "err", "sched"):
+            assert torch.equal(getattr(b, name), getattr(one, name)), name
+        counts, offsets, perm, err = oracle.segments(np.ascontiguousarray(c, dtype=np.int32), A)
+        n = int(offsets[-1])
+        assert np.array_equal(b.counts.cpu().numpy(), counts)
+        assert np.array_equal(b.offsets.cpu().numpy(), offsets)
+        assert np.array_equal(b.perm.cpu().numpy()[:n], perm)
+        assert np.array_equal(one.perm.cpu().numpy()[:n], perm)
+        if len(c):
+            assert int(b.err.item()) == err
+
+
 def _check_forward(case, tol):
     y, v, seg = case.forward()
     y_ref, v_ref = case.oracle_forward()
