@@ -24,8 +24,8 @@ int run_shrink(int dtype, bool trans_w, const ShrinkParams& p, const ReduceParam
                hipStream_t st);
 int64_t shrink_part_ld(int32_t r_max);
 int64_t shrink_part_floats(int dtype, int32_t T, int32_t K, int32_t r_max);
-int run_expand(int dtype, bool trans_w, const ExpandParams& p, int32_t T, int32_t num_adapters, int32_t r_max,
-               hipStream_t st);
+int expand_plan(const ExpandParams& p, int32_t T, int32_t num_adapters, int32_t r_max, ExpandParams* q,
+                unsigned* grid);
 
 // Workspace layout of lora_backward (fp32 elements): g by sorted position
 // (row-major and rank-major), v rank-major, and the split-K partials of the
@@ -50,6 +50,33 @@ struct BwdWs {
     }
 };
 }  // namespace lora
+
+namespace {
+// dX += s A^T g on the first n_expand workgroups and the contraction's fix-up
+// of cut tiles on the kContractGrid after them: one launch for two
+// independent steps (the fix-up's few, latency-bound workgroups run beside
+// the expand's).
+template <int DT, int KS>
+__global__ __launch_bounds__(kExpandWaves * kWave) __attribute__((amdgpu_waves_per_eu(KS == 4 ? 2 : 3)))
+void dx_fixup_kernel(ExpandParams ep, ContractParams cp, int n_expand) {
+    static_assert(kExpandWaves == 4, "the fix-up runs on 4-wave workgroups");
+    if ((int)blockIdx.x < n_expand)
+        expand_body<DT, true, KS>(ep, blockIdx.x, n_expand);
+    else
+        contract_fixup_body(cp, kContractGrid, (int)blockIdx.x - n_expand);
+}
+
+template <int DT>
+void launch_dx_fixup(int ks, const ExpandParams& ep, const ContractParams& cp, unsigned n_expand, hipStream_t st) {
+    const dim3 grid(n_expand + kContractGrid), block(kExpandWaves * kWave);
+    if (ks == 1)
+        hipLaunchKernelGGL((dx_fixup_kernel<DT, 1>), grid, block, 0, st, ep, cp, (int)n_expand);
+    else if (ks == 2)
+        hipLaunchKernelGGL((dx_fixup_kernel<DT, 2>), grid, block, 0, st, ep, cp, (int)n_expand);
+    else
+        hipLaunchKernelGGL((dx_fixup_kernel<DT, 4>), grid, block, 0, st, ep, cp, (int)n_expand);
+}
+}  // namespace
 
 extern "C" size_t lora_backward_workspace_bytes(int dtype, int32_t T_ft, int32_t d_in, int32_t d_out, int32_t r_max) {
     if (!valid_dtype(dtype) || T_ft < 0 || d_in < 1 || d_out < 1 || r_max < 1 || r_max > LORA_MAX_RANK) return 0;
@@ -133,24 +160,7 @@ extern "C" int lora_backward(int dtype, const void* x, int64_t ldx, const void* 
         if ((rc = run_shrink(dtype, false, vp, vr, T_ft, num_adapters, st)) != LORA_OK) return rc;
     }
 
-    // 3. dX += s A^T g.
-    if (dx) {
-        ExpandParams ep{};
-        ep.v = g;
-        ep.ldv = w.ldg;
-        ep.v_by_pos = 1;
-        ep.adapters = adapters;
-        ep.r_max = r_max;
-        ep.perm = seg_ft.perm;
-        ep.sched = seg_ft.sched;
-        ep.y = dx;
-        ep.ldy = lddx;
-        ep.N = d_in;
-        ep.err = seg_ft.err;
-        if ((rc = run_expand(dtype, true, ep, T_ft, num_adapters, r_max, st)) != LORA_OK) return rc;
-    }
-
-    // 4. dA += s g^T x, dB += s dy^T v.
+    // 3. dA += s g^T x, dB += s dy^T v.
     ContractParams cp{};
     cp.x = x;
     cp.ldx = ldx;
@@ -181,6 +191,31 @@ extern "C" int lora_backward(int dtype, const void* x, int64_t ldx, const void* 
     else
         hipLaunchKernelGGL(contract_kernel<LORA_F32>, dim3(kContractGrid), dim3(contract_waves<LORA_F32>() * kWave), 0,
                            st, cp);
-    hipLaunchKernelGGL(contract_fixup_kernel, dim3(kContractGrid), dim3(4 * kWave), 0, st, cp, (int)kContractGrid);
+    if (hipGetLastError() != hipSuccess) return LORA_ERR_HIP;
+
+    // 4. dX += s A^T g, in the launch of the contraction's fix-up.
+    if (dx) {
+        ExpandParams ep{};
+        ep.v = g;
+        ep.ldv = w.ldg;
+        ep.v_by_pos = 1;
+        ep.adapters = adapters;
+        ep.r_max = r_max;
+        ep.perm = seg_ft.perm;
+        ep.sched = seg_ft.sched;
+        ep.y = dx;
+        ep.ldy = lddx;
+        ep.N = d_in;
+        ep.err = seg_ft.err;
+        ExpandParams q;
+        unsigned n_expand;
+        const int ks = expand_plan(ep, T_ft, num_adapters, r_max, &q, &n_expand);
+        if (dtype == LORA_BF16)
+            launch_dx_fixup<LORA_BF16>(ks, q, cp, n_expand, st);
+        else
+            launch_dx_fixup<LORA_F32>(ks, q, cp, n_expand, st);
+    } else {
+        hipLaunchKernelGGL(contract_fixup_kernel, dim3(kContractGrid), dim3(4 * kWave), 0, st, cp, (int)kContractGrid);
+    }
     return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }

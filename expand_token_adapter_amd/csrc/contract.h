@@ -416,8 +416,8 @@ void contract_kernel(ContractParams p) {
 // Adds the partial tiles of each cut tile in workgroup order, then s times
 // the sum to dA / dB.  Workgroup g handles the tile it owns (if any); the
 // later workgroups that hold the same tile follow g in order.
-__global__ __launch_bounds__(4 * kWave) void contract_fixup_kernel(ContractParams p, int G) {
-    const int g0 = blockIdx.x;
+// (as workgroup g0 of a 4-wave grid part)
+__device__ __forceinline__ void contract_fixup_body(const ContractParams& p, int G, int g0) {
     const int nb = wave_id();
     const int lane = threadIdx.x & (kWave - 1);
     const int lr = lane & 15;
@@ -464,6 +464,10 @@ __global__ __launch_bounds__(4 * kWave) void contract_fixup_kernel(ContractParam
             }
         }
     }
+}
+
+__global__ __launch_bounds__(4 * kWave) void contract_fixup_kernel(ContractParams p, int G) {
+    contract_fixup_body(p, G, blockIdx.x);
 }
 
 }  // namespace lora

@@ -363,15 +363,19 @@ struct SchedLayout {
 struct TaskSlice {
     int64_t begin, end, stride;
 };
-__device__ __forceinline__ TaskSlice xcd_slice(int64_t n, int units_per_wg, int unit) {
-    const int x = blockIdx.x % kNumXcd;
+// (for workgroup b of G, G a multiple of 8, placed at launch index b)
+__device__ __forceinline__ TaskSlice xcd_slice_of(int b, int G, int64_t n, int units_per_wg, int unit) {
+    const int x = b % kNumXcd;
     const int64_t per = (n + kNumXcd - 1) / kNumXcd;
     TaskSlice s;
     s.begin = (int64_t)x * per;
     s.end = s.begin + per < n ? s.begin + per : n;
-    s.begin += (int64_t)(blockIdx.x / kNumXcd) * units_per_wg + unit;
-    s.stride = (int64_t)(gridDim.x / kNumXcd) * units_per_wg;
+    s.begin += (int64_t)(b / kNumXcd) * units_per_wg + unit;
+    s.stride = (int64_t)(G / kNumXcd) * units_per_wg;
     return s;
+}
+__device__ __forceinline__ TaskSlice xcd_slice(int64_t n, int units_per_wg, int unit) {
+    return xcd_slice_of(blockIdx.x, gridDim.x, n, units_per_wg, unit);
 }
 
 // Table entries and tile records, read with global loads.

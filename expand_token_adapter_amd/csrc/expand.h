@@ -48,9 +48,11 @@ struct ExpandParams {
     int32_t* err;
 };
 
+// The kernel's work as workgroup blk of nblk (nblk a multiple of 8, the
+// workgroup at launch index blk), so that another kernel can run it on part
+// of its grid.
 template <int DT, bool TRANS_W, int KS>
-__global__ __launch_bounds__(kExpandWaves * kWave) __attribute__((amdgpu_waves_per_eu(KS == 4 ? 2 : 3)))
-void expand_kernel(ExpandParams p) {
+__device__ __forceinline__ void expand_body(const ExpandParams& p, int blk, int nblk) {
     using F = Frag<DT>;
     using E = Elem<DT>;
     using O = F32Operand<DT>;
@@ -74,7 +76,7 @@ void expand_kernel(ExpandParams p) {
     const int yc = 8 * (lane & 7);  // first column (of the wave's 64) in that layout
     const int ncg = (p.N + kExpandCols - 1) / kExpandCols;
     const int64_t n_tasks = (int64_t)p.sched[1] * ncg;
-    const TaskSlice ts = xcd_slice(n_tasks, 1, 0);
+    const TaskSlice ts = xcd_slice_of(blk, nblk, n_tasks, 1, 0);
     char* ybase = static_cast<char*>(p.y);
     float* tw = &s_t[wave][0];
 
@@ -231,6 +233,12 @@ void expand_kernel(ExpandParams p) {
         }
         __syncthreads();  // s_row / s_frag are rewritten by the next task
     }
+}
+
+template <int DT, bool TRANS_W, int KS>
+__global__ __launch_bounds__(kExpandWaves * kWave) __attribute__((amdgpu_waves_per_eu(KS == 4 ? 2 : 3)))
+void expand_kernel(ExpandParams p) {
+    expand_body<DT, TRANS_W, KS>(p, blockIdx.x, gridDim.x);
 }
 
 }  // namespace lora

@@ -150,13 +150,22 @@ int64_t shrink_part_floats(int dtype, int32_t T, int32_t K, int32_t r_max) {
     return (int64_t)shrink_slices(dtype, K) * (T > 0 ? T : 1) * shrink_part_ld(r_max);
 }
 
+// Rank-split, tile offset and grid of an expand launch (shared with the
+// backward, which runs the dX expand together with another kernel).
+int expand_plan(const ExpandParams& p, int32_t T, int32_t num_adapters, int32_t r_max, ExpandParams* q,
+                unsigned* grid) {
+    *q = p;
+    q->tiles64_off = SchedLayout::make(T, num_adapters).tiles64;
+    const int64_t tasks = SchedLayout::max_tiles64(T, num_adapters) * ((p.N + kExpandCols - 1) / kExpandCols);
+    *grid = grid_for(tasks, 1, kMaxGrid);
+    return r_max <= 32 ? 1 : (r_max <= 64 ? 2 : 4);
+}
+
 int run_expand(int dtype, bool trans_w, const ExpandParams& p, int32_t T, int32_t num_adapters, int32_t r_max,
                hipStream_t st) {
-    const int ks = r_max <= 32 ? 1 : (r_max <= 64 ? 2 : 4);
-    ExpandParams q = p;
-    q.tiles64_off = SchedLayout::make(T, num_adapters).tiles64;
-    const int64_t tasks = SchedLayout::max_tiles64(T, num_adapters) * ((p.N + kExpandCols - 1) / kExpandCols);
-    const unsigned grid = grid_for(tasks, 1, kMaxGrid);
+    ExpandParams q;
+    unsigned grid;
+    const int ks = expand_plan(p, T, num_adapters, r_max, &q, &grid);
     if (dtype == LORA_BF16)
         return trans_w ? launch_expand_t<LORA_BF16, true>(ks, q, grid, st)
                        : launch_expand_t<LORA_BF16, false>(ks, q, grid, st);
