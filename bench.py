@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--overlap", action="store_true",
                     help="run the fine-tuning backward (v recomputed) on a second stream, concurrently with the "
                          "forward, joining at the end of each step")
+    ap.add_argument("--fused", action="store_true",
+                    help="forward as one lora_forward launch (v written for the backward) instead of "
+                         "lora_shrink + lora_expand_add")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-min-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -165,6 +168,9 @@ def algorithmic(wl):
     out["segments"] = dict(bytes=seg_bytes(T) + seg_bytes(wl.ft_count), flops=0)
     out["shrink"] = dict(bytes=e * n_valid * d_in + e * d_in * sum_ru + 4 * sum_rt, flops=2 * d_in * sum_rt)
     out["expand"] = dict(bytes=4 * sum_rt + e * d_out * sum_ru + 2 * e * n_valid * d_out, flops=2 * d_out * sum_rt)
+    # the one-launch forward: the two without the v round trip (v is still written once, for the backward)
+    fwd = dict(bytes=out["shrink"]["bytes"] + out["expand"]["bytes"] - 4 * sum_rt,
+               flops=out["shrink"]["flops"] + out["expand"]["flops"])
     ft = wl.ft_ids
     Tf = wl.ft_count
     rft = ranks[ft].astype(np.int64)
@@ -175,6 +181,7 @@ def algorithmic(wl):
         + 8 * r_u * (d_in + d_out) + 4 * int(rft.sum()),
         flops=4 * int(rft.sum()) * (d_in + d_out))
     out["step"] = dict(bytes=sum(v["bytes"] for v in out.values()), flops=sum(v["flops"] for v in out.values()))
+    out["forward_fused"] = fwd
     return out
 
 
@@ -272,12 +279,19 @@ def main():
             lb.lora_segments_build_batch([(st["ids"], st["seg"]), (st["ft_ids"], st["seg_ft"])], wl.num_adapters)
         else:
             lb.lora_segments_build(st["ids"], wl.num_adapters, out=st["seg"])
-        lb.lora_shrink(st["x"], st["table"], st["seg"], v=st["v"], ws=st["ws_shrink"])
-        if ev is not None:
-            ev[0].record()
-        lb.lora_expand_add(st["v"], st["table"], st["seg"], st["y"])
-        if ev is not None:
-            ev[1].record()
+        if args.fused:
+            if ev is not None:
+                ev[0].record()
+            lb.lora_forward(st["x"], st["table"], st["seg"], st["y"], v=st["v"])
+            if ev is not None:
+                ev[1].record()
+        else:
+            lb.lora_shrink(st["x"], st["table"], st["seg"], v=st["v"], ws=st["ws_shrink"])
+            if ev is not None:
+                ev[0].record()
+            lb.lora_expand_add(st["v"], st["table"], st["seg"], st["y"])
+            if ev is not None:
+                ev[1].record()
         if side is not None and has_ft:
             torch.cuda.current_stream(dev).wait_stream(side)
         elif has_ft:
@@ -350,7 +364,8 @@ def main():
     if any(errs):
         raise RuntimeError(f"device-side data errors reported: {errs}")
 
-    ex = alg["expand"]
+    ex = alg["forward_fused"] if args.fused else alg["expand"]
+    kern_name = "lora_forward (fused_forward_kernel)" if args.fused else "lora_expand_add (expand_kernel)"
     achieved = ex["bytes"] / (kern_ms * 1e-3) / 1e9
     line = {
         "metric": "LoRA delta tokens/s + achieved HBM GB/s (or MFMA %) vs peak, mixed multi-LoRA batch",
@@ -369,13 +384,13 @@ def main():
                    "d_out": wl.d_out, "adapters": wl.num_adapters, "ranks": RANKS_DESC[args.workload],
                    "ft_adapter_rank": r_ft, "seed": 0, "input_sets": args.sets,
                    "launch": "graph" if graphs is not None else "eager",
-                   "streams": 2 if args.overlap else 1},
+                   "streams": 2 if args.overlap else 1, "forward": "fused" if args.fused else "split"},
         "host_enqueue_ms_per_step": (t_enq - t0) * 1e3 / K,
         "step_algorithmic_GBps": alg["step"]["bytes"] / (ms * 1e-3) / 1e9,
         "step_algorithmic_bytes": alg["step"]["bytes"],
-        "roofline": {"bound": "hbm", "kernel": "lora_expand_add (expand_kernel)", "achieved": achieved,
+        "roofline": {"bound": "hbm", "kernel": kern_name, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic() if args.workload == 3 else None,
+                     "traffic": measured_traffic() if args.workload == 3 and not args.fused else None,
                      "algorithmic_bytes_per_launch": ex["bytes"], "avg_launch_ms": kern_ms, "timing": kern_how,
                      "mfma_frac": ex["flops"] / (kern_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
     }

@@ -23,7 +23,8 @@ from ._abi import LORA_BF16, LORA_F32, LORA_MAX_RANK, LoraError
 
 __all__ = [
     "AdapterTable", "GradTable", "Segments", "LoraError",
-    "lora_segments_build", "lora_segments_build_batch", "lora_shrink", "lora_expand_add", "lora_backward",
+    "lora_segments_build", "lora_segments_build_batch", "lora_shrink", "lora_expand_add", "lora_forward",
+    "lora_backward",
     "lora_abi_version", "lora_status_string",
     "lora_segments_workspace_bytes", "lora_shrink_workspace_bytes", "lora_backward_workspace_bytes",
     "lora_segments_sched_elems",
@@ -245,6 +246,28 @@ def lora_expand_add(v: torch.Tensor, adapters: AdapterTable, seg: Segments, y: t
     st = _abi.load().lora_expand_add(_dtype_code(y), pv, ldv, T, d_out, adapters.ptr, len(adapters), r_max,
                                      seg.c, py, ldy, _stream(y.device))
     _abi.check("lora_expand_add", st)
+    return y
+
+
+def lora_forward(x: torch.Tensor, adapters: AdapterTable, seg: Segments, y: torch.Tensor,
+                 v: Optional[torch.Tensor] = None, r_max: Optional[int] = None) -> torch.Tensor:
+    """y[t] += s_a B_a A_a x[t] in one launch (for decode-like batches); v, if given, receives A_a x[t]."""
+    _on_gpu(x, y, v)
+    px, T, d_in, ldx = _rows(x, "x")
+    py, Ty, d_out, ldy = _rows(y, "y")
+    if Ty != T:
+        raise ValueError("x and y must have the same number of rows")
+    if y.dtype != x.dtype:
+        raise ValueError("x and y must have the same element type")
+    pv, ldv = 0, 0
+    if v is not None:
+        pv, Tv, _, ldv = _rows(v, "v")
+        if Tv != T or v.dtype != torch.float32:
+            raise ValueError("v must be fp32 with one row per row of x")
+    r_max = adapters.r_max if r_max is None else r_max
+    st = _abi.load().lora_forward(_dtype_code(x), px, ldx, T, d_in, d_out, adapters.ptr, len(adapters), r_max,
+                                  seg.c, py, ldy, pv or None, ldv, _stream(x.device))
+    _abi.check("lora_forward", st)
     return y
 
 

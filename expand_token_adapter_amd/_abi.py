@@ -57,6 +57,8 @@ SIGNATURES = {
                                    _vp, _i64, _vp, _sz, _vp]),
     "lora_expand_add": (ctypes.c_int, [ctypes.c_int, _vp, _i64, _i32, _i32, _vp, _i32, _i32, LoraSegments,
                                        _vp, _i64, _vp]),
+    "lora_forward": (ctypes.c_int, [ctypes.c_int, _vp, _i64, _i32, _i32, _i32, _vp, _i32, _i32, LoraSegments,
+                                    _vp, _i64, _vp, _i64, _vp]),
     "lora_backward": (ctypes.c_int, [ctypes.c_int, _vp, _i64, _vp, _i64, _vp, _i64, _i32, _i32, _i32, _vp,
                                      _vp, _i32, _i32, LoraSegments, _vp, _i64, _vp, _sz, _vp]),
 }

@@ -1,0 +1,325 @@
+// fused.h -- one-launch forward: y += s B (A x) for batches of short row groups (gfx950).
+//
+// h(x) = W x + B A x with each row applying its own adapter (MOLT section 2.1;
+// DeltaServe section 2.2, multi-LoRA batching).  The split path runs the
+// shrink (K split into slices), the sum of the slices and the expand as three
+// launches with v in HBM between them; that suits tiles of many rows, whose
+// y traffic needs the whole chip.  When adapters have few rows each (decode),
+// the work is the weights A_a and B_a plus launch latency, and a workgroup can
+// carry a tile from x to y.  A task = (64-row tile, one of `nsplit` column
+// ranges of d_out):
+//   phase 1  v = A_a x for the tile's rows and ranks (up to 32 KS).  The waves
+//            cover the tile's 16-row blocks (1, 2 or 4 of them) times equal
+//            parts of d_in (8, 4 or 2), with several 32-element K chunks in
+//            flight; the parts are added in order through LDS.  v stays in
+//            LDS (the task of column range 0 also writes it out on request).
+//            Each task of a tile computes v itself: A_a is read once per
+//            column range (from L2 after the first).
+//   phase 2  the waves walk the range's 64-column chunks: weight block and y
+//            rows of the next chunk in flight while the current chunk's MFMA
+//            tiles (16 columns x 16 rows, v as hi/lo bf16 fragments) are added
+//            to y in fp32 and rounded once.
+// The arithmetic per output is the split path's: fp32 accumulation, MFMA
+// 16x16x32 bf16 (fp32 operands split into hi/lo bf16 pairs), one rounding of
+// y.  Only the association of the sum over d_in differs, and it is fixed by
+// the tile's row count: results are bit-reproducible.
+#pragma once
+
+#include "device_common.h"
+
+namespace lora {
+
+constexpr int kFusedWaves = 8;
+constexpr int kFusedThreads = kFusedWaves * kWave;
+constexpr int kFusedPitch = 68;  // LDS pitch (floats) of a 16-row transpose buffer
+
+struct FusedParams {
+    const void* x;       // [row][ldx], rows through perm
+    int64_t ldx;
+    int32_t K;           // d_in
+    const lora_adapter* adapters;
+    int32_t r_max;
+    const int32_t* perm;
+    const int32_t* sched;
+    int64_t tiles64_off;
+    void* y;             // [row][ldy], rows through perm
+    int64_t ldy;
+    int32_t N;           // d_out
+    int32_t nsplit;      // column ranges of d_out per tile
+    float* v;            // optional [row][ldv]: v as lora_shrink writes it
+    int64_t ldv;
+    int32_t* err;
+};
+
+template <int DT, int KS>
+struct FusedLds {
+    static constexpr int NMB = 2 * KS;
+    static constexpr int kTBytes = kFusedWaves * 16 * kFusedPitch * 4;  // phase 2 transposes
+    static constexpr int kRedBytes = 7 * NMB * kWave * 16;             // phase 1: up to 7 parts of one row block
+    static constexpr int kScratch = kTBytes > kRedBytes ? kTBytes : kRedBytes;
+    static constexpr int kFrag = 4 * KS * kWave * 2 * 16;               // v as MFMA B fragments
+    static constexpr int kVPitch = 32 * KS + 4;                         // floats
+    static constexpr int kV = 64 * kVPitch * 4;
+    static constexpr int kBytes = kScratch + kFrag + kV + 64 * 4;
+};
+
+// KS: 32-rank steps (ranks covered = 32 KS >= r_max).
+template <int DT, int KS>
+__global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void fused_forward_kernel(FusedParams p) {
+    using F = Frag<DT>;
+    using E = Elem<DT>;
+    using O = F32Operand<DT>;
+    using L = FusedLds<DT, KS>;
+    constexpr int EB = F::kBytes;
+    constexpr int YQ = EB / 2;          // 16-byte quads per 8 elements
+    constexpr int NMB = 2 * KS;         // 16-rank blocks
+    constexpr int NF = (4 * KS * kWave + kFusedThreads - 1) / kFusedThreads;  // v fragments built per thread
+    // K chunks in flight per wave in phase 1; the next chunk's weight block
+    // and y rows in flight in phase 2 (where the registers allow it)
+    constexpr int NPF = DT == LORA_BF16 ? (NMB <= 2 ? 4 : (NMB <= 4 ? 3 : 2)) : (NMB <= 2 ? 2 : 1);
+    constexpr bool PF = DT == LORA_BF16 && KS <= 2;
+    static_assert(sizeof(O) == 32, "fragment pair is two quads");
+    __shared__ __attribute__((aligned(16))) char s_mem[L::kBytes];
+    char* scratch = s_mem;
+    u32x4_t* s_frag = reinterpret_cast<u32x4_t*>(s_mem + L::kScratch);
+    float* s_v = reinterpret_cast<float*>(s_mem + L::kScratch + L::kFrag);
+    int32_t* s_row = reinterpret_cast<int32_t*>(s_mem + L::kScratch + L::kFrag + L::kV);
+
+    const int wave = wave_id();
+    const int lane = threadIdx.x & (kWave - 1);
+    const int lr = lane & 15;
+    const int lg = lane >> 4;
+    const int yr = lane >> 3;       // phase 2: row (and row + 8) of a step in the row-contiguous layout
+    const int yc = 8 * (lane & 7);  // phase 2: first column of the chunk in that layout
+    const int ntiles = p.sched[1];
+    const int64_t ntasks = (int64_t)ntiles * p.nsplit;
+    const TaskSlice ts = xcd_slice(ntasks, 1, 0);
+    const int nkc = (p.K + 31) / 32;          // 32-element K chunks
+    const int nch = (p.N + 63) / 64;          // 64-column chunks of d_out
+    char* ybase = static_cast<char*>(p.y);
+    float* tw = reinterpret_cast<float*>(scratch) + wave * 16 * kFusedPitch;
+
+    for (int64_t task = ts.begin; task < ts.end; task += ts.stride) {
+        const int tile = (int)(task / p.nsplit);
+        const int split = (int)(task % p.nsplit);
+        const TileRec rec = load_tile(p.sched, p.tiles64_off, tile);
+        const lora_adapter ad = load_adapter(p.adapters, rec.adapter);
+        if (!adapter_ok(ad, p.r_max)) {
+            if (split == 0 && threadIdx.x == 0) atomicAdd(p.err, 1);
+            continue;
+        }
+        const int r = ad.rank;
+        const float s = ad.scale;
+        const int nrows = rec.rows;
+        const int nst = (nrows + 15) >> 4;
+        if (threadIdx.x < 64)
+            s_row[threadIdx.x] = p.perm[rec.pos0 + ((int)threadIdx.x < nrows ? (int)threadIdx.x : 0)];
+        __syncthreads();
+
+        // ---- phase 1: v = A x.  A operand: rank rows of A_a, B operand: x rows.
+        {
+            const int nrb = nst == 1 ? 1 : (nst == 2 ? 2 : 4);  // row blocks
+            const int nkp = kFusedWaves / nrb;                  // parts of d_in
+            const int rb = wave % nrb;
+            const int kp = wave / nrb;
+            const int kc0 = kp * nkc / nkp, kc1 = (kp + 1) * nkc / nkp;
+            const char* A = static_cast<const char*>(ad.A);
+            const char* xr = static_cast<const char*>(p.x) + (int64_t)s_row[16 * rb + lr] * p.ldx * EB;
+            f32x4_t acc[NMB];
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb) acc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            // rank rows past r read row r - 1 and are zeroed; K past the part reads K 0 and is zeroed
+            auto load_chunk = [&](int kc, F& xf, F (&af)[NMB]) {
+                const int k = 32 * kc + 8 * lg;
+                const bool kok = kc < kc1 && k < p.K;
+                const int ks = kok ? k : 0;
+                xf = F::load(xr + (int64_t)ks * EB);
+                if (!kok) xf = F::zero();
+#pragma unroll
+                for (int mb = 0; mb < NMB; ++mb) {
+                    const int rk = 16 * mb + lr;
+                    const bool ok = kok && rk < r;
+                    const F a = F::load(A + ((int64_t)(rk < r ? rk : r - 1) * p.K + ks) * EB);
+                    af[mb] = ok ? a : F::zero();
+                }
+            };
+            F xq[NPF];
+            F aq[NPF][NMB];
+#pragma unroll
+            for (int i = 0; i < NPF; ++i) load_chunk(kc0 + i, xq[i], aq[i]);
+            for (int kc = kc0; kc < kc1; kc += NPF) {
+#pragma unroll
+                for (int i = 0; i < NPF; ++i) {
+#pragma unroll
+                    for (int mb = 0; mb < NMB; ++mb) acc[mb] = mma(aq[i][mb], xq[i], acc[mb]);
+                    load_chunk(kc + NPF + i, xq[i], aq[i]);
+                }
+            }
+            // D rows 4 (l / 16) + i of block mb = ranks, column l % 16 = row of the block.
+            // Parts 1 .. nkp - 1 go through LDS; part 0 adds them in order.
+            f32x4_t* red = reinterpret_cast<f32x4_t*>(scratch);
+            if (kp > 0) {
+#pragma unroll
+                for (int mb = 0; mb < NMB; ++mb) red[(((kp - 1) * nrb + rb) * NMB + mb) * kWave + lane] = acc[mb];
+            }
+            __syncthreads();
+            if (kp == 0) {
+                const int row = 16 * rb + lr;
+                for (int q = 1; q < nkp; ++q)
+#pragma unroll
+                    for (int mb = 0; mb < NMB; ++mb) acc[mb] += red[(((q - 1) * nrb + rb) * NMB + mb) * kWave + lane];
+#pragma unroll
+                for (int mb = 0; mb < NMB; ++mb) {
+                    f32x4_t sum = acc[mb];
+                    const int rk = 16 * mb + 4 * lg;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (rk + i >= r) sum[i] = 0.f;
+                    *reinterpret_cast<f32x4_t*>(s_v + row * L::kVPitch + rk) = sum;
+                    // v as lora_shrink writes it: ranks < r, zeros up to round_up(r, 8)
+                    if (p.v && split == 0 && row < nrows && rk < (r + 7) / 8 * 8)
+                        *gptr(reinterpret_cast<f32x4_t*>(p.v + (int64_t)s_row[row] * p.ldv + rk)) = sum;
+                }
+            }
+            __syncthreads();
+        }
+
+        // ---- v fragments: step st (16 rows), rank step ks: lane (row lr, ranks 32 ks + 8 lg .. + 7),
+        //      for the tile's steps only.
+#pragma unroll
+        for (int i = 0; i < NF; ++i) {
+            const int f = threadIdx.x + kFusedThreads * i;
+            const int st = f / (KS * kWave);
+            if (f < 4 * KS * kWave && st < nst) {
+                const int ks = (f / kWave) % KS;
+                const int row = 16 * st + (f & 15);
+                const int kk = 32 * ks + 8 * ((f >> 4) & 3);
+                float fv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) fv[e] = s_v[row * L::kVPitch + kk + e];
+                const O o = O::make(fv);
+                const u32x4_t* oq = reinterpret_cast<const u32x4_t*>(&o);
+                s_frag[2 * f] = oq[0];
+                s_frag[2 * f + 1] = oq[1];
+            }
+        }
+        __syncthreads();
+
+        // ---- phase 2: chunks of this task's column range, ch = lo + wave, lo + wave + 8, ...
+        const int ch_lo = split * nch / p.nsplit, ch_hi = (split + 1) * nch / p.nsplit;
+        const char* B = static_cast<const char*>(ad.B);
+        const bool b_units = (r & 7) == 0;  // B_a rows of 16-byte units
+        auto load_w = [&](int ch, F (&wf)[4][KS]) {
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) {
+                const int col = 64 * ch + 16 * mb + lr;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int kk = 32 * ks + 8 * lg;
+                    if (b_units) {
+                        const bool ok = ch < ch_hi && col < p.N && kk < r;
+                        const F w = F::load(B + (ok ? (int64_t)col * r + kk : 0) * EB);
+                        wf[mb][ks] = ok ? w : F::zero();
+                    } else {
+                        const int nval = (ch < ch_hi && col < p.N) ? max(0, min(8, r - kk)) : 0;
+                        wf[mb][ks] = F::load_strided(B + (nval ? (int64_t)col * r + kk : 0) * EB, 1, nval);
+                    }
+                }
+            }
+        };
+        // y rows of a chunk (the tile's 16-row steps; columns past N and
+        // chunks past the range re-read column 0 of the rows)
+        auto load_y_step = [&](int ch, int st, u32x4_t (&yq)[2][YQ]) {
+            const int c = 64 * ch + yc;
+            const int col = ch < ch_hi && c < p.N ? c : 0;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int64_t row = s_row[16 * st + 8 * u + yr];
+                const LORA_GLOBAL u32x4_t* src =
+                    gptr(reinterpret_cast<const u32x4_t*>(ybase + (row * p.ldy + col) * EB));
+#pragma unroll
+                for (int q = 0; q < YQ; ++q) yq[u][q] = __builtin_nontemporal_load(src + q);
+            }
+        };
+        auto load_y = [&](int ch, u32x4_t (&yq)[4][2][YQ]) {
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+                if (st < nst) load_y_step(ch, st, yq[st]);
+        };
+        F wcur[4][KS], wnext[4][KS];
+        u32x4_t ycur[4][2][YQ], ynext[4][2][YQ];
+        if constexpr (PF) {
+            load_w(ch_lo + wave, wcur);
+            load_y(ch_lo + wave, ycur);
+        }
+        for (int ch = ch_lo + wave; ch < ch_hi; ch += kFusedWaves) {
+            if constexpr (PF) {
+                load_w(ch + kFusedWaves, wnext);
+                load_y(ch + kFusedWaves, ynext);
+            } else {
+                load_w(ch, wcur);
+                // without prefetch the y rows of one step are read just before
+                // they are needed (fewer registers live)
+            }
+            const int c = 64 * ch + yc;
+            const bool col_ok = c < p.N;
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                if (st < nst) {
+                    if constexpr (!PF) load_y_step(ch, st, ycur[st]);
+                    f32x4_t acc[4];
+#pragma unroll
+                    for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) {
+                        const int f = (st * KS + ks) * kWave + lane;
+                        O o;
+                        u32x4_t* oq = reinterpret_cast<u32x4_t*>(&o);
+                        oq[0] = s_frag[2 * f];
+                        oq[1] = s_frag[2 * f + 1];
+#pragma unroll
+                        for (int mb = 0; mb < 4; ++mb) acc[mb] = o.mma_right(wcur[mb][ks], acc[mb]);
+                    }
+                    // D[m][n] of block mb: column 16 mb + m, row n; this lane has m = 4 lg + i, n = lr.
+#pragma unroll
+                    for (int mb = 0; mb < 4; ++mb)
+                        *reinterpret_cast<f32x4_t*>(tw + lr * kFusedPitch + 16 * mb + 4 * lg) = acc[mb];
+                    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const int row_in_tile = 16 * st + 8 * u + yr;
+                        const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(tw + (8 * u + yr) * kFusedPitch + yc);
+                        const f32x4_t a1 =
+                            *reinterpret_cast<const f32x4_t*>(tw + (8 * u + yr) * kFusedPitch + yc + 4);
+                        float yv[8];
+                        E::unpack8(&ycur[st][u][0], yv);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            yv[e] = yv[e] + s * a0[e];
+                            yv[4 + e] = yv[4 + e] + s * a1[e];
+                        }
+                        if (col_ok && row_in_tile < nrows)
+                            E::store8_nt(ybase + ((int64_t)s_row[row_in_tile] * p.ldy + c) * EB, yv);
+                    }
+                    __builtin_amdgcn_wave_barrier();
+                }
+            }
+            if constexpr (PF) {
+#pragma unroll
+                for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) wcur[mb][ks] = wnext[mb][ks];
+#pragma unroll
+                for (int st = 0; st < 4; ++st)
+#pragma unroll
+                    for (int u = 0; u < 2; ++u)
+#pragma unroll
+                        for (int q = 0; q < YQ; ++q) ycur[st][u][q] = ynext[st][u][q];
+            }
+        }
+        __syncthreads();  // s_row, s_v and s_frag are rewritten by the next task
+    }
+}
+
+}  // namespace lora

@@ -211,6 +211,27 @@ int lora_expand_add(int dtype, const float* v, int64_t ldv, int32_t T, int32_t d
                     lora_segments seg, void* y, int64_t ldy, void* stream);
 
 /*
+ * Fused forward: y_t += s_{a(t)} B_{a(t)} (A_{a(t)} x_t) in one launch, the
+ * whole h(x) = W x + B A x delta of MOLT section 2.1 for every row with an
+ * adapter, without v passing through HBM and without a workspace.  One
+ * workgroup carries each 64-row tile from x to y (v = A x over all of d_in
+ * into LDS, then all of d_out), so it suits batches whose adapters have few
+ * rows each (decode; many adapters): there the weights and launch latency
+ * dominate.  Batches of long row groups (prefill, fine-tuning) run faster on
+ * lora_shrink + lora_expand_add, which spread each tile's y traffic over the
+ * whole chip.  Results equal lora_shrink + lora_expand_add up to the order of
+ * the fp32 sum over d_in (a fixed order: bit-reproducible).
+ *   x [T, ldx], y [T, ldy] in/out (dtype); adapters, seg as for lora_shrink.
+ *   v: optional [T, ldv] fp32 output (ldv >= r_max, multiple of 8), written as
+ *   lora_shrink writes it (columns r_a..round_up(r_a, 8)-1 zero; rows without
+ *   an adapter unchanged), e.g. for a later lora_backward; NULL skips it.
+ * Errors and device-side data checks as for lora_shrink / lora_expand_add.
+ */
+int lora_forward(int dtype, const void* x, int64_t ldx, int32_t T, int32_t d_in, int32_t d_out,
+                 const lora_adapter* adapters, int32_t num_adapters, int32_t r_max, lora_segments seg,
+                 void* y, int64_t ldy, float* v, int64_t ldv, void* stream);
+
+/*
  * LoRA backward over T_ft fine-tuning rows (DeltaServe, section 3.2: the
  * backward computes the LoRA gradients from the saved layer input).
  *   x  [T_ft, ldx]  layer input of the fine-tuning rows (dtype)

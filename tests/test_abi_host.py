@@ -116,6 +116,26 @@ def test_zero_rows_is_a_no_op(lib):
     assert st == _abi.LORA_OK
     st = lib.lora_backward(0, 0, 0, 0, 0, 0, 0, 0, 256, 256, FAKE, FAKE, 4, 8, _seg(), 0, 0, 0, 0, None)
     assert st == _abi.LORA_OK
+    st = lib.lora_forward(0, 0, 0, 0, 256, 256, FAKE, 4, 8, _seg(), 0, 0, 0, 0, None)
+    assert st == _abi.LORA_OK
+
+
+def test_fused_forward_rejects(lib):
+    def call(dtype=0, x=FAKE, ldx=256, T=10, d_in=256, d_out=512, A=4, r_max=16, seg=None, y=FAKE, ldy=512,
+             v=0, ldv=0):
+        return lib.lora_forward(dtype, x, ldx, T, d_in, d_out, FAKE, A, r_max, seg or _seg(), y, ldy, v, ldv, None)
+
+    bad, uns = _abi.LORA_ERR_INVALID_ARG, _abi.LORA_ERR_UNSUPPORTED
+    assert call(dtype=2) == bad
+    assert call(x=0) == bad and call(y=0) == bad
+    assert call(x=FAKE + 8) == bad            # not 16-byte aligned
+    assert call(ldx=128) == bad               # ld < d_in
+    assert call(d_in=260, ldx=264) == uns     # d_in not a multiple of 8
+    assert call(d_out=0) == bad and call(T=-1) == bad and call(A=0) == bad
+    assert call(r_max=0) == bad and call(r_max=129) == bad
+    assert call(seg=_seg(False)) == bad
+    assert call(v=FAKE, ldv=8) == bad         # ldv < r_max
+    assert call(v=FAKE, ldv=20) == bad        # ldv not a multiple of 8
 
 
 def test_segments_build_rejects(lib):

@@ -85,8 +85,8 @@ def test_segments_build_batch_matches_single_builds():
             assert int(b.err.item()) == err
 
 
-def _check_forward(case, tol):
-    y, v, seg = case.forward()
+def _check_forward(case, tol, fused=False):
+    y, v, seg = case.forward(fused=fused)
     y_ref, v_ref = case.oracle_forward()
     assert int(seg.err.item()) == 0
     e = rel_err(y, y_ref)
@@ -168,6 +168,63 @@ def test_forward_bad_table_entries_are_skipped_and_counted():
     assert not torch.equal(y[ok], case.y0[ok])
 
 
+# ------------------------------------------------------------------ fused forward
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("y0_zero", [False, True])
+def test_fused_forward_small_mixed(dtype, y0_zero):
+    """Ranks 5..128 (one to four 32-rank steps, rows that are not 16-byte units), ragged tiles."""
+    case = GpuCase(_small_mixed(dtype), y0_zero=y0_zero)
+    _check_forward(case, TOL[dtype], fused=True)
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+def test_fused_forward_configs_full_size(idx):
+    wl = _config(idx)
+    print(f"fused forward {wl.name} T={wl.T}", flush=True)
+    case = GpuCase(wl, y0_zero=idx == 2)
+    _check_forward(case, TOL[wl.dtype], fused=True)
+
+
+def test_fused_forward_matches_split_path_and_is_deterministic():
+    wl = _small_mixed("bf16")
+    case = GpuCase(wl, y0_zero=True)
+    yf, vf, _ = case.forward(fused=True)
+    yf2, vf2, _ = case.forward(fused=True)
+    assert torch.equal(yf, yf2) and torch.equal(vf, vf2)
+    ys, vs, _ = case.forward()
+    assert rel_err(yf, ys.double().cpu().numpy()) <= TOL["bf16"]
+    assert rel_err(vf, vs.double().cpu().numpy()) <= 1e-5  # both fp32 sums of the same bf16 products
+    # columns r_a .. round_up(r_a, 8) - 1 of v are zero, as lora_shrink writes them
+    for a, r in enumerate(wl.ranks):
+        rows = torch.from_numpy(wl.ids == a).cuda()
+        hi = (r + 7) // 8 * 8
+        if rows.any() and hi > r:
+            assert not vf[rows][:, r:hi].any()
+
+
+def test_fused_forward_b_zero_is_bit_exact_identity():
+    wl = _small_mixed("bf16")
+    wl.B = [np.zeros_like(b) for b in wl.B]
+    case = GpuCase(wl)
+    y, _, _ = case.forward(fused=True)
+    assert torch.equal(y, case.y0)
+
+
+def test_fused_forward_bad_table_entries_are_skipped_and_counted():
+    wl = _small_mixed("bf16")
+    case = GpuCase(wl)
+    y = case.y0.clone()
+    seg = lb.lora_segments_build(case.ids, wl.num_adapters)
+    lb.lora_forward(case.x, case.table, seg, y, r_max=64)
+    torch.cuda.synchronize()
+    assert int(seg.err.item()) > 0
+    rows128 = torch.from_numpy(wl.ids == 4).cuda()  # rank-128 adapter exceeds r_max=64
+    assert torch.equal(y[rows128], case.y0[rows128])
+    ok = torch.from_numpy(wl.ids == 3).cuda()
+    assert not torch.equal(y[ok], case.y0[ok])
+
+
 def test_empty_batch_is_a_no_op():
     wl = _small_mixed("bf16")
     case = GpuCase(wl)
@@ -177,6 +234,7 @@ def test_empty_batch_is_a_no_op():
     v = lb.lora_shrink(x, case.table, seg)
     y = case.y0[:0].clone()
     lb.lora_expand_add(v, case.table, seg, y)
+    lb.lora_forward(x, case.table, seg, y)
     torch.cuda.synchronize()
     assert v.shape[0] == 0
 
