@@ -118,6 +118,11 @@ struct Frag<LORA_BF16> {
     }
     // Raw 16-bit pattern of element i.
     __device__ __forceinline__ uint32_t raw(int i) const { return (q[i >> 1] >> (16 * (i & 1))) & 0xffffu; }
+    // The fragment where ok holds, else zeros (a mask, not a branch).
+    __device__ __forceinline__ Frag masked(bool ok) const {
+        const uint32_t m = 0u - (uint32_t)ok;
+        return Frag{u32x4_t{q[0] & m, q[1] & m, q[2] & m, q[3] & m}};
+    }
 };
 
 template <>
@@ -152,7 +157,15 @@ struct Frag<LORA_F32> {
         return __uint_as_float(i < 4 ? q0[i & 3] : q1[i & 3]);
     }
     __device__ __forceinline__ uint32_t raw(int i) const { return i < 4 ? q0[i & 3] : q1[i & 3]; }
+    __device__ __forceinline__ Frag masked(bool ok) const {
+        const uint32_t m = 0u - (uint32_t)ok;
+        return Frag{u32x4_t{q0[0] & m, q0[1] & m, q0[2] & m, q0[3] & m},
+                    u32x4_t{q1[0] & m, q1[1] & m, q1[2] & m, q1[3] & m}};
+    }
 };
+
+// Elements of an 8-element rank group starting at kk that lie below rank r.
+__device__ __forceinline__ int wkeep(int r, int kk) { return max(0, min(8, r - kk)); }
 
 // acc += A_frag (rows) x B_frag (columns) over the 8-element K group of each lane.
 __device__ __forceinline__ f32x4_t mma(const Frag<LORA_BF16>& a, const Frag<LORA_BF16>& b, f32x4_t c) {

@@ -284,15 +284,18 @@ extern "C" int lora_forward(int dtype, const void* x, int64_t ldx, int32_t T, in
     const unsigned grid = grid_for(max_tiles * p.nsplit, 1, kMaxGrid);
     hipStream_t st = static_cast<hipStream_t>(stream);
     const dim3 block(kFusedThreads);
-    const int ks = r_max <= 32 ? 1 : (r_max <= 64 ? 2 : 4);
+    // 16-rank blocks: 1 (r_max <= 16), 2, 4 or 8
+    const int nmb = r_max <= 16 ? 1 : (r_max <= 32 ? 2 : (r_max <= 64 ? 4 : 8));
     if (dtype == LORA_BF16) {
-        if (ks == 1) hipLaunchKernelGGL((fused_forward_kernel<LORA_BF16, 1>), dim3(grid), block, 0, st, p);
-        else if (ks == 2) hipLaunchKernelGGL((fused_forward_kernel<LORA_BF16, 2>), dim3(grid), block, 0, st, p);
-        else hipLaunchKernelGGL((fused_forward_kernel<LORA_BF16, 4>), dim3(grid), block, 0, st, p);
+        if (nmb == 1) hipLaunchKernelGGL((fused_forward_kernel<LORA_BF16, 1, 1>), dim3(grid), block, 0, st, p);
+        else if (nmb == 2) hipLaunchKernelGGL((fused_forward_kernel<LORA_BF16, 1, 2>), dim3(grid), block, 0, st, p);
+        else if (nmb == 4) hipLaunchKernelGGL((fused_forward_kernel<LORA_BF16, 2, 4>), dim3(grid), block, 0, st, p);
+        else hipLaunchKernelGGL((fused_forward_kernel<LORA_BF16, 4, 8>), dim3(grid), block, 0, st, p);
     } else {
-        if (ks == 1) hipLaunchKernelGGL((fused_forward_kernel<LORA_F32, 1>), dim3(grid), block, 0, st, p);
-        else if (ks == 2) hipLaunchKernelGGL((fused_forward_kernel<LORA_F32, 2>), dim3(grid), block, 0, st, p);
-        else hipLaunchKernelGGL((fused_forward_kernel<LORA_F32, 4>), dim3(grid), block, 0, st, p);
+        if (nmb == 1) hipLaunchKernelGGL((fused_forward_kernel<LORA_F32, 1, 1>), dim3(grid), block, 0, st, p);
+        else if (nmb == 2) hipLaunchKernelGGL((fused_forward_kernel<LORA_F32, 1, 2>), dim3(grid), block, 0, st, p);
+        else if (nmb == 4) hipLaunchKernelGGL((fused_forward_kernel<LORA_F32, 2, 4>), dim3(grid), block, 0, st, p);
+        else hipLaunchKernelGGL((fused_forward_kernel<LORA_F32, 4, 8>), dim3(grid), block, 0, st, p);
     }
     return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }

@@ -63,8 +63,9 @@ struct FusedLds {
     static constexpr int kBytes = kScratch + kFrag + kV + 64 * 4;
 };
 
-// KS: 32-rank steps (ranks covered = 32 KS >= r_max).
-template <int DT, int KS>
+// KS: 32-rank steps of phase 2 (32 KS >= r_max); NMB: 16-rank blocks of
+// phase 1 (16 NMB >= r_max, NMB <= 2 KS).
+template <int DT, int KS, int NMB>
 __global__ __launch_bounds__(kFusedThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void fused_forward_kernel(FusedParams p) {
     using F = Frag<DT>;
@@ -73,12 +74,13 @@ void fused_forward_kernel(FusedParams p) {
     using L = FusedLds<DT, KS>;
     constexpr int EB = F::kBytes;
     constexpr int YQ = EB / 2;          // 16-byte quads per 8 elements
-    constexpr int NMB = 2 * KS;         // 16-rank blocks
     constexpr int NF = (4 * KS * kWave + kFusedThreads - 1) / kFusedThreads;  // v fragments built per thread
     // K chunks in flight per wave in phase 1; the next chunk's weight block
     // and y rows in flight in phase 2 (where the registers allow it)
-    constexpr int NPF = DT == LORA_BF16 ? (NMB <= 2 ? 4 : (NMB <= 4 ? 3 : 2)) : (NMB <= 2 ? 2 : 1);
-    constexpr bool PF = DT == LORA_BF16 && KS <= 2;
+    constexpr int NPF = DT == LORA_BF16 ? (NMB == 1 ? 8 : (NMB <= 2 ? 4 : 2)) : (NMB <= 2 ? 2 : 1);
+    static_assert(NMB >= 1 && NMB <= 2 * KS, "phase 1 covers at most the ranks of phase 2");
+    constexpr bool PFW = DT == LORA_BF16 && KS <= 2;  // next chunk's weight block in flight
+    constexpr bool PFY = DT == LORA_BF16 && KS == 1;  // and its y rows
     static_assert(sizeof(O) == 32, "fragment pair is two quads");
     __shared__ __attribute__((aligned(16))) char s_mem[L::kBytes];
     char* scratch = s_mem;
@@ -117,6 +119,56 @@ void fused_forward_kernel(FusedParams p) {
             s_row[threadIdx.x] = p.perm[rec.pos0 + ((int)threadIdx.x < nrows ? (int)threadIdx.x : 0)];
         __syncthreads();
 
+        // Phase 2 walks the chunks of this task's column range, ch = lo + wave,
+        // lo + wave + 8, ...  Its first chunk's weight block and y rows do not
+        // depend on v: they are issued here, before phase 1.
+        const int ch_lo = split * nch / p.nsplit, ch_hi = (split + 1) * nch / p.nsplit;
+        const char* B = static_cast<const char*>(ad.B);
+        const bool b_units = (r & 7) == 0;  // B_a rows of 16-byte units
+        // Rows in whole 16-byte units: the loads only clamp addresses (columns
+        // past N or the range read B_a's first unit and are not stored); groups
+        // past rank r are zeroed where they are used, so the next chunk's loads
+        // are not waited for early.  Otherwise elements are read one by one.
+        auto load_w = [&](int ch, F (&wf)[4][KS]) {
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) {
+                const int col = 64 * ch + 16 * mb + lr;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int kk = 32 * ks + 8 * lg;
+                    const bool ok = ch < ch_hi && col < p.N && kk < r;
+                    const char* src = B + (ok ? (int64_t)col * r + kk : 0) * EB;
+                    wf[mb][ks] = b_units ? F::load(src) : F::load_strided(src, 1, ok ? wkeep(r, kk) : 0);
+                }
+            }
+        };
+        // y rows of a chunk (the tile's 16-row steps; columns past N and
+        // chunks past the range re-read column 0 of the rows)
+        auto load_y_step = [&](int ch, int st, u32x4_t (&yq)[2][YQ]) {
+            const int c = 64 * ch + yc;
+            const int col = ch < ch_hi && c < p.N ? c : 0;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int64_t row = s_row[16 * st + 8 * u + yr];
+                const LORA_GLOBAL u32x4_t* src =
+                    gptr(reinterpret_cast<const u32x4_t*>(ybase + (row * p.ldy + col) * EB));
+#pragma unroll
+                for (int q = 0; q < YQ; ++q) yq[u][q] = __builtin_nontemporal_load(src + q);
+            }
+        };
+        auto load_y = [&](int ch, u32x4_t (&yq)[4][2][YQ]) {
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+                if (st < nst) load_y_step(ch, st, yq[st]);
+        };
+        // (the empty asm statements with a memory clobber keep the prefetches
+        // where they are issued, as in phase 1)
+        F wcur[4][KS], wnext[4][KS];
+        u32x4_t ycur[4][2][YQ], ynext[4][2][YQ];
+        if constexpr (PFW) load_w(ch_lo + wave, wcur);
+        if constexpr (PFY) load_y(ch_lo + wave, ycur);
+        asm volatile("" ::: "memory");
+
         // ---- phase 1: v = A x.  A operand: rank rows of A_a, B operand: x rows.
         {
             const int nrb = nst == 1 ? 1 : (nst == 2 ? 2 : 4);  // row blocks
@@ -129,20 +181,23 @@ void fused_forward_kernel(FusedParams p) {
             f32x4_t acc[NMB];
 #pragma unroll
             for (int mb = 0; mb < NMB; ++mb) acc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            // rank rows past r read row r - 1 and are zeroed; K past the part reads K 0 and is zeroed
+            // Loads only clamp addresses: rank rows past r read row r - 1 (their
+            // sums are dropped below), K past the part reads K 0.  The x operand
+            // of a chunk past the part is zeroed where it is used, so that the
+            // chunks in flight are not waited for when they are issued.
             auto load_chunk = [&](int kc, F& xf, F (&af)[NMB]) {
                 const int k = 32 * kc + 8 * lg;
-                const bool kok = kc < kc1 && k < p.K;
-                const int ks = kok ? k : 0;
+                const int ks = kc < kc1 && k < p.K ? k : 0;
                 xf = F::load(xr + (int64_t)ks * EB);
-                if (!kok) xf = F::zero();
 #pragma unroll
                 for (int mb = 0; mb < NMB; ++mb) {
                     const int rk = 16 * mb + lr;
-                    const bool ok = kok && rk < r;
-                    const F a = F::load(A + ((int64_t)(rk < r ? rk : r - 1) * p.K + ks) * EB);
-                    af[mb] = ok ? a : F::zero();
+                    af[mb] = F::load(A + ((int64_t)(rk < r ? rk : r - 1) * p.K + ks) * EB);
                 }
+                // keeps the loads where they are issued: without it the loads of
+                // the prologue and of the loop body merge into one load at the
+                // top of the loop, which is then waited for at once
+                asm volatile("" ::: "memory");
             };
             F xq[NPF];
             F aq[NPF][NMB];
@@ -151,8 +206,9 @@ void fused_forward_kernel(FusedParams p) {
             for (int kc = kc0; kc < kc1; kc += NPF) {
 #pragma unroll
                 for (int i = 0; i < NPF; ++i) {
+                    const F xv = xq[i].masked((kc + i < kc1) & (32 * (kc + i) + 8 * lg < p.K));
 #pragma unroll
-                    for (int mb = 0; mb < NMB; ++mb) acc[mb] = mma(aq[i][mb], xq[i], acc[mb]);
+                    for (int mb = 0; mb < NMB; ++mb) acc[mb] = mma(aq[i][mb], xv, acc[mb]);
                     load_chunk(kc + NPF + i, xq[i], aq[i]);
                 }
             }
@@ -181,6 +237,10 @@ void fused_forward_kernel(FusedParams p) {
                     if (p.v && split == 0 && row < nrows && rk < (r + 7) / 8 * 8)
                         *gptr(reinterpret_cast<f32x4_t*>(p.v + (int64_t)s_row[row] * p.ldv + rk)) = sum;
                 }
+                // ranks past the blocks of phase 1 (and so past r) enter phase 2 as zeros
+#pragma unroll
+                for (int mb = NMB; mb < 2 * KS; ++mb)
+                    *reinterpret_cast<f32x4_t*>(s_v + row * L::kVPitch + 16 * mb + 4 * lg) = f32x4_t{0.f, 0.f, 0.f, 0.f};
             }
             __syncthreads();
         }
@@ -207,67 +267,21 @@ void fused_forward_kernel(FusedParams p) {
         __syncthreads();
 
         // ---- phase 2: chunks of this task's column range, ch = lo + wave, lo + wave + 8, ...
-        const int ch_lo = split * nch / p.nsplit, ch_hi = (split + 1) * nch / p.nsplit;
-        const char* B = static_cast<const char*>(ad.B);
-        const bool b_units = (r & 7) == 0;  // B_a rows of 16-byte units
-        auto load_w = [&](int ch, F (&wf)[4][KS]) {
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {
-                const int col = 64 * ch + 16 * mb + lr;
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const int kk = 32 * ks + 8 * lg;
-                    if (b_units) {
-                        const bool ok = ch < ch_hi && col < p.N && kk < r;
-                        const F w = F::load(B + (ok ? (int64_t)col * r + kk : 0) * EB);
-                        wf[mb][ks] = ok ? w : F::zero();
-                    } else {
-                        const int nval = (ch < ch_hi && col < p.N) ? max(0, min(8, r - kk)) : 0;
-                        wf[mb][ks] = F::load_strided(B + (nval ? (int64_t)col * r + kk : 0) * EB, 1, nval);
-                    }
-                }
-            }
-        };
-        // y rows of a chunk (the tile's 16-row steps; columns past N and
-        // chunks past the range re-read column 0 of the rows)
-        auto load_y_step = [&](int ch, int st, u32x4_t (&yq)[2][YQ]) {
-            const int c = 64 * ch + yc;
-            const int col = ch < ch_hi && c < p.N ? c : 0;
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int64_t row = s_row[16 * st + 8 * u + yr];
-                const LORA_GLOBAL u32x4_t* src =
-                    gptr(reinterpret_cast<const u32x4_t*>(ybase + (row * p.ldy + col) * EB));
-#pragma unroll
-                for (int q = 0; q < YQ; ++q) yq[u][q] = __builtin_nontemporal_load(src + q);
-            }
-        };
-        auto load_y = [&](int ch, u32x4_t (&yq)[4][2][YQ]) {
-#pragma unroll
-            for (int st = 0; st < 4; ++st)
-                if (st < nst) load_y_step(ch, st, yq[st]);
-        };
-        F wcur[4][KS], wnext[4][KS];
-        u32x4_t ycur[4][2][YQ], ynext[4][2][YQ];
-        if constexpr (PF) {
-            load_w(ch_lo + wave, wcur);
-            load_y(ch_lo + wave, ycur);
-        }
         for (int ch = ch_lo + wave; ch < ch_hi; ch += kFusedWaves) {
-            if constexpr (PF) {
+            if constexpr (PFW)
                 load_w(ch + kFusedWaves, wnext);
-                load_y(ch + kFusedWaves, ynext);
-            } else {
+            else
                 load_w(ch, wcur);
-                // without prefetch the y rows of one step are read just before
-                // they are needed (fewer registers live)
-            }
+            // without prefetch the y rows of one step are read just before
+            // they are needed (fewer registers live)
+            if constexpr (PFY) load_y(ch + kFusedWaves, ynext);
+            asm volatile("" ::: "memory");
             const int c = 64 * ch + yc;
             const bool col_ok = c < p.N;
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
                 if (st < nst) {
-                    if constexpr (!PF) load_y_step(ch, st, ycur[st]);
+                    if constexpr (!PFY) load_y_step(ch, st, ycur[st]);
                     f32x4_t acc[4];
 #pragma unroll
                     for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -278,8 +292,9 @@ void fused_forward_kernel(FusedParams p) {
                         u32x4_t* oq = reinterpret_cast<u32x4_t*>(&o);
                         oq[0] = s_frag[2 * f];
                         oq[1] = s_frag[2 * f + 1];
+                        const bool keep = !b_units || 32 * ks + 8 * lg < r;
 #pragma unroll
-                        for (int mb = 0; mb < 4; ++mb) acc[mb] = o.mma_right(wcur[mb][ks], acc[mb]);
+                        for (int mb = 0; mb < 4; ++mb) acc[mb] = o.mma_right(wcur[mb][ks].masked(keep), acc[mb]);
                     }
                     // D[m][n] of block mb: column 16 mb + m, row n; this lane has m = 4 lg + i, n = lr.
 #pragma unroll
@@ -305,11 +320,13 @@ void fused_forward_kernel(FusedParams p) {
                     __builtin_amdgcn_wave_barrier();
                 }
             }
-            if constexpr (PF) {
+            if constexpr (PFW) {
 #pragma unroll
                 for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
                     for (int ks = 0; ks < KS; ++ks) wcur[mb][ks] = wnext[mb][ks];
+            }
+            if constexpr (PFY) {
 #pragma unroll
                 for (int st = 0; st < 4; ++st)
 #pragma unroll
