@@ -34,7 +34,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp%d" % os.getpid()
         cmd = ["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
-               "-fno-fast-math", "-std=c99", "-o", tmp, _SRC]
+               "-fno-fast-math", "-std=c99", "-o", tmp, _SRC, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB)
     return _LIB
@@ -60,6 +60,8 @@ def _load():
                                     i32p, ctypes.c_int32, i32p, f64p, f64pp, f64pp, f64p, f64pp,
                                     f64pp, f64p, f64p, ctypes.c_int32]
     lib.oracle_backward.restype = None
+    lib.oracle_adamw.argtypes = [ctypes.c_int64, f64p, f64p, f64p, f64p] + [ctypes.c_double] * 6 + [ctypes.c_int32]
+    lib.oracle_adamw.restype = None
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
     lib.oracle_threads.restype = ctypes.c_int
     _lib = lib
@@ -164,6 +166,21 @@ def backward(x: np.ndarray, dy: np.ndarray, ids: np.ndarray, ranks: np.ndarray,
                         _ptr_table(A), _ptr_table(B), _p64(dx), _ptr_table(dA), _ptr_table(dB),
                         _p64(g), _p64(v), r_max)
     return dx, dA, dB, g, v
+
+
+def adamw(w: np.ndarray, grad: np.ndarray, m: np.ndarray, v: np.ndarray, *, lr: float, beta1: float,
+          beta2: float, eps: float, weight_decay: float, step: int, grad_scale: float = 1.0):
+    """One AdamW step; returns new (w, m, v) float64 arrays of w's shape (inputs untouched)."""
+    lib = _load()
+    w = np.array(w, dtype=np.float64, order="C", copy=True)
+    m = np.array(m, dtype=np.float64, order="C", copy=True)
+    v = np.array(v, dtype=np.float64, order="C", copy=True)
+    g = np.ascontiguousarray(grad, dtype=np.float64)
+    if not (w.shape == m.shape == v.shape == g.shape):
+        raise ValueError("w, grad, m, v must have one shape")
+    lib.oracle_adamw(w.size, _p64(w), _p64(g), _p64(m), _p64(v), lr, beta1, beta2, eps, weight_decay,
+                     grad_scale, int(step))
+    return w, m, v
 
 
 def from_workload(wl) -> dict:

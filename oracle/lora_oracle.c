@@ -32,6 +32,7 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#include <math.h>
 #ifdef _OPENMP
 #include <omp.h>
 #endif
@@ -213,4 +214,38 @@ void oracle_backward(int64_t T, int32_t d_in, int32_t d_out,
     }
     free(G);
     free(V);
+}
+
+/*
+ * One AdamW step (Adam with decoupled weight decay, Loshchilov and Hutter) on
+ * one tensor of adapter weights.  The fine-tuning updates the shared adapter
+ * weights directly once the gradients of a backward batch have been
+ * accumulated (DeltaServe, section 3.2, "Backward subprocess"); its optimizer
+ * is AdamW with learning rate 1e-3 and weight decay 0.01 (DeltaServe, section
+ * 4.1).  With step count t >= 1, element by element:
+ *     g      = grad_scale * grad
+ *     m      = beta1 m + (1 - beta1) g
+ *     v      = beta2 v + (1 - beta2) g^2
+ *     m_hat  = m / (1 - beta1^t)
+ *     v_hat  = v / (1 - beta2^t)
+ *     w      = w - lr (weight_decay w + m_hat / (sqrt(v_hat) + eps))
+ * w, m, v are updated in place.
+ */
+void oracle_adamw(int64_t n, double* w, const double* grad, double* m, double* v,
+                  double lr, double beta1, double beta2, double eps, double weight_decay,
+                  double grad_scale, int32_t step) {
+    double c1 = 1.0, c2 = 1.0;
+    for (int32_t i = 0; i < step; ++i) {
+        c1 *= beta1;
+        c2 *= beta2;
+    }
+    const double bc1 = 1.0 - c1, bc2 = 1.0 - c2;
+    for (int64_t i = 0; i < n; ++i) {
+        const double g = grad_scale * grad[i];
+        m[i] = beta1 * m[i] + (1.0 - beta1) * g;
+        v[i] = beta2 * v[i] + (1.0 - beta2) * g * g;
+        const double m_hat = m[i] / bc1;
+        const double v_hat = v[i] / bc2;
+        w[i] = w[i] - lr * (weight_decay * w[i] + m_hat / (sqrt(v_hat) + eps));
+    }
 }

@@ -292,3 +292,72 @@ def test_segments_match_library_sort(kind):
     if perm.size:
         assert np.all(np.diff(ids[perm]) >= 0)
         assert len(set(perm.tolist())) == perm.size
+
+
+# ------------------------------------------------------------- AdamW step
+#
+# The optimizer step is Adam with decoupled weight decay (AdamW), lr 1e-3 and
+# weight decay 0.01 (DeltaServe, section 4.1).  Pins: torch's own AdamW in
+# float64 on the CPU (an independent implementation of the same published
+# algorithm), the closed form of the first step, pure decay for zero
+# gradients, and invariance to the gradient's scale when eps vanishes.
+
+ADAMW_HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+
+
+def test_adamw_matches_torch_adamw_fp64_over_several_steps():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(11)
+    w0 = rng.standard_normal((3, 7)) * 0.02
+    grads = [rng.standard_normal((3, 7)) * (0.1 + k) for k in range(5)]
+    p = torch.nn.Parameter(torch.tensor(w0, dtype=torch.float64))
+    opt = torch.optim.AdamW([p], lr=ADAMW_HP["lr"], betas=(ADAMW_HP["beta1"], ADAMW_HP["beta2"]),
+                            eps=ADAMW_HP["eps"], weight_decay=ADAMW_HP["weight_decay"])
+    w, m, v = w0.copy(), np.zeros_like(w0), np.zeros_like(w0)
+    for k, g in enumerate(grads, start=1):
+        p.grad = torch.tensor(g, dtype=torch.float64)
+        opt.step()
+        w, m, v = oracle.adamw(w, g, m, v, step=k, **ADAMW_HP)
+        st = opt.state[p]
+        np.testing.assert_allclose(w, p.detach().numpy(), rtol=1e-13, atol=1e-16)
+        np.testing.assert_allclose(m, st["exp_avg"].numpy(), rtol=1e-13, atol=1e-16)
+        np.testing.assert_allclose(v, st["exp_avg_sq"].numpy(), rtol=1e-13, atol=1e-18)
+
+
+def test_adamw_first_step_closed_form():
+    # m = v = 0 before step 1: m_hat = g, v_hat = g^2, so
+    # w1 = w0 - lr (wd w0 + g / (|g| + eps)).
+    rng = np.random.default_rng(12)
+    w0 = rng.standard_normal(50)
+    g = rng.standard_normal(50) * 3.0
+    lr, wd, eps = 2e-3, 0.05, 1e-6
+    w, m, v = oracle.adamw(w0, g, np.zeros(50), np.zeros(50), lr=lr, beta1=0.8, beta2=0.99, eps=eps,
+                           weight_decay=wd, step=1)
+    np.testing.assert_allclose(w, w0 - lr * (wd * w0 + g / (np.abs(g) + eps)), rtol=1e-14, atol=1e-16)
+    np.testing.assert_allclose(m, 0.2 * g, rtol=1e-15)
+    np.testing.assert_allclose(v, 0.01 * g * g, rtol=1e-14)
+
+
+def test_adamw_zero_gradient_is_pure_decay():
+    rng = np.random.default_rng(13)
+    w0 = rng.standard_normal(20)
+    w, m, v = w0.copy(), np.zeros(20), np.zeros(20)
+    for k in range(1, 6):
+        w, m, v = oracle.adamw(w, np.zeros(20), m, v, step=k, **ADAMW_HP)
+    decay = 1.0 - ADAMW_HP["lr"] * ADAMW_HP["weight_decay"]
+    np.testing.assert_allclose(w, w0 * decay ** 5, rtol=1e-14)
+    assert not m.any() and not v.any()
+
+
+def test_adamw_is_invariant_to_gradient_scale_when_eps_vanishes():
+    rng = np.random.default_rng(14)
+    w0 = rng.standard_normal(30)
+    gs = [rng.standard_normal(30) for _ in range(3)]
+    hp = dict(ADAMW_HP, eps=1e-300)
+    a = (w0.copy(), np.zeros(30), np.zeros(30))
+    b = (w0.copy(), np.zeros(30), np.zeros(30))
+    for k, g in enumerate(gs, start=1):
+        a = oracle.adamw(a[0], g, a[1], a[2], step=k, **hp)
+        b = oracle.adamw(b[0], 1e3 * g, b[1], b[2], step=k, grad_scale=1e-3 * 7.0, **hp)
+        # b sees 7 g: Adam's update does not depend on the gradient's scale
+    np.testing.assert_allclose(a[0], b[0], rtol=1e-12)
