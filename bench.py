@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--fused", action="store_true",
                     help="forward as one lora_forward launch (v written for the backward) instead of "
                          "lora_shrink + lora_expand_add")
+    ap.add_argument("--adamw", action="store_true",
+                    help="end each step with the AdamW update of the fine-tuning adapter (fp32 master weights)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-min-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -214,6 +216,11 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
               "the multi-GPU layout is described in DESIGN.md and not built", file=sys.stderr)
         sys.exit(2)
+    if args.adamw and args.graph:
+        # the step count (bias corrections) is a launch argument: a captured
+        # graph would replay the first step's constants
+        print("--adamw runs eagerly only", file=sys.stderr)
+        sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
         return
@@ -257,6 +264,13 @@ def main():
             st["seg_ft"] = lb.Segments(n, wl.num_adapters, dev)
             st["ws"] = torch.empty(lb.lora_backward_workspace_bytes(torch.bfloat16, n, wl.d_in, wl.d_out,
                                                                     st["table"].r_max), dtype=torch.uint8, device=dev)
+            if args.adamw:
+                # AdamW state of the fine-tuning adapter's A and B: fp32 master copies and moments
+                st["opt"] = [(w, gr, torch.zeros(w.shape, dtype=torch.float32, device=dev),
+                              torch.zeros(w.shape, dtype=torch.float32, device=dev), w.float())
+                             for a in sorted(set(int(i) for i in wl.ft_ids))
+                             for w, gr in ((A[a], st["dA"][a]), (B[a], st["dB"][a]))]
+                st["opt_step"] = 0
         st["ws_shrink"] = torch.empty(lb.lora_shrink_workspace_bytes(torch.bfloat16, T, wl.d_in, st["table"].r_max),
                                       dtype=torch.uint8, device=dev)
         sets.append(st)
@@ -296,6 +310,13 @@ def main():
             torch.cuda.current_stream(dev).wait_stream(side)
         elif has_ft:
             backward(st, st["v"][s:s + n])
+        if args.adamw and has_ft:
+            st["opt_step"] += 1
+            if ev is not None:
+                ev[2].record()
+            lb.lora_adamw_step(st["opt"], step=st["opt_step"], zero_grad=True)
+            if ev is not None:
+                ev[3].record()
 
     graphs = None
     if args.graph:
@@ -330,7 +351,7 @@ def main():
     # step carries one; with 4 input sets and a stride of 5 every set is
     # sampled).
     sampled = [i for i in range(K) if i % EVENT_EVERY == 0]
-    evs = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for i in sampled}
+    evs = {i: tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for i in sampled}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
@@ -345,7 +366,7 @@ def main():
     # replay the events cannot sit inside the graph, so a separate eager loop
     # of back-to-back expand launches (same rotating buffers) is timed instead.
     if graphs is None:
-        kern_ms = float(np.mean([a.elapsed_time(b) for a, b in evs.values()]))
+        kern_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs.values()]))
         kern_how = f"events around the launch in every {EVENT_EVERY}th timed step ({len(evs)} launches)"
     else:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -394,6 +415,16 @@ def main():
                      "algorithmic_bytes_per_launch": ex["bytes"], "avg_launch_ms": kern_ms, "timing": kern_how,
                      "mfma_frac": ex["flops"] / (kern_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
     }
+    if args.adamw and has_ft:
+        # per element: master, grad, m, v read (16 B); m, v, master written, the
+        # gradient zeroed (16 B); the bf16 weight written (2 B)
+        n_el = sum(t[0].numel() for t in sets[0]["opt"])
+        opt_bytes = 34 * n_el
+        line["config"]["optimizer"] = "adamw"
+        if graphs is None:
+            opt_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs.values()]))
+            line["adamw"] = {"elements": n_el, "algorithmic_bytes_per_launch": opt_bytes, "avg_launch_ms": opt_ms,
+                             "achieved_GBps": opt_bytes / (opt_ms * 1e-3) / 1e9}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_min_seconds)
     print(json.dumps(line), flush=True)

@@ -24,7 +24,7 @@ from ._abi import LORA_BF16, LORA_F32, LORA_MAX_RANK, LoraError
 __all__ = [
     "AdapterTable", "GradTable", "Segments", "LoraError",
     "lora_segments_build", "lora_segments_build_batch", "lora_shrink", "lora_expand_add", "lora_forward",
-    "lora_backward",
+    "lora_backward", "lora_adamw_step",
     "lora_abi_version", "lora_status_string",
     "lora_segments_workspace_bytes", "lora_shrink_workspace_bytes", "lora_backward_workspace_bytes",
     "lora_segments_sched_elems",
@@ -299,3 +299,37 @@ def lora_backward(x: torch.Tensor, dy: torch.Tensor, adapters: AdapterTable, gra
                            grads.ptr, len(adapters), r_max, seg_ft.c, pvs or None, ldv, ws.data_ptr(), ws.numel(),
                            _stream(x.device))
     _abi.check("lora_backward", st)
+
+
+def lora_adamw_step(tensors, *, step: int, lr: float = 1e-3, betas=(0.9, 0.999), eps: float = 1e-8,
+                    weight_decay: float = 0.01, grad_scale: float = 1.0, zero_grad: bool = False) -> None:
+    """One AdamW step over a list of (w, grad, m, v[, master]) tensors (in place, one launch).
+
+    w: bfloat16 or float32 weights (all entries one element type); grad, m, v and the
+    optional master copy: float32 with w's element count, contiguous.
+    """
+    entries = [tuple(e) + (None,) * (5 - len(e)) for e in tensors]
+    if len(entries) > _abi.LORA_ADAMW_MAX_TENSORS:
+        raise ValueError(f"at most {_abi.LORA_ADAMW_MAX_TENSORS} tensors per step")
+    arr = (_abi.LoraAdamwTensor * max(1, len(entries)))()
+    dtype = None
+    dev = None
+    for i, (w, grad, m, v, master) in enumerate(entries):
+        _on_gpu(w, grad, m, v, master)
+        code = _dtype_code(w)
+        if dtype is not None and code != dtype:
+            raise ValueError("all weights of one step must share their element type")
+        dtype, dev = code, w.device
+        for name, t in (("w", w), ("grad", grad), ("m", m), ("v", v), ("master", master)):
+            if t is None and name != "master":
+                raise ValueError(f"{name} is required")
+            if t is not None and (not t.is_contiguous() or t.numel() != w.numel()):
+                raise ValueError(f"{name} must be contiguous with w's element count")
+            if t is not None and name != "w" and t.dtype != torch.float32:
+                raise ValueError(f"{name} must be float32")
+        arr[i] = _abi.LoraAdamwTensor(w.data_ptr(), master.data_ptr() if master is not None else None,
+                                      grad.data_ptr(), m.data_ptr(), v.data_ptr(), w.numel())
+    hp = _abi.LoraAdamwParams(lr, betas[0], betas[1], eps, weight_decay, grad_scale, int(step), int(bool(zero_grad)))
+    stream = _stream(dev) if dev is not None else 0
+    st = _abi.load().lora_adamw_step(LORA_BF16 if dtype is None else dtype, arr, len(entries), hp, stream or None)
+    _abi.check("lora_adamw_step", st)

@@ -40,6 +40,19 @@ class LoraSegments(ctypes.Structure):
     _fields_ = [("counts", _vp), ("offsets", _vp), ("perm", _vp), ("err", _vp), ("sched", _vp)]
 
 
+class LoraAdamwTensor(ctypes.Structure):
+    _fields_ = [("w", _vp), ("master", _vp), ("grad", _vp), ("m", _vp), ("v", _vp), ("n", _i64)]
+
+
+class LoraAdamwParams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float), ("grad_scale", ctypes.c_float),
+                ("step", _i32), ("zero_grad", _i32)]
+
+
+LORA_ADAMW_MAX_TENSORS = 32
+
+
 class LoraSegmentsJob(ctypes.Structure):
     _fields_ = [("adapter_ids", _vp), ("T", _i32), ("seg", LoraSegments), ("ws", _vp), ("ws_bytes", _sz)]
 
@@ -59,6 +72,7 @@ SIGNATURES = {
                                        _vp, _i64, _vp]),
     "lora_forward": (ctypes.c_int, [ctypes.c_int, _vp, _i64, _i32, _i32, _i32, _vp, _i32, _i32, LoraSegments,
                                     _vp, _i64, _vp, _i64, _vp]),
+    "lora_adamw_step": (ctypes.c_int, [ctypes.c_int, _vp, _i32, LoraAdamwParams, _vp]),
     "lora_backward": (ctypes.c_int, [ctypes.c_int, _vp, _i64, _vp, _i64, _vp, _i64, _i32, _i32, _i32, _vp,
                                      _vp, _i32, _i32, LoraSegments, _vp, _i64, _vp, _sz, _vp]),
 }

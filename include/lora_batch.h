@@ -255,6 +255,61 @@ int lora_backward(int dtype, const void* x, int64_t ldx, const void* dy, int64_t
                   const float* v_saved, int64_t ldv, void* ws, size_t ws_bytes,
                   void* stream);
 
+/*
+ * AdamW step on adapter weights.  The fine-tuning applies its optimizer to the
+ * shared adapter weights in place once the gradients of a backward batch have
+ * been accumulated (DeltaServe, section 3.2, "Backward subprocess"); the
+ * optimizer is AdamW with learning rate 1e-3 and weight decay 0.01 (DeltaServe,
+ * section 4.1), i.e. Adam with decoupled weight decay.  For step t >= 1, for
+ * every element of every listed tensor, in fp32:
+ *     g = grad_scale * grad
+ *     m = beta1 m + (1 - beta1) g
+ *     v = beta2 v + (1 - beta2) g^2
+ *     w = w (1 - lr weight_decay) - lr / (1 - beta1^t) * m / (sqrt(v) / sqrt(1 - beta2^t) + eps)
+ * (the bias corrections are computed in double on the host).
+ *   tensors: HOST array of n_tensors (0..LORA_ADAMW_MAX_TENSORS) entries, e.g.
+ *     dA and dB of each trained adapter (one launch for all of them):
+ *     w      [n] dtype, the weights (A_a or B_a), updated in place;
+ *     master [n] fp32 master copy or NULL.  With a master, the update reads
+ *            and writes the master and w receives its rounding (bf16: round
+ *            to nearest even); without one, w itself is read and rounded;
+ *     grad   [n] fp32 accumulated gradient (dA_a or dB_a from lora_backward);
+ *            set to zero after it is read when hp.zero_grad != 0;
+ *     m, v   [n] fp32 moments (zero before step 1), updated in place;
+ *     n      element count (n = 0 entries are skipped).
+ *   Every non-NULL pointer 16-byte aligned; the arrays of one entry must not
+ *   overlap each other or those of another entry.
+ *   hp: lr >= 0, 0 <= beta1, beta2 < 1, eps > 0, weight_decay >= 0, all
+ *   finite; step >= 1.  Defaults of the pages' fine-tuning: lr 1e-3,
+ *   weight_decay 0.01; beta1 0.9, beta2 0.999, eps 1e-8 (not stated there).
+ * Errors: LORA_ERR_INVALID_ARG for a bad dtype, count, pointer, alignment or
+ * hyper-parameter, before anything is enqueued.  One kernel.
+ */
+#define LORA_ADAMW_MAX_TENSORS 32
+
+typedef struct {
+    void* w;
+    float* master;
+    float* grad;
+    float* m;
+    float* v;
+    int64_t n;
+} lora_adamw_tensor;
+
+typedef struct {
+    float lr;
+    float beta1;
+    float beta2;
+    float eps;
+    float weight_decay;
+    float grad_scale;
+    int32_t step;
+    int32_t zero_grad;
+} lora_adamw_params;
+
+int lora_adamw_step(int dtype, const lora_adamw_tensor* tensors, int32_t n_tensors, lora_adamw_params hp,
+                    void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -46,6 +46,63 @@ def test_struct_sizes_match_header():
     assert _abi.LoraSegmentsJob.seg.offset == 16 and _abi.LoraSegmentsJob.ws_bytes.offset == 64
 
 
+def test_struct_layouts_match_header_compiled_by_gcc(tmp_path):
+    # sizes and offsets of the header's structs as a C compiler lays them out
+    probe = tmp_path / "probe.c"
+    probe.write_text("""#include <stdio.h>
+#include <stddef.h>
+#include "lora_batch.h"
+int main(void) {
+  printf("%zu %zu %zu %zu %zu %zu\\n", sizeof(lora_adapter), sizeof(lora_adapter_grad), sizeof(lora_segments),
+         sizeof(lora_segments_job), sizeof(lora_adamw_tensor), sizeof(lora_adamw_params));
+  printf("%zu %zu %zu %zu\\n", offsetof(lora_adamw_tensor, n), offsetof(lora_adamw_params, step),
+         offsetof(lora_adamw_params, zero_grad), offsetof(lora_segments_job, ws_bytes));
+  return 0;
+}
+""")
+    exe = tmp_path / "probe"
+    import subprocess
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(probe), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()
+    sizes = [int(v) for v in out]
+    assert sizes[:6] == [ctypes.sizeof(t) for t in (_abi.LoraAdapter, _abi.LoraAdapterGrad, _abi.LoraSegments,
+                                                      _abi.LoraSegmentsJob, _abi.LoraAdamwTensor,
+                                                      _abi.LoraAdamwParams)]
+    assert sizes[6:] == [_abi.LoraAdamwTensor.n.offset, _abi.LoraAdamwParams.step.offset,
+                         _abi.LoraAdamwParams.zero_grad.offset, _abi.LoraSegmentsJob.ws_bytes.offset]
+
+
+def test_adamw_rejects_before_touching_the_gpu(lib):
+    bad = _abi.LORA_ERR_INVALID_ARG
+
+    def hp(**kw):
+        d = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, grad_scale=1.0, step=1, zero_grad=0)
+        d.update(kw)
+        return _abi.LoraAdamwParams(**d)
+
+    def arr(*ts):
+        a = (_abi.LoraAdamwTensor * max(1, len(ts)))(*ts)
+        return a
+
+    good = _abi.LoraAdamwTensor(FAKE, None, FAKE, FAKE, FAKE, 1024)
+    # nothing to do: no tensors, or only empty ones
+    assert lib.lora_adamw_step(0, None, 0, hp(), None) == _abi.LORA_OK
+    assert lib.lora_adamw_step(0, arr(_abi.LoraAdamwTensor(None, None, None, None, None, 0)), 1, hp(), None) == 0
+    assert lib.lora_adamw_step(2, arr(good), 1, hp(), None) == bad          # dtype
+    assert lib.lora_adamw_step(0, None, 1, hp(), None) == bad               # no array
+    assert lib.lora_adamw_step(0, arr(good), -1, hp(), None) == bad
+    assert lib.lora_adamw_step(0, arr(*[good] * 33), 33, hp(), None) == bad  # more than the maximum
+    for t in (_abi.LoraAdamwTensor(None, None, FAKE, FAKE, FAKE, 8), _abi.LoraAdamwTensor(FAKE, None, None, FAKE, FAKE, 8),
+              _abi.LoraAdamwTensor(FAKE, None, FAKE, None, FAKE, 8), _abi.LoraAdamwTensor(FAKE, None, FAKE, FAKE, None, 8),
+              _abi.LoraAdamwTensor(FAKE + 4, None, FAKE, FAKE, FAKE, 8),
+              _abi.LoraAdamwTensor(FAKE, FAKE + 8, FAKE, FAKE, FAKE, 8),
+              _abi.LoraAdamwTensor(FAKE, None, FAKE, FAKE, FAKE, -1)):
+        assert lib.lora_adamw_step(0, arr(good, t), 2, hp(), None) == bad
+    for kw in (dict(lr=-1.0), dict(lr=float("inf")), dict(beta1=1.0), dict(beta2=-0.1), dict(eps=0.0),
+               dict(weight_decay=-0.01), dict(grad_scale=float("nan")), dict(step=0), dict(lr=float("nan"))):
+        assert lib.lora_adamw_step(0, arr(good), 1, hp(**kw), None) == bad, kw
+
+
 def test_workspace_queries(lib):
     assert lib.lora_segments_workspace_bytes(0, 4) > 0
     assert lib.lora_segments_workspace_bytes(-1, 4) == 0
