@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--fused", action="store_true",
                     help="forward as one lora_forward launch (v written for the backward) instead of "
                          "lora_shrink + lora_expand_add")
+    ap.add_argument("--preemptible", action="store_true",
+                    help="run the backward through lora_backward_preemptible with a granted grant word")
     ap.add_argument("--adamw", action="store_true",
                     help="end each step with the AdamW update of the fine-tuning adapter (fp32 master weights)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -278,7 +280,14 @@ def main():
 
     side = torch.cuda.Stream(device=dev) if args.overlap else None  # default priority
 
+    grant = torch.ones(1, dtype=torch.int32, device=dev) if args.preemptible else None
+    status = torch.zeros(1, dtype=torch.int32, device=dev) if args.preemptible else None
+
     def backward(st, v_saved):
+        if grant is not None:
+            lb.lora_backward_preemptible(st["x"][s:s + n], st["dy"], st["table"], st["grads"], st["seg_ft"], grant,
+                                         status, dx=st["dx"], v_saved=v_saved, ws=st["ws"])
+            return
         lb.lora_backward(st["x"][s:s + n], st["dy"], st["table"], st["grads"], st["seg_ft"], dx=st["dx"],
                          v_saved=v_saved, ws=st["ws"])
 
@@ -381,6 +390,8 @@ def main():
         torch.cuda.synchronize()
         kern_ms = e0.elapsed_time(e1) / K
         kern_how = "events around back-to-back launches"
+    if status is not None and int(status.item()) != 0:
+        raise RuntimeError("the granted preemptible backward reported a yield")
     errs = [int(st["seg"].err.item()) + (int(st["seg_ft"].err.item()) if has_ft else 0) for st in sets]
     if any(errs):
         raise RuntimeError(f"device-side data errors reported: {errs}")
@@ -405,7 +416,8 @@ def main():
                    "d_out": wl.d_out, "adapters": wl.num_adapters, "ranks": RANKS_DESC[args.workload],
                    "ft_adapter_rank": r_ft, "seed": 0, "input_sets": args.sets,
                    "launch": "graph" if graphs is not None else "eager",
-                   "streams": 2 if args.overlap else 1, "forward": "fused" if args.fused else "split"},
+                   "streams": 2 if args.overlap else 1, "forward": "fused" if args.fused else "split",
+                   "backward": "preemptible" if args.preemptible else "plain"},
         "host_enqueue_ms_per_step": (t_enq - t0) * 1e3 / K,
         "step_algorithmic_GBps": alg["step"]["bytes"] / (ms * 1e-3) / 1e9,
         "step_algorithmic_bytes": alg["step"]["bytes"],

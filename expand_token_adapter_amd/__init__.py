@@ -24,7 +24,7 @@ from ._abi import LORA_BF16, LORA_F32, LORA_MAX_RANK, LoraError
 __all__ = [
     "AdapterTable", "GradTable", "Segments", "LoraError",
     "lora_segments_build", "lora_segments_build_batch", "lora_shrink", "lora_expand_add", "lora_forward",
-    "lora_backward", "lora_adamw_step",
+    "lora_backward", "lora_backward_preemptible", "lora_adamw_step",
     "lora_abi_version", "lora_status_string",
     "lora_segments_workspace_bytes", "lora_shrink_workspace_bytes", "lora_backward_workspace_bytes",
     "lora_segments_sched_elems",
@@ -275,6 +275,22 @@ def lora_backward(x: torch.Tensor, dy: torch.Tensor, adapters: AdapterTable, gra
                   dx: Optional[torch.Tensor] = None, v_saved: Optional[torch.Tensor] = None,
                   r_max: Optional[int] = None, ws: Optional[torch.Tensor] = None) -> None:
     """Accumulate dX (if given), dA and dB of the fine-tuning rows x / dy."""
+    _backward("lora_backward", x, dy, adapters, grads, seg_ft, dx, v_saved, r_max, ws, ())
+
+
+def lora_backward_preemptible(x: torch.Tensor, dy: torch.Tensor, adapters: AdapterTable, grads: GradTable,
+                              seg_ft: Segments, grant: torch.Tensor, status: torch.Tensor,
+                              dx: Optional[torch.Tensor] = None, v_saved: Optional[torch.Tensor] = None,
+                              r_max: Optional[int] = None, ws: Optional[torch.Tensor] = None) -> None:
+    """lora_backward that yields while grant[0] == 0; status[0] becomes 0 (ran) or 1 (yielded, outputs untouched)."""
+    for name, t in (("grant", grant), ("status", status)):
+        if not t.is_cuda or t.dtype != torch.int32 or t.numel() < 1:
+            raise ValueError(f"{name} must be an int32 tensor on the GPU")
+    _backward("lora_backward_preemptible", x, dy, adapters, grads, seg_ft, dx, v_saved, r_max, ws,
+              (grant.data_ptr(), status.data_ptr()))
+
+
+def _backward(fn, x, dy, adapters, grads, seg_ft, dx, v_saved, r_max, ws, extra) -> None:
     _on_gpu(x, dy, dx, v_saved)
     px, T, d_in, ldx = _rows(x, "x")
     pdy, Td, d_out, lddy = _rows(dy, "dy")
@@ -295,10 +311,10 @@ def lora_backward(x: torch.Tensor, dy: torch.Tensor, adapters: AdapterTable, gra
     need = lib.lora_backward_workspace_bytes(_dtype_code(x), T, d_in, d_out, r_max)
     if ws is None or ws.numel() < need:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
-    st = lib.lora_backward(_dtype_code(x), px, ldx, pdy, lddy, pdx or None, lddx, T, d_in, d_out, adapters.ptr,
-                           grads.ptr, len(adapters), r_max, seg_ft.c, pvs or None, ldv, ws.data_ptr(), ws.numel(),
-                           _stream(x.device))
-    _abi.check("lora_backward", st)
+    st = getattr(lib, fn)(_dtype_code(x), px, ldx, pdy, lddy, pdx or None, lddx, T, d_in, d_out, adapters.ptr,
+                          grads.ptr, len(adapters), r_max, seg_ft.c, pvs or None, ldv, ws.data_ptr(), ws.numel(),
+                          *extra, _stream(x.device))
+    _abi.check(fn, st)
 
 
 def lora_adamw_step(tensors, *, step: int, lr: float = 1e-3, betas=(0.9, 0.999), eps: float = 1e-8,

@@ -75,6 +75,9 @@ SIGNATURES = {
     "lora_adamw_step": (ctypes.c_int, [ctypes.c_int, _vp, _i32, LoraAdamwParams, _vp]),
     "lora_backward": (ctypes.c_int, [ctypes.c_int, _vp, _i64, _vp, _i64, _vp, _i64, _i32, _i32, _i32, _vp,
                                      _vp, _i32, _i32, LoraSegments, _vp, _i64, _vp, _sz, _vp]),
+    "lora_backward_preemptible": (ctypes.c_int, [ctypes.c_int, _vp, _i64, _vp, _i64, _vp, _i64, _i32, _i32, _i32,
+                                                 _vp, _vp, _i32, _i32, LoraSegments, _vp, _i64, _vp, _sz, _vp, _vp,
+                                                 _vp]),
 }
 
 _lib = None

@@ -83,11 +83,25 @@ extern "C" size_t lora_backward_workspace_bytes(int dtype, int32_t T_ft, int32_t
     return (size_t)BwdWs::make(dtype, T_ft, d_in, d_out, r_max).total * sizeof(float);
 }
 
-extern "C" int lora_backward(int dtype, const void* x, int64_t ldx, const void* dy, int64_t lddy, void* dx,
-                             int64_t lddx, int32_t T_ft, int32_t d_in, int32_t d_out, const lora_adapter* adapters,
-                             const lora_adapter_grad* grads, int32_t num_adapters, int32_t r_max,
-                             lora_segments seg_ft, const float* v_saved, int64_t ldv, void* ws, size_t ws_bytes,
-                             void* stream) {
+namespace {
+
+// Backward preemption gate (one thread): status = 1 ("yield") when the grant
+// has been withdrawn (*grant == 0) or an earlier gate of the same call has
+// already yielded; otherwise 0.  The grant is read with a system-scope load,
+// so a flag in host memory mapped for the device, or in device memory updated
+// by a copy, is read fresh.
+__global__ __launch_bounds__(kWave) void bwd_gate_kernel(const int32_t* grant, int32_t* status, int32_t first) {
+    if (threadIdx.x != 0) return;
+    const int32_t g = __hip_atomic_load(grant, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    const int32_t before = first ? 0 : __hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(status, (before != 0 || g == 0) ? 1 : 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+int backward_impl(int dtype, const void* x, int64_t ldx, const void* dy, int64_t lddy, void* dx, int64_t lddx,
+                  int32_t T_ft, int32_t d_in, int32_t d_out, const lora_adapter* adapters,
+                  const lora_adapter_grad* grads, int32_t num_adapters, int32_t r_max, lora_segments seg_ft,
+                  const float* v_saved, int64_t ldv, void* ws, size_t ws_bytes, const int32_t* grant,
+                  int32_t* status, void* stream) {
     int rc = check_common(dtype, T_ft, num_adapters, r_max, adapters, seg_ft);
     if (rc != LORA_OK) return rc;
     if (d_in < 1 || d_out < 1 || !grads || ((uintptr_t)grads & 7u)) return LORA_ERR_INVALID_ARG;
@@ -103,6 +117,12 @@ extern "C" int lora_backward(int dtype, const void* x, int64_t ldx, const void* 
     hipStream_t st = static_cast<hipStream_t>(stream);
     const SchedLayout sl = SchedLayout::make(T_ft, num_adapters);
     float* wsf = static_cast<float*>(ws);
+    // preemption: gate before the skinny part (whose kernels then skip their
+    // work if it yielded) and before the output part (all or nothing)
+    if (grant) {
+        hipLaunchKernelGGL(bwd_gate_kernel, dim3(1), dim3(kWave), 0, st, grant, status, 1);
+        if (hipGetLastError() != hipSuccess) return LORA_ERR_HIP;
+    }
     float* g = wsf + w.g;
     float* gT = wsf + w.gT;
     float* vT = wsf + w.vT;
@@ -123,6 +143,7 @@ extern "C" int lora_backward(int dtype, const void* x, int64_t ldx, const void* 
     sp.nslices = shrink_slices(dtype, d_out);
     sp.err = seg_ft.err;
     sp.rgroups = rank_groups(r_max);
+    sp.stop = grant ? status : nullptr;
     ReduceParams rp{};
     rp.part = sp.part;
     rp.ldp = sp.ldp;
@@ -138,6 +159,7 @@ extern "C" int lora_backward(int dtype, const void* x, int64_t ldx, const void* 
     rp.out_by_pos = 1;
     rp.outT = gT;
     rp.ldT = w.ldT;
+    rp.stop = sp.stop;
     // 2. v = A x, rank-major by sorted position: the caller's v, copied by the
     //    reduce of g, or a second shrink.
     if (v_saved) {
@@ -161,6 +183,10 @@ extern "C" int lora_backward(int dtype, const void* x, int64_t ldx, const void* 
     }
 
     // 3. dA += s g^T x, dB += s dy^T v.
+    if (grant) {
+        hipLaunchKernelGGL(bwd_gate_kernel, dim3(1), dim3(kWave), 0, st, grant, status, 0);
+        if (hipGetLastError() != hipSuccess) return LORA_ERR_HIP;
+    }
     ContractParams cp{};
     cp.x = x;
     cp.ldx = ldx;
@@ -184,6 +210,7 @@ extern "C" int lora_backward(int dtype, const void* x, int64_t ldx, const void* 
     cp.err = seg_ft.err;
     cp.fix = wsf + w.fix;
     cp.fix_meta = reinterpret_cast<int32_t*>(wsf + w.fix_meta);
+    cp.stop = grant ? status : nullptr;
     // kContractGrid workgroups (a multiple of the 8 XCDs) split the work evenly
     if (dtype == LORA_BF16)
         hipLaunchKernelGGL(contract_kernel<LORA_BF16>, dim3(kContractGrid), dim3(contract_waves<LORA_BF16>() * kWave),
@@ -207,6 +234,7 @@ extern "C" int lora_backward(int dtype, const void* x, int64_t ldx, const void* 
         ep.ldy = lddx;
         ep.N = d_in;
         ep.err = seg_ft.err;
+        ep.stop = cp.stop;
         ExpandParams q;
         unsigned n_expand;
         const int ks = expand_plan(ep, T_ft, num_adapters, r_max, &q, &n_expand);
@@ -218,4 +246,26 @@ extern "C" int lora_backward(int dtype, const void* x, int64_t ldx, const void* 
         hipLaunchKernelGGL(contract_fixup_kernel, dim3(kContractGrid), dim3(4 * kWave), 0, st, cp, (int)kContractGrid);
     }
     return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" int lora_backward(int dtype, const void* x, int64_t ldx, const void* dy, int64_t lddy, void* dx,
+                             int64_t lddx, int32_t T_ft, int32_t d_in, int32_t d_out, const lora_adapter* adapters,
+                             const lora_adapter_grad* grads, int32_t num_adapters, int32_t r_max,
+                             lora_segments seg_ft, const float* v_saved, int64_t ldv, void* ws, size_t ws_bytes,
+                             void* stream) {
+    return backward_impl(dtype, x, ldx, dy, lddy, dx, lddx, T_ft, d_in, d_out, adapters, grads, num_adapters, r_max,
+                         seg_ft, v_saved, ldv, ws, ws_bytes, nullptr, nullptr, stream);
+}
+
+extern "C" int lora_backward_preemptible(int dtype, const void* x, int64_t ldx, const void* dy, int64_t lddy,
+                                         void* dx, int64_t lddx, int32_t T_ft, int32_t d_in, int32_t d_out,
+                                         const lora_adapter* adapters, const lora_adapter_grad* grads,
+                                         int32_t num_adapters, int32_t r_max, lora_segments seg_ft,
+                                         const float* v_saved, int64_t ldv, void* ws, size_t ws_bytes,
+                                         const int32_t* grant, int32_t* status, void* stream) {
+    if (!grant || !status || ((uintptr_t)grant & 3u) || ((uintptr_t)status & 3u)) return LORA_ERR_INVALID_ARG;
+    return backward_impl(dtype, x, ldx, dy, lddy, dx, lddx, T_ft, d_in, d_out, adapters, grads, num_adapters, r_max,
+                         seg_ft, v_saved, ldv, ws, ws_bytes, grant, status, stream);
 }

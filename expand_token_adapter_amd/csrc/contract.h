@@ -74,6 +74,9 @@ struct ContractParams {
     float* fix;       // [grid][2] partial tiles of cut tiles (kFixFloats floats each)
     int32_t* fix_meta;  // [grid][2][kFixMeta]: first unit of the tile (lo, hi; -1: none, -2: empty
                         // range), adapter, rank group, column block, owner
+    // backward preemption: when set and *stop != 0 at the start, the
+    // workgroup does nothing (null in the forward)
+    const int32_t* stop;
 };
 
 constexpr int kContractGrid = 256;  // one workgroup per CU
@@ -216,6 +219,7 @@ __global__ __launch_bounds__(contract_waves<DT>() * kWave) __attribute__((amdgpu
 void contract_kernel(ContractParams p) {
     constexpr int NW = contract_waves<DT>();
     __shared__ __attribute__((aligned(16))) char s_mem[ContractLds<DT>::kBytes];
+    if (p.stop && *p.stop) return;
 
     const int wave = wave_id();
     const int lane = threadIdx.x & (kWave - 1);
@@ -418,6 +422,7 @@ void contract_kernel(ContractParams p) {
 // later workgroups that hold the same tile follow g in order.
 // (as workgroup g0 of a 4-wave grid part)
 __device__ __forceinline__ void contract_fixup_body(const ContractParams& p, int G, int g0) {
+    if (p.stop && *p.stop) return;
     const int nb = wave_id();
     const int lane = threadIdx.x & (kWave - 1);
     const int lr = lane & 15;

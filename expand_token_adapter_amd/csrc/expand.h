@@ -46,6 +46,9 @@ struct ExpandParams {
     int64_t ldy;
     int32_t N;          // output columns (d_out, or d_in for dX)
     int32_t* err;
+    // backward preemption: when set and *stop != 0 at the start, the
+    // workgroup does nothing (null in the forward)
+    const int32_t* stop;
 };
 
 // The kernel's work as workgroup blk of nblk (nblk a multiple of 8, the
@@ -74,6 +77,7 @@ __device__ __forceinline__ void expand_body(const ExpandParams& p, int blk, int 
     const int lg = lane >> 4;
     const int yr = lane >> 3;       // row (and row + 8) of the step in the row-contiguous layout
     const int yc = 8 * (lane & 7);  // first column (of the wave's 64) in that layout
+    if (p.stop && *p.stop) return;
     const int ncg = (p.N + kExpandCols - 1) / kExpandCols;
     const int64_t n_tasks = (int64_t)p.sched[1] * ncg;
     const TaskSlice ts = xcd_slice_of(blk, nblk, n_tasks, 1, 0);

@@ -55,6 +55,7 @@ constexpr int kReduceJ = LORA_MAX_RANK / 16;
 
 __global__ __launch_bounds__(kReduceWaves * kWave) void shrink_reduce_kernel(ReduceParams p) {
     __shared__ f32x4_t s_acc[kReduceWaves - 1][kReduceJ][kWave];
+    if (p.stop && *p.stop) return;
     const int wave = wave_id();
     const int lane = threadIdx.x & (kWave - 1);
     const int n = lane & 15;

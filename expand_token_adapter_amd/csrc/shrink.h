@@ -58,6 +58,9 @@ struct ShrinkParams {
     int32_t nslices;
     int32_t* err;
     int32_t rgroups; // ceil(r_max / 64)
+    // backward preemption: when set and *stop != 0 at the start, the
+    // workgroup does nothing (null in the forward)
+    const int32_t* stop;
 };
 
 // acc[mb] += W(rank block mb) x X over chunks cc0 .. cc0 + SCH - 1 of the slice
@@ -106,6 +109,7 @@ void shrink_kernel(ShrinkParams p) {
     char* s_wb = reinterpret_cast<char*>(s_w);
     f32x4_t* s_red = reinterpret_cast<f32x4_t*>(s_w);  // reused after the MFMA pass
 
+    if (p.stop && *p.stop) return;
     const int wave = wave_id();
     const int lane = threadIdx.x & (kWave - 1);
     const int lr = lane & 15;  // MFMA row / column within the 16x16 tile
@@ -313,6 +317,9 @@ struct ReduceParams {
     const float* vsrc;
     int64_t ldvsrc;
     float* vT;
+    // backward preemption: when set and *stop != 0 at the start, the
+    // workgroup does nothing (null in the forward)
+    const int32_t* stop;
 };
 
 // shrink_reduce_kernel(ReduceParams) is defined in forward.hip.

@@ -256,6 +256,33 @@ int lora_backward(int dtype, const void* x, int64_t ldx, const void* dy, int64_t
                   void* stream);
 
 /*
+ * lora_backward that yields to inference.  DeltaServe (section 3.4, backward
+ * preemption) lets its backward run next to decode steps and preempts it for
+ * prefill through a shared GPU-grant flag that the backward checks at every
+ * layer boundary: the inference side clears the flag before a step with
+ * prefill rows and sets it again afterwards.  Here the flag is checked on the
+ * device at two points of the call: before the skinny part (g = B^T dy, v) and
+ * before the output part (dA, dB, dX).
+ *   grant: int32 readable by the device (device memory, or host memory mapped
+ *          for the device), read with system-scope loads; nonzero = granted.
+ *   status: device int32, written by the call: 0 = the backward ran to the
+ *          end; 1 = it yielded: the grant was zero at one of the two points,
+ *          and dA, dB and dX are left exactly as they were (the output part
+ *          runs completely or not at all; the kernels of a yielded part skip
+ *          their work).  The caller re-issues the call once granted again.
+ *          Read it after the call has completed on the stream.
+ * Other arguments, results and errors as for lora_backward; additionally
+ * LORA_ERR_INVALID_ARG for a NULL or misaligned grant / status.  With
+ * T_ft == 0 nothing is enqueued and status is not written.
+ */
+int lora_backward_preemptible(int dtype, const void* x, int64_t ldx, const void* dy, int64_t lddy,
+                              void* dx, int64_t lddx, int32_t T_ft, int32_t d_in, int32_t d_out,
+                              const lora_adapter* adapters, const lora_adapter_grad* grads,
+                              int32_t num_adapters, int32_t r_max, lora_segments seg_ft,
+                              const float* v_saved, int64_t ldv, void* ws, size_t ws_bytes,
+                              const int32_t* grant, int32_t* status, void* stream);
+
+/*
  * AdamW step on adapter weights.  The fine-tuning applies its optimizer to the
  * shared adapter weights in place once the gradients of a backward batch have
  * been accumulated (DeltaServe, section 3.2, "Backward subprocess"); the

@@ -56,7 +56,8 @@ class GpuCase:
         torch.cuda.synchronize()
         return y, v, seg
 
-    def backward(self, v_saved=None, dx0=None, dA0=None, dB0=None, with_dx=True):
+    def backward(self, v_saved=None, dx0=None, dA0=None, dB0=None, with_dx=True, grant=None, status=None):
+        """lora_backward, or lora_backward_preemptible when a grant word is given."""
         wl = self.wl
         s, n = wl.ft_start, wl.ft_count
         dev = self.dev
@@ -70,7 +71,11 @@ class GpuCase:
         if with_dx:
             dx = torch.zeros((n, wl.d_in), dtype=self.x.dtype, device=dev) if dx0 is None else to_dev(dx0, wl.dtype, dev)
         dy = to_dev(wl.dy, wl.dtype, dev)
-        lb.lora_backward(self.x[s:s + n], dy, self.table, grads, seg_ft, dx=dx, v_saved=v_saved)
+        if grant is None:
+            lb.lora_backward(self.x[s:s + n], dy, self.table, grads, seg_ft, dx=dx, v_saved=v_saved)
+        else:
+            lb.lora_backward_preemptible(self.x[s:s + n], dy, self.table, grads, seg_ft, grant, status, dx=dx,
+                                         v_saved=v_saved)
         torch.cuda.synchronize()
         return dx, dA, dB, seg_ft
 

@@ -72,6 +72,20 @@ int main(void) {
                          _abi.LoraAdamwParams.zero_grad.offset, _abi.LoraSegmentsJob.ws_bytes.offset]
 
 
+def test_backward_preemptible_rejects(lib):
+    bad = _abi.LORA_ERR_INVALID_ARG
+    need = lib.lora_backward_workspace_bytes(0, 64, 256, 512, 16)
+
+    def call(grant=FAKE, status=FAKE, T=64, A=4):
+        return lib.lora_backward_preemptible(0, FAKE, 256, FAKE, 512, None, 0, T, 256, 512, FAKE, FAKE, A, 16,
+                                             _seg(), None, 0, FAKE, need, grant, status, None)
+
+    assert call(grant=None) == bad and call(status=None) == bad
+    assert call(grant=FAKE + 2) == bad and call(status=FAKE + 1) == bad   # not 4-byte aligned
+    assert call(A=0) == bad                                                # the backward's own checks follow
+    assert call(T=-1) == bad
+
+
 def test_adamw_rejects_before_touching_the_gpu(lib):
     bad = _abi.LORA_ERR_INVALID_ARG
 
