@@ -57,6 +57,9 @@ def parse():
                     help="run the backward through lora_backward_preemptible with a granted grant word")
     ap.add_argument("--adamw", action="store_true",
                     help="end each step with the AdamW update of the fine-tuning adapter (fp32 master weights)")
+    ap.add_argument("--cost-model", action="store_true",
+                    help="calibrate and fit the cost model of the library's calls, then check its predictions on "
+                         "the four bf16 workloads (held out); prints JSON lines, not the bench line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-min-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -212,6 +215,66 @@ def cpu_baseline(wl, min_seconds):
                       f"repeated {reps}x in {el:.1f} s, fp64 plain loops, OpenMP over rows"}
 
 
+def cost_model_report(reps: int = 10):
+    """Fit the cost model on synthetic calibration batches, then predict the workloads' calls."""
+    import torch
+    import expand_token_adapter_amd as lb
+    from expand_token_adapter_amd import cost_model as cm
+    import workloads
+
+    t0 = time.perf_counter()
+    samples = cm.calibrate(reps=reps)
+    model = cm.fit_samples(samples)
+    errs = cm.relative_errors(model, samples)
+    for op in cm.OPS:
+        e = np.abs(errs[op])
+        print(json.dumps({"cost_model": op, "coef": dict(zip(cm.FEATURES, model.coef[op].tolist())),
+                          "calibration_samples": int(e.size), "median_abs_rel_err": float(np.median(e)),
+                          "max_abs_rel_err": float(e.max())}), flush=True)
+    print(json.dumps({"calibration_seconds": time.perf_counter() - t0}), flush=True)
+    dev = torch.device("cuda:0")
+    for w in (2, 3, 4, 5):
+        wl = workloads.config(w, seed=0)
+        dev_e = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        A, B = [dev_e(a) for a in wl.A], [dev_e(b) for b in wl.B]
+        table = lb.AdapterTable(A, B, wl.scales.tolist())
+        ids = torch.from_numpy(wl.ids).to(dev)
+        x, y = dev_e(wl.x), dev_e(wl.y0)
+        seg = lb.Segments(wl.T, wl.num_adapters, dev)
+        lb.lora_segments_build(ids, wl.num_adapters, out=seg)
+        v = torch.zeros((wl.T, (table.r_max + 7) // 8 * 8), dtype=torch.float32, device=dev)
+        ws = torch.empty(lb.lora_shrink_workspace_bytes(torch.bfloat16, wl.T, wl.d_in, table.r_max),
+                         dtype=torch.uint8, device=dev)
+        calls = {"segments": (lambda: lb.lora_segments_build(ids, wl.num_adapters, out=seg), wl.ids),
+                 "forward": (lambda: (lb.lora_shrink(x, table, seg, v=v, ws=ws),
+                                      lb.lora_expand_add(v, table, seg, y)), wl.ids),
+                 "forward_fused": (lambda: lb.lora_forward(x, table, seg, y, v=v), wl.ids)}
+        if wl.ft_count:
+            s, n = wl.ft_start, wl.ft_count
+            seg_ft = lb.Segments(n, wl.num_adapters, dev)
+            lb.lora_segments_build(ids[s:s + n].contiguous(), wl.num_adapters, out=seg_ft)
+            dy, dx = dev_e(wl.dy), torch.zeros((n, wl.d_in), dtype=torch.bfloat16, device=dev)
+            grads = lb.GradTable([torch.zeros(a.shape, dtype=torch.float32, device=dev) for a in A],
+                                 [torch.zeros(b.shape, dtype=torch.float32, device=dev) for b in B])
+            bws = torch.empty(lb.lora_backward_workspace_bytes(torch.bfloat16, n, wl.d_in, wl.d_out, table.r_max),
+                              dtype=torch.uint8, device=dev)
+            calls["backward"] = (lambda: lb.lora_backward(x[s:s + n], dy, table, grads, seg_ft, dx=dx,
+                                                          v_saved=v[s:s + n], ws=bws), wl.ids[s:s + n])
+        for op, (f, op_ids) in calls.items():
+            f()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                f()
+            e1.record()
+            torch.cuda.synchronize()
+            meas = e0.elapsed_time(e1) * 1e-3 / reps
+            pred = model.predict(op, op_ids, wl.ranks, wl.d_in, wl.d_out)
+            print(json.dumps({"workload": workloads.CONFIG_NAMES[w], "op": op, "measured_us": meas * 1e6,
+                              "predicted_us": pred * 1e6, "rel_err": pred / meas - 1.0}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -225,6 +288,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.cost_model:
+        cost_model_report()
         return
     if args.traffic_from:
         traffic_from(*args.traffic_from)

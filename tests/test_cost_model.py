@@ -1,0 +1,62 @@
+"""Host tests of the cost model: its features against a brute-force count, and
+its fit against coefficients it must recover."""
+import numpy as np
+import pytest
+
+from expand_token_adapter_amd import cost_model as cm
+
+
+def test_features_by_brute_force():
+    ids = [0, 2, 2, -1, 5, 2, 0]      # 5 is out of range: no adapter
+    ranks = [4, 8, 16]
+    d_in, d_out = 24, 40
+    f = cm.features(ids, ranks, d_in, d_out)
+    rows = [i for i in ids if 0 <= i < len(ranks)]
+    used = sorted(set(rows))
+    want = [1.0, len(ids) * (d_in + d_out), sum(ranks[a] for a in used) * (d_in + d_out),
+            sum(ranks[i] for i in rows), len(used)]
+    assert f.tolist() == want
+    assert cm.features([], ranks, d_in, d_out).tolist() == [1.0, 0.0, 0.0, 0.0, 0.0]
+
+
+def _design(rng, n):
+    # feature columns with the magnitudes of real calls
+    T = rng.integers(16, 8192, size=n)
+    d = rng.choice([4096, 8192, 18432], size=n)
+    return np.stack([np.ones(n), T * d, rng.integers(16, 4096, size=n) * d, T * rng.integers(8, 64, size=n),
+                     rng.integers(1, 320, size=n)], axis=1).astype(np.float64)
+
+
+def test_fit_recovers_exact_coefficients():
+    rng = np.random.default_rng(0)
+    X = _design(rng, 60)
+    c = np.array([8e-6, 2.5e-13, 2.6e-13, 1e-11, 3e-8])
+    got = cm.fit(X, X @ c)
+    np.testing.assert_allclose(got, c, rtol=1e-5)
+
+
+def test_fit_with_noise_and_a_zero_coefficient():
+    rng = np.random.default_rng(1)
+    X = _design(rng, 200)
+    c = np.array([5e-6, 3e-13, 0.0, 2e-11, 1e-8])
+    t = X @ c * (1.0 + 0.01 * rng.standard_normal(200))
+    got = cm.fit(X, t)
+    assert np.all(got >= 0.0)
+    np.testing.assert_allclose(got[[0, 1, 3]], c[[0, 1, 3]], rtol=0.1)
+    assert got[2] * X[:, 2].max() < 0.05 * t.min()   # the absent term stays negligible
+    rel = X @ got / t - 1.0
+    assert np.median(np.abs(rel)) < 0.02
+
+
+def test_fit_needs_enough_samples():
+    with pytest.raises(ValueError):
+        cm.fit(np.ones((3, 5)), np.ones(3))
+
+
+def test_model_json_round_trip_and_predict():
+    m = cm.CostModel({"forward": [1e-6, 1e-12, 2e-12, 3e-11, 4e-9]})
+    m2 = cm.CostModel.from_json(m.to_json())
+    ids, ranks = [0, 1, 1], [8, 16]
+    assert m2.predict("forward", ids, ranks, 64, 32) == pytest.approx(m.predict("forward", ids, ranks, 64, 32))
+    f = cm.features(ids, ranks, 64, 32)
+    assert m.predict("forward", ids, ranks, 64, 32) == pytest.approx(float(f @ m.coef["forward"]))
