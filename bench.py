@@ -60,6 +60,9 @@ def parse():
     ap.add_argument("--cost-model", action="store_true",
                     help="calibrate and fit the cost model of the library's calls, then check its predictions on "
                          "the four bf16 workloads (held out); prints JSON lines, not the bench line")
+    ap.add_argument("--multi-slice", action="store_true",
+                    help="q/k/v projections of the decode workload (d_out 4096/1024/1024): three split forwards, "
+                         "three lora_forward launches and one lora_forward_multi; prints JSON lines, not the bench line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-min-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -215,6 +218,57 @@ def cpu_baseline(wl, min_seconds):
                       f"repeated {reps}x in {el:.1f} s, fp64 plain loops, OpenMP over rows"}
 
 
+def multi_slice_report(steps: int, warmup: int, n_sets: int):
+    """Forward of three projections sharing x (decode batch): split, three fused launches, one multi-slice launch."""
+    import torch
+    import expand_token_adapter_amd as lb
+    import workloads
+
+    dev = torch.device("cuda:0")
+    wq = workloads.config(2, seed=0)
+    wls = [wq] + [workloads.custom(wq.ids, wq.ranks, wq.d_in, 1024, "bf16", seed=100 + k) for k in range(2)]
+    dev_e = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    sets = []
+    for k in range(n_sets):
+        st = {"x": dev_e(wq.x), "ids": torch.from_numpy(wq.ids).to(dev), "seg": lb.Segments(wq.T, wq.num_adapters, dev)}
+        st["tables"] = [lb.AdapterTable([dev_e(a) for a in w.A], [dev_e(b) for b in w.B], w.scales.tolist())
+                        for w in wls]
+        st["ys"] = [dev_e(w.y0) for w in wls]
+        st["vs"] = [torch.zeros((wq.T, 16), dtype=torch.float32, device=dev) for _ in wls]
+        st["ws"] = torch.empty(lb.lora_shrink_workspace_bytes(torch.bfloat16, wq.T, wq.d_in, 16), dtype=torch.uint8,
+                               device=dev)
+        sets.append(st)
+
+    def split(st):
+        for t, y, v in zip(st["tables"], st["ys"], st["vs"]):
+            lb.lora_shrink(st["x"], t, st["seg"], v=v, ws=st["ws"])
+            lb.lora_expand_add(v, t, st["seg"], y)
+
+    def fused3(st):
+        for t, y, v in zip(st["tables"], st["ys"], st["vs"]):
+            lb.lora_forward(st["x"], t, st["seg"], y, v=v)
+
+    def multi(st):
+        lb.lora_forward_multi(st["x"], list(zip(st["tables"], st["ys"], st["vs"])), st["seg"])
+
+    alg = sum(algorithmic(w)["forward_fused"]["bytes"] for w in wls) - 2 * 2 * int((wq.ids >= 0).sum()) * wq.d_in  # x read once
+    for name, fwd in (("split x3", split), ("lora_forward x3", fused3), ("lora_forward_multi", multi)):
+        def step(st):
+            lb.lora_segments_build(st["ids"], wq.num_adapters, out=st["seg"])
+            fwd(st)
+        for i in range(warmup):
+            step(sets[i % n_sets])
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(sets[i % n_sets])
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        print(json.dumps({"multi_slice": name, "workload": "decode-64x-r16-4096 q/k/v (d_out 4096/1024/1024)",
+                          "rows": wq.T, "ms_per_step": ms, "rows_per_s": wq.T / (ms * 1e-3),
+                          "forward_algorithmic_bytes": alg, "steps": steps}), flush=True)
+
+
 def cost_model_report(reps: int = 10):
     """Fit the cost model on synthetic calibration batches, then predict the workloads' calls."""
     import torch
@@ -291,6 +345,9 @@ def main():
         return
     if args.cost_model:
         cost_model_report()
+        return
+    if args.multi_slice:
+        multi_slice_report(args.steps, args.warmup, args.sets)
         return
     if args.traffic_from:
         traffic_from(*args.traffic_from)

@@ -24,7 +24,7 @@ from ._abi import LORA_BF16, LORA_F32, LORA_MAX_RANK, LoraError
 __all__ = [
     "AdapterTable", "GradTable", "Segments", "LoraError",
     "lora_segments_build", "lora_segments_build_batch", "lora_shrink", "lora_expand_add", "lora_forward",
-    "lora_backward", "lora_backward_preemptible", "lora_adamw_step",
+    "lora_forward_multi", "lora_backward", "lora_backward_preemptible", "lora_adamw_step",
     "lora_abi_version", "lora_status_string",
     "lora_segments_workspace_bytes", "lora_shrink_workspace_bytes", "lora_backward_workspace_bytes",
     "lora_segments_sched_elems",
@@ -269,6 +269,38 @@ def lora_forward(x: torch.Tensor, adapters: AdapterTable, seg: Segments, y: torc
                                   seg.c, py, ldy, pv or None, ldv, _stream(x.device))
     _abi.check("lora_forward", st)
     return y
+
+
+def lora_forward_multi(x: torch.Tensor, slices, seg: Segments, r_max: Optional[int] = None) -> None:
+    """Several projections of the same x in one launch: slices = [(adapters, y[, v]), ...] (1..3 entries).
+
+    For every slice, y[t] += s_a B_a A_a x[t] with that slice's adapter table (same adapter ids).
+    """
+    entries = [tuple(e) + (None,) * (3 - len(e)) for e in slices]
+    if not 1 <= len(entries) <= _abi.LORA_MAX_SLICES:
+        raise ValueError(f"1 to {_abi.LORA_MAX_SLICES} slices")
+    _on_gpu(x)
+    px, T, d_in, ldx = _rows(x, "x")
+    arr = (_abi.LoraSlice * len(entries))()
+    n_adapters = len(entries[0][0])
+    for i, (table, y, v) in enumerate(entries):
+        _on_gpu(y, v)
+        py, Ty, d_out, ldy = _rows(y, "y")
+        if Ty != T or y.dtype != x.dtype:
+            raise ValueError("every y must have x's rows and element type")
+        if len(table) != n_adapters:
+            raise ValueError("every slice's adapter table must have the same number of entries")
+        pv, ldv = 0, 0
+        if v is not None:
+            pv, Tv, _, ldv = _rows(v, "v")
+            if Tv != T or v.dtype != torch.float32:
+                raise ValueError("v must be fp32 with one row per row of x")
+        arr[i] = _abi.LoraSlice(table.ptr, py, ldy, pv or None, ldv, d_out, 0)
+    if r_max is None:
+        r_max = max(e[0].r_max for e in entries)
+    st = _abi.load().lora_forward_multi(_dtype_code(x), px, ldx, T, d_in, arr, len(entries), n_adapters, r_max,
+                                        seg.c, _stream(x.device))
+    _abi.check("lora_forward_multi", st)
 
 
 def lora_backward(x: torch.Tensor, dy: torch.Tensor, adapters: AdapterTable, grads: GradTable, seg_ft: Segments,

@@ -53,6 +53,14 @@ class LoraAdamwParams(ctypes.Structure):
 LORA_ADAMW_MAX_TENSORS = 32
 
 
+class LoraSlice(ctypes.Structure):
+    _fields_ = [("adapters", _vp), ("y", _vp), ("ldy", _i64), ("v", _vp), ("ldv", _i64), ("d_out", _i32),
+                ("reserved", _i32)]
+
+
+LORA_MAX_SLICES = 3
+
+
 class LoraSegmentsJob(ctypes.Structure):
     _fields_ = [("adapter_ids", _vp), ("T", _i32), ("seg", LoraSegments), ("ws", _vp), ("ws_bytes", _sz)]
 
@@ -72,6 +80,8 @@ SIGNATURES = {
                                        _vp, _i64, _vp]),
     "lora_forward": (ctypes.c_int, [ctypes.c_int, _vp, _i64, _i32, _i32, _i32, _vp, _i32, _i32, LoraSegments,
                                     _vp, _i64, _vp, _i64, _vp]),
+    "lora_forward_multi": (ctypes.c_int, [ctypes.c_int, _vp, _i64, _i32, _i32, _vp, _i32, _i32, _i32, LoraSegments,
+                                          _vp]),
     "lora_adamw_step": (ctypes.c_int, [ctypes.c_int, _vp, _i32, LoraAdamwParams, _vp]),
     "lora_backward": (ctypes.c_int, [ctypes.c_int, _vp, _i64, _vp, _i64, _vp, _i64, _i32, _i32, _i32, _vp,
                                      _vp, _i32, _i32, LoraSegments, _vp, _i64, _vp, _sz, _vp]),

@@ -10,14 +10,12 @@
 #include "host_checks.h"
 #include "shrink.h"
 #include "expand.h"
-#include "fused.h"
 
 using namespace lora;
 
 namespace {
 
 constexpr int64_t kMaxGrid = 8192;
-constexpr int64_t kNumCus = 256;  // MI355X compute units
 constexpr int64_t kShrinkMaxGrid = 1024;
 
 template <int DT>
@@ -252,51 +250,3 @@ extern "C" int lora_expand_add(int dtype, const float* v, int64_t ldv, int32_t T
     return run_expand(dtype, false, p, T, num_adapters, r_max, static_cast<hipStream_t>(stream));
 }
 
-extern "C" int lora_forward(int dtype, const void* x, int64_t ldx, int32_t T, int32_t d_in, int32_t d_out,
-                            const lora_adapter* adapters, int32_t num_adapters, int32_t r_max, lora_segments seg,
-                            void* y, int64_t ldy, float* v, int64_t ldv, void* stream) {
-    int rc = check_common(dtype, T, num_adapters, r_max, adapters, seg);
-    if (rc != LORA_OK) return rc;
-    if (d_in < 1 || d_out < 1) return LORA_ERR_INVALID_ARG;
-    if (T == 0) return LORA_OK;
-    if ((rc = check_matrix(x, d_in, ldx)) != LORA_OK) return rc;
-    if ((rc = check_matrix(y, d_out, ldy)) != LORA_OK) return rc;
-    if (v && (rc = check_f32_rows(v, ldv, r_max)) != LORA_OK) return rc;
-    FusedParams p{};
-    p.x = x;
-    p.ldx = ldx;
-    p.K = d_in;
-    p.adapters = adapters;
-    p.r_max = r_max;
-    p.perm = seg.perm;
-    p.sched = seg.sched;
-    p.tiles64_off = SchedLayout::make(T, num_adapters).tiles64;
-    p.y = y;
-    p.ldy = ldy;
-    p.N = d_out;
-    p.v = v;
-    p.ldv = ldv;
-    p.err = seg.err;
-    // column ranges per tile: enough tasks for one per CU (each range
-    // recomputes v; at most one range per eight 64-column chunks)
-    const int64_t max_tiles = SchedLayout::max_tiles64(T, num_adapters);
-    const int64_t nch = (d_out + 63) / 64;
-    p.nsplit = (int32_t)std::max<int64_t>(1, std::min<int64_t>(kNumCus / max_tiles, std::max<int64_t>(1, nch / 8)));
-    const unsigned grid = grid_for(max_tiles * p.nsplit, 1, kMaxGrid);
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    const dim3 block(kFusedThreads);
-    // 16-rank blocks: 1 (r_max <= 16), 2, 4 or 8
-    const int nmb = r_max <= 16 ? 1 : (r_max <= 32 ? 2 : (r_max <= 64 ? 4 : 8));
-    if (dtype == LORA_BF16) {
-        if (nmb == 1) hipLaunchKernelGGL((fused_forward_kernel<LORA_BF16, 1, 1>), dim3(grid), block, 0, st, p);
-        else if (nmb == 2) hipLaunchKernelGGL((fused_forward_kernel<LORA_BF16, 1, 2>), dim3(grid), block, 0, st, p);
-        else if (nmb == 4) hipLaunchKernelGGL((fused_forward_kernel<LORA_BF16, 2, 4>), dim3(grid), block, 0, st, p);
-        else hipLaunchKernelGGL((fused_forward_kernel<LORA_BF16, 4, 8>), dim3(grid), block, 0, st, p);
-    } else {
-        if (nmb == 1) hipLaunchKernelGGL((fused_forward_kernel<LORA_F32, 1, 1>), dim3(grid), block, 0, st, p);
-        else if (nmb == 2) hipLaunchKernelGGL((fused_forward_kernel<LORA_F32, 1, 2>), dim3(grid), block, 0, st, p);
-        else if (nmb == 4) hipLaunchKernelGGL((fused_forward_kernel<LORA_F32, 2, 4>), dim3(grid), block, 0, st, p);
-        else hipLaunchKernelGGL((fused_forward_kernel<LORA_F32, 4, 8>), dim3(grid), block, 0, st, p);
-    }
-    return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
-}

@@ -232,6 +232,42 @@ int lora_forward(int dtype, const void* x, int64_t ldx, int32_t T, int32_t d_in,
                  void* y, int64_t ldy, float* v, int64_t ldv, void* stream);
 
 /*
+ * Multi-slice fused forward: several projections that read the same x, each
+ * with its own adapters, in one launch.  DeltaServe (section 4.1) adapts all
+ * attention projections of a layer; the q, k and v projections (or the gate
+ * and up projections of an MLP) read one input, so x is read once per tile for
+ * all of them and v = A x of every slice stays in LDS.  For each slice q and
+ * each row t with adapter a = a(t) (the same adapter index in every slice):
+ *     y_q[t] += s_{q,a} B_{q,a} (A_{q,a} x_t),
+ * exactly what lora_forward computes for that slice alone.
+ *   slices: HOST array of n_slices (1..LORA_MAX_SLICES) entries:
+ *     adapters  device table [num_adapters] of the slice (A [r, d_in],
+ *               B [d_out, r]; ranks may differ between slices);
+ *     y [T, ldy] in/out (dtype) with d_out columns; v optional as in
+ *     lora_forward; d_out >= 1; reserved must be 0.
+ *   r_max: the largest rank over every slice's adapters.
+ * Errors as for lora_forward; LORA_ERR_UNSUPPORTED for n_slices > 1 with
+ * r_max > 64 (the slices' v rows and fragments would not fit the LDS).
+ * Bad table entries are counted in seg.err once per slice and tile, and only
+ * that slice's rows are skipped.
+ */
+#define LORA_MAX_SLICES 3
+
+typedef struct {
+    const lora_adapter* adapters;
+    void* y;
+    int64_t ldy;
+    float* v;
+    int64_t ldv;
+    int32_t d_out;
+    int32_t reserved;
+} lora_slice;
+
+int lora_forward_multi(int dtype, const void* x, int64_t ldx, int32_t T, int32_t d_in,
+                       const lora_slice* slices, int32_t n_slices, int32_t num_adapters, int32_t r_max,
+                       lora_segments seg, void* stream);
+
+/*
  * LoRA backward over T_ft fine-tuning rows (DeltaServe, section 3.2: the
  * backward computes the LoRA gradients from the saved layer input).
  *   x  [T_ft, ldx]  layer input of the fine-tuning rows (dtype)

@@ -53,8 +53,8 @@ def test_struct_layouts_match_header_compiled_by_gcc(tmp_path):
 #include <stddef.h>
 #include "lora_batch.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu\\n", sizeof(lora_adapter), sizeof(lora_adapter_grad), sizeof(lora_segments),
-         sizeof(lora_segments_job), sizeof(lora_adamw_tensor), sizeof(lora_adamw_params));
+  printf("%zu %zu %zu %zu %zu %zu %zu\\n", sizeof(lora_adapter), sizeof(lora_adapter_grad), sizeof(lora_segments),
+         sizeof(lora_segments_job), sizeof(lora_adamw_tensor), sizeof(lora_adamw_params), sizeof(lora_slice));
   printf("%zu %zu %zu %zu\\n", offsetof(lora_adamw_tensor, n), offsetof(lora_adamw_params, step),
          offsetof(lora_adamw_params, zero_grad), offsetof(lora_segments_job, ws_bytes));
   return 0;
@@ -65,11 +65,34 @@ int main(void) {
     subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(probe), "-o", str(exe)], check=True)
     out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()
     sizes = [int(v) for v in out]
-    assert sizes[:6] == [ctypes.sizeof(t) for t in (_abi.LoraAdapter, _abi.LoraAdapterGrad, _abi.LoraSegments,
+    assert sizes[:7] == [ctypes.sizeof(t) for t in (_abi.LoraAdapter, _abi.LoraAdapterGrad, _abi.LoraSegments,
                                                       _abi.LoraSegmentsJob, _abi.LoraAdamwTensor,
-                                                      _abi.LoraAdamwParams)]
-    assert sizes[6:] == [_abi.LoraAdamwTensor.n.offset, _abi.LoraAdamwParams.step.offset,
+                                                      _abi.LoraAdamwParams, _abi.LoraSlice)]
+    assert sizes[7:] == [_abi.LoraAdamwTensor.n.offset, _abi.LoraAdamwParams.step.offset,
                          _abi.LoraAdamwParams.zero_grad.offset, _abi.LoraSegmentsJob.ws_bytes.offset]
+
+
+def test_forward_multi_rejects(lib):
+    bad, uns = _abi.LORA_ERR_INVALID_ARG, _abi.LORA_ERR_UNSUPPORTED
+
+    def sl(adapters=FAKE, y=FAKE, ldy=512, v=None, ldv=0, d_out=512, reserved=0):
+        return _abi.LoraSlice(adapters, y, ldy, v, ldv, d_out, reserved)
+
+    def call(*slices, n=None, r_max=16, T=10, A=4, seg=None):
+        arr = (_abi.LoraSlice * max(1, len(slices)))(*slices)
+        return lib.lora_forward_multi(0, FAKE, 256, T, 256, arr, len(slices) if n is None else n, A, r_max,
+                                      seg or _seg(), None)
+
+    assert call(sl(), n=0) == bad and call(sl(), sl(), sl(), sl()) == bad      # 1..3 slices
+    assert lib.lora_forward_multi(0, FAKE, 256, 10, 256, None, 1, 4, 16, _seg(), None) == bad
+    assert call(sl(), sl(adapters=None)) == bad and call(sl(), sl(adapters=FAKE + 4)) == bad
+    assert call(sl(), sl(d_out=0)) == bad and call(sl(reserved=1)) == bad
+    assert call(sl(), sl(y=None)) == bad and call(sl(), sl(ldy=256)) == bad
+    assert call(sl(), sl(d_out=260, ldy=264)) == uns                          # d_out not a multiple of 8
+    assert call(sl(), sl(v=FAKE, ldv=8)) == bad                               # ldv < r_max
+    assert call(sl(), sl(), r_max=72) == uns                                  # several slices above rank 64
+    assert call(sl(), r_max=129) == bad and call(sl(), seg=_seg(False)) == bad
+    assert call(sl(y=None), sl(y=None), T=0) == 0                             # nothing to do
 
 
 def test_backward_preemptible_rejects(lib):
