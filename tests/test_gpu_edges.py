@@ -1,0 +1,87 @@
+"""GPU parity on degenerate shapes: d_in = 8 (less than one K chunk),
+d_out = 24 (less than one 64-column block), rank 1 and odd ranks, a single
+row, and batches whose rows have no adapter.  Every entry point is checked
+against the fp64 oracle (bf16: 2e-2 * max|ref|, fp32: 1e-5 * max|ref|)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import expand_token_adapter_amd as lb
+    from gpu_helpers import TOL, GpuCase, rel_err, to_dev
+
+
+def _case(ids, ranks, d_in, d_out, dtype, ft=(0, 0), seed=0):
+    return workloads.custom(np.asarray(ids, np.int32), ranks, d_in, d_out, dtype, seed=seed,
+                            ft_start=ft[0], ft_count=ft[1], name="edge")
+
+
+SHAPES = [
+    # ids, ranks, d_in, d_out
+    ([0, 1, 1, -1, 2], [1, 3, 16], 8, 24),
+    ([2], [5, 8, 1], 40, 8),
+    ([0] * 70 + [1] * 3, [1, 7], 16, 136),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", range(len(SHAPES)))
+def test_forward_paths_on_degenerate_shapes(shape, dtype):
+    ids, ranks, d_in, d_out = SHAPES[shape]
+    wl = _case(ids, ranks, d_in, d_out, dtype)
+    c = GpuCase(wl)
+    y_ref, v_ref = c.oracle_forward()
+    for fused in (False, True):
+        y, v, seg = c.forward(fused=fused)
+        assert seg.err.item() == 0
+        assert rel_err(y, y_ref) <= TOL[dtype], fused
+    # the multi-slice form with the same projection twice
+    y1, y2 = c.y0.clone(), c.y0.clone()
+    seg = lb.lora_segments_build(c.ids, wl.num_adapters)
+    lb.lora_forward_multi(c.x, [(c.table, y1), (c.table, y2)], seg)
+    torch.cuda.synchronize()
+    assert rel_err(y1, y_ref) <= TOL[dtype] and torch.equal(y1, y2)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", range(len(SHAPES)))
+def test_backward_on_degenerate_shapes(shape, dtype):
+    ids, ranks, d_in, d_out = SHAPES[shape]
+    n = len(ids)
+    ids_ft = [max(i, 0) for i in ids]  # every fine-tuning row has an adapter
+    wl = _case(ids_ft, ranks, d_in, d_out, dtype, ft=(0, n))
+    c = GpuCase(wl)
+    dx, dA, dB, seg_ft = c.backward()
+    assert seg_ft.err.item() == 0
+    dx_r, dA_r, dB_r, _, _ = c.oracle_backward()
+    assert rel_err(dx, dx_r) <= TOL[dtype]
+    used = sorted(set(ids_ft))
+    for a in used:
+        assert rel_err(dA[a], dA_r[a]) <= TOL[dtype], a
+        assert rel_err(dB[a], dB_r[a]) <= TOL[dtype], a
+    for a in set(range(len(ranks))) - set(used):
+        assert not dA[a].any().item() and not dB[a].any().item()
+
+
+def test_rows_without_adapters_are_left_alone():
+    wl = _case([-1] * 37, [8, 16], 64, 72, "bf16")
+    c = GpuCase(wl)
+    for fused in (False, True):
+        y, v, seg = c.forward(fused=fused)
+        assert torch.equal(y, c.y0), fused
+        assert seg.err.item() == 0
+    # a preemptible backward over rows of one adapter with a 1-row batch
+    wl1 = _case([1], [8, 16], 64, 72, "f32", ft=(0, 1))
+    c1 = GpuCase(wl1)
+    grant = torch.ones(1, dtype=torch.int32, device="cuda:0")
+    status = torch.full((1,), 7, dtype=torch.int32, device="cuda:0")
+    dx, dA, dB, _ = c1.backward(grant=grant, status=status)
+    dx_r, dA_r, dB_r, _, _ = c1.oracle_backward()
+    assert status.item() == 0
+    assert rel_err(dx, dx_r) <= TOL["f32"] and rel_err(dA[1], dA_r[1]) <= TOL["f32"]
+    assert rel_err(dB[1], dB_r[1]) <= TOL["f32"]
