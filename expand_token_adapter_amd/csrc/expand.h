@@ -51,6 +51,34 @@ struct ExpandParams {
     const int32_t* stop;
 };
 
+// Raw element type of the weights read element by element, and the fragment
+// of 8 such elements (elements n .. 7 zeroed).
+template <int DT>
+struct GatherElem;
+template <>
+struct GatherElem<LORA_BF16> {
+    using type = uint16_t;
+    __device__ __forceinline__ static Frag<LORA_BF16> frag(const uint32_t (&h)[8], int n) {
+        u32x4_t q;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) q[j] = (2 * j < n ? h[2 * j] : 0u) | ((2 * j + 1 < n ? h[2 * j + 1] : 0u) << 16);
+        return Frag<LORA_BF16>{q};
+    }
+};
+template <>
+struct GatherElem<LORA_F32> {
+    using type = uint32_t;
+    __device__ __forceinline__ static Frag<LORA_F32> frag(const uint32_t (&h)[8], int n) {
+        u32x4_t a, b;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            a[j] = j < n ? h[j] : 0u;
+            b[j] = j + 4 < n ? h[j + 4] : 0u;
+        }
+        return Frag<LORA_F32>{a, b};
+    }
+};
+
 // The kernel's work as workgroup blk of nblk (nblk a multiple of 8, the
 // workgroup at launch index blk), so that another kernel can run it on part
 // of its grid.
@@ -119,7 +147,8 @@ __device__ __forceinline__ void expand_body(const ExpandParams& p, int blk, int 
                     wf[mb][ks] = ok ? w : F::zero();
                 }
             }
-        } else {
+        } else if constexpr (!TRANS_W) {
+            // rows of B_a not in whole 16-byte units (rare): element by element
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb) {
                 const int col = c0 + 16 * mb + lr;
@@ -127,13 +156,37 @@ __device__ __forceinline__ void expand_body(const ExpandParams& p, int blk, int 
                 for (int ks = 0; ks < KS; ++ks) {
                     const int kk = 32 * ks + 8 * lg;
                     const int nval = (col < p.N) ? max(0, min(8, r - kk)) : 0;
-                    if (TRANS_W)
-                        wf[mb][ks] = F::load_strided(wbase + ((int64_t)(nval ? kk : 0) * p.N + (nval ? col : 0)) * EB,
-                                                     p.N, nval);
-                    else
-                        wf[mb][ks] = F::load_strided(wbase + (nval ? (int64_t)col * r + kk : 0) * EB, 1, nval);
+                    wf[mb][ks] = F::load_strided(wbase + (nval ? (int64_t)col * r + kk : 0) * EB, 1, nval);
                 }
             }
+        } else {
+            // A_a read transposed, element by element: every element load of
+            // the block is issued before any is packed, with clamped indices
+            // and no branches (a conditional load is waited for where its
+            // branch joins, which made this one round trip per pair of
+            // elements).
+            using ET = typename GatherElem<DT>::type;
+            const int64_t stride = p.N;
+            uint32_t h[4][KS][8];
+            int nv[4][KS];
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) {
+                const int col = c0 + 16 * mb + lr;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int kk = 32 * ks + 8 * lg;
+                    const int nval = (col < p.N) ? max(0, min(8, r - kk)) : 0;
+                    nv[mb][ks] = nval;
+                    const int64_t e0 = nval ? (int64_t)kk * p.N + col : 0;
+                    const LORA_GLOBAL ET* src = gptr(reinterpret_cast<const ET*>(wbase)) + e0;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) h[mb][ks][i] = src[(i < nval ? i : 0) * stride];
+                }
+            }
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) wf[mb][ks] = GatherElem<DT>::frag(h[mb][ks], nv[mb][ks]);
         }
         if (threadIdx.x < ROWS) s_row[threadIdx.x] = my_row;
         __syncthreads();
