@@ -455,19 +455,26 @@ __device__ __forceinline__ void contract_fixup_body(const ContractParams& p, int
         const int c0 = (is_dA ? cb_all : cb_all - p.ncb_in) * 64;
         const int N = is_dA ? p.d_in : p.d_out;
         const int col = c0 + 16 * nb + lr;
+        // read-modify-write of dA / dB: every load issued before any add
+        // (clamped addresses, unconditional), the stores masked
+        float old[kContractMB][4];
+        float* dst[kContractMB][4];
+        bool ok[kContractMB][4];
 #pragma unroll
-        for (int mb = 0; mb < kContractMB; ++mb) {
-            if (mb < nmb) {
+        for (int mb = 0; mb < kContractMB; ++mb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int rk = rank0 + 16 * mb + 4 * lg + i;
-                    if (col < N && rk < r) {
-                        float* dst = is_dA ? gr.dA + (int64_t)rk * p.d_in + col : gr.dB + (int64_t)col * r + rk;
-                        *gptr(dst) += ad.scale * sum[mb][i];
-                    }
-                }
+            for (int i = 0; i < 4; ++i) {
+                const int rk = rank0 + 16 * mb + 4 * lg + i;
+                ok[mb][i] = mb < nmb && col < N && rk < r;
+                const int rk_ = ok[mb][i] ? rk : 0, col_ = ok[mb][i] ? col : 0;
+                dst[mb][i] = is_dA ? gr.dA + (int64_t)rk_ * p.d_in + col_ : gr.dB + (int64_t)col_ * r + rk_;
+                old[mb][i] = *gptr(dst[mb][i]);
             }
-        }
+#pragma unroll
+        for (int mb = 0; mb < kContractMB; ++mb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (ok[mb][i]) *gptr(dst[mb][i]) = old[mb][i] + ad.scale * sum[mb][i];
     }
 }
 

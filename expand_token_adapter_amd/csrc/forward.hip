@@ -49,10 +49,14 @@ namespace lora {
 // all its loads in flight, and wave 0 adds the four wave sums in wave order,
 // so the result does not depend on timing.
 constexpr int kReduceWaves = 4;
-constexpr int kReduceJ = LORA_MAX_RANK / 16;
 
+// NJ: 16-rank blocks covered (16 NJ >= r_max).  Every partial is loaded
+// unconditionally (quads at or past r read quad 0 of the row, which exists,
+// and are dropped where they are added): conditional loads are waited for one
+// at a time, these are all in flight together.
+template <int NJ>
 __global__ __launch_bounds__(kReduceWaves * kWave) void shrink_reduce_kernel(ReduceParams p) {
-    __shared__ f32x4_t s_acc[kReduceWaves - 1][kReduceJ][kWave];
+    __shared__ f32x4_t s_acc[kReduceWaves - 1][NJ][kWave];
     if (p.stop && *p.stop) return;
     const int wave = wave_id();
     const int lane = threadIdx.x & (kWave - 1);
@@ -71,41 +75,53 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void shrink_reduce_kernel(Red
         const int pos = rec.pos0 + (row_ok ? n : 0);
         const int64_t orow = wave == 0 && p.out && !p.out_by_pos ? p.perm[pos] : pos;
         const int64_t vrow = wave == 1 && p.vsrc ? p.perm[pos] : 0;
-        // quads at or past r hold no partial (and may lie past the workspace): not read
-        const float* src = p.part + (int64_t)pos * p.ldp + 4 * q;
-        f32x4_t acc[kReduceJ];
+        const float* src = p.part + (int64_t)pos * p.ldp;
+        bool qok[NJ];
+        int qoff[NJ];
 #pragma unroll
-        for (int j = 0; j < kReduceJ; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
+        for (int j = 0; j < NJ; ++j) {
+            qok[j] = 16 * j + 4 * q < r;
+            qoff[j] = qok[j] ? 16 * j + 4 * q : 0;
+        }
+        f32x4_t acc[NJ];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll(NJ <= 4 ? 2 : 1)
         for (int sl = s0; sl < s1; ++sl) {
+            f32x4_t part[NJ];
 #pragma unroll
-            for (int j = 0; j < kReduceJ; ++j)
-                if (j < nj && 16 * j + 4 * q < r)
-                    acc[j] += *gptr(reinterpret_cast<const f32x4_t*>(src + (int64_t)sl * p.slice_stride + 16 * j));
+            for (int j = 0; j < NJ; ++j)
+                part[j] = *gptr(reinterpret_cast<const f32x4_t*>(src + (int64_t)sl * p.slice_stride + qoff[j]));
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+                if (qok[j]) acc[j] += part[j];
         }
         if (wave > 0) {
 #pragma unroll
-            for (int j = 0; j < kReduceJ; ++j)
+            for (int j = 0; j < NJ; ++j)
                 if (j < nj) s_acc[wave - 1][j][lane] = acc[j];
         }
         lds_barrier();
         if (wave == 1 && p.vsrc && row_ok) {
             // rank-major copy of the caller's v rows of this tile (quads below
             // round_up(r, 4) <= the caller's pitch)
+            f32x4_t vv[NJ];
 #pragma unroll
-            for (int j = 0; j < kReduceJ; ++j) {
+            for (int j = 0; j < NJ; ++j)
+                vv[j] = *gptr(reinterpret_cast<const f32x4_t*>(p.vsrc + vrow * p.ldvsrc + qoff[j]));
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
                 const int k = 16 * j + 4 * q;
-                if (j < nj && k < r) {
-                    const f32x4_t vv = *gptr(reinterpret_cast<const f32x4_t*>(p.vsrc + vrow * p.ldvsrc + k));
+                if (qok[j]) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        if (k + i < r) gptr(p.vT)[(int64_t)(k + i) * p.ldT + pos] = vv[i];
+                        if (k + i < r) gptr(p.vT)[(int64_t)(k + i) * p.ldT + pos] = vv[j][i];
                 }
             }
         }
         if (wave == 0 && row_ok) {
 #pragma unroll
-            for (int j = 0; j < kReduceJ; ++j) {
+            for (int j = 0; j < NJ; ++j) {
                 if (j < nj) {
                     f32x4_t sum = acc[j];
 #pragma unroll
@@ -141,7 +157,15 @@ int run_shrink(int dtype, bool trans_w, const ShrinkParams& p, const ReduceParam
                                       : launch_shrink_t<LORA_F32>(trans_w, p, grid, st);
     if (rc != LORA_OK) return rc;
     const unsigned rgrid = (unsigned)std::min<int64_t>(SchedLayout::max_tiles16(T, num_adapters), kMaxGrid);
-    hipLaunchKernelGGL(shrink_reduce_kernel, dim3(rgrid), dim3(kReduceWaves * kWave), 0, st, rp);
+    const dim3 rb(kReduceWaves * kWave);
+    if (rp.r_max <= 16)
+        hipLaunchKernelGGL(shrink_reduce_kernel<1>, dim3(rgrid), rb, 0, st, rp);
+    else if (rp.r_max <= 32)
+        hipLaunchKernelGGL(shrink_reduce_kernel<2>, dim3(rgrid), rb, 0, st, rp);
+    else if (rp.r_max <= 64)
+        hipLaunchKernelGGL(shrink_reduce_kernel<4>, dim3(rgrid), rb, 0, st, rp);
+    else
+        hipLaunchKernelGGL(shrink_reduce_kernel<8>, dim3(rgrid), rb, 0, st, rp);
     return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
