@@ -8,17 +8,21 @@
 // the work is the weights A_a and B_a plus launch latency, and a workgroup can
 // carry a tile from x to y.  A task = (64-row tile, one of `nsplit` column
 // ranges of d_out):
-//   phase 1  v = A_a x for the tile's rows and ranks (up to 32 KS).  The waves
-//            cover the tile's 16-row blocks (1, 2 or 4 of them) times equal
-//            parts of d_in (8, 4 or 2), with several 32-element K chunks in
-//            flight; the parts are added in order through LDS.  v stays in
+//   phase 1  v = A_a x for the tile's rows and ranks (16 NMB of them).  The
+//            waves cover the tile's 16-row blocks (1, 2 or 4 of them) times
+//            equal parts of d_in (8, 4 or 2), with several 32-element K chunks
+//            in flight; the parts are added in order through LDS.  v stays in
 //            LDS (the task of column range 0 also writes it out on request).
 //            Each task of a tile computes v itself: A_a is read once per
-//            column range (from L2 after the first).
-//   phase 2  the waves walk the range's 64-column chunks: weight block and y
-//            rows of the next chunk in flight while the current chunk's MFMA
-//            tiles (16 columns x 16 rows, v as hi/lo bf16 fragments) are added
-//            to y in fp32 and rounded once.
+//            column range (from L2 after the first).  The weight block and y
+//            rows of the task's first output chunk are requested before phase
+//            1 starts: they do not depend on v.
+//   phase 2  the waves walk the range's 64-column chunks (up to 32 KS ranks):
+//            for bf16 with KS <= 2 the next chunk's weight block (and, for
+//            KS = 1 and at most two slices, its y rows) is in flight while
+//            the current chunk's MFMA
+//            tiles (16 columns x 16 rows, v as hi/lo bf16 fragments) are
+//            added to y in fp32 and rounded once.
 // Several projections that read the same x (multi-slice: e.g. the q, k and v
 // projections, each with its own adapters; DeltaServe section 4.1 adapts all
 // attention projections) go through one launch: phase 1 multiplies each x
