@@ -20,9 +20,8 @@
 //   phase 2  the waves walk the range's 64-column chunks (up to 32 KS ranks):
 //            for bf16 with KS <= 2 the next chunk's weight block (and, for
 //            KS = 1 and at most two slices, its y rows) is in flight while
-//            the current chunk's MFMA
-//            tiles (16 columns x 16 rows, v as hi/lo bf16 fragments) are
-//            added to y in fp32 and rounded once.
+//            the current chunk's MFMA tiles (16 columns x 16 rows, v as hi/lo
+//            bf16 fragments) are added to y in fp32 and rounded once.
 // Several projections that read the same x (multi-slice: e.g. the q, k and v
 // projections, each with its own adapters; DeltaServe section 4.1 adapts all
 // attention projections) go through one launch: phase 1 multiplies each x
