@@ -57,6 +57,27 @@ def test_segments_bit_exact(kind, T, A):
     n = int(offsets[-1])
     assert np.array_equal(seg.perm.cpu().numpy()[:n], perm)
     assert int(seg.err.item()) == err
+    _check_tile_records(seg.sched.cpu().numpy(), counts, offsets, T, A)
+
+
+def _check_tile_records(sched, counts, offsets, T, A):
+    """The scheduling records the compute kernels walk, bit for bit: a header
+    (16-row tiles, 64-row tiles, active adapters), the active adapters in
+    ascending order, then per active adapter its rows in runs of 16 and of 64
+    consecutive sorted positions, as (adapter, first position, rows)."""
+    active = [a for a in range(A) if counts[a] > 0]
+
+    def tiles(n):
+        return [(a, int(offsets[a]) + j, min(n, int(counts[a]) - j)) for a in active for j in range(0, counts[a], n)]
+
+    t16, t64 = tiles(16), tiles(64)
+    assert list(sched[:3]) == [len(t16), len(t64), len(active)]
+    off16 = 4 + (A + 3) // 4 * 4
+    off64 = off16 + 4 * ((T + 15) // 16 + A)
+    assert list(sched[4:4 + len(active)]) == active
+    for off, want in ((off16, t16), (off64, t64)):
+        got = sched[off:off + 4 * len(want)].reshape(-1, 4)[:, :3]
+        assert np.array_equal(got, np.array(want, dtype=np.int64).reshape(-1, 3)), off
 
 
 def test_segments_build_batch_matches_single_builds():
@@ -83,6 +104,7 @@ def test_segments_build_batch_matches_single_builds():
         assert np.array_equal(one.perm.cpu().numpy()[:n], perm)
         if len(c):
             assert int(b.err.item()) == err
+            _check_tile_records(b.sched.cpu().numpy(), counts, offsets, len(c), A)
 
 
 def _check_forward(case, tol, fused=False):
