@@ -332,8 +332,8 @@ def cost_model_report(reps: int = 10):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
-              "the multi-GPU layout is described in DESIGN.md and not built", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the hot path runs on "
+              "one GPU's share of the batch and no multi-GPU sharding is built", file=sys.stderr)
         sys.exit(2)
     if args.adamw and args.graph:
         # the step count (bias corrections) is a launch argument: a captured
