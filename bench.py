@@ -414,7 +414,11 @@ def main():
         lb.lora_backward(st["x"][s:s + n], st["dy"], st["table"], st["grads"], st["seg_ft"], dx=st["dx"],
                          v_saved=v_saved, ws=st["ws"])
 
-    def step(st, ev=None):
+    def step(st, ev=None, ph=None):
+        # ph: events recorded at the start, after the segment build, after the
+        # forward and at the end of the step (the timing-distribution pass)
+        if ph is not None:
+            ph[0].record()
         if side is not None and has_ft:
             side.wait_stream(torch.cuda.current_stream(dev))
             with torch.cuda.stream(side):
@@ -425,6 +429,8 @@ def main():
             lb.lora_segments_build_batch([(st["ids"], st["seg"]), (st["ft_ids"], st["seg_ft"])], wl.num_adapters)
         else:
             lb.lora_segments_build(st["ids"], wl.num_adapters, out=st["seg"])
+        if ph is not None:
+            ph[1].record()
         if args.fused:
             if ev is not None:
                 ev[0].record()
@@ -438,6 +444,8 @@ def main():
             lb.lora_expand_add(st["v"], st["table"], st["seg"], st["y"])
             if ev is not None:
                 ev[1].record()
+        if ph is not None:
+            ph[2].record()
         if side is not None and has_ft:
             torch.cuda.current_stream(dev).wait_stream(side)
         elif has_ft:
@@ -449,6 +457,8 @@ def main():
             lb.lora_adamw_step(st["opt"], step=st["opt_step"], zero_grad=True)
             if ev is not None:
                 ev[3].record()
+        if ph is not None:
+            ph[3].record()
 
     graphs = None
     if args.graph:
@@ -513,6 +523,35 @@ def main():
         torch.cuda.synchronize()
         kern_ms = e0.elapsed_time(e1) / K
         kern_how = "events around back-to-back launches"
+    # Distribution of step times, outside the timed region above: a second
+    # pass of K steps with events at the start, after the segment build, after
+    # the forward and at the end of every step.
+    dist = None
+    if graphs is None:
+        phs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(K)]
+        for i in range(K):
+            step(sets[(args.warmup + K + i) % len(sets)], None, phs[i])
+        torch.cuda.synchronize()
+        pct = lambda a: {"p10": float(np.percentile(a, 10)), "median": float(np.median(a)),
+                         "p90": float(np.percentile(a, 90))}
+        dist = {"steps": K, "step_ms": pct([e[0].elapsed_time(e[3]) for e in phs]),
+                "forward_with_segment_build_ms": pct([e[0].elapsed_time(e[2]) for e in phs]),
+                "forward_without_segment_build_ms": pct([e[1].elapsed_time(e[2]) for e in phs])}
+        if has_ft:
+            dist["backward_ms"] = pct([e[2].elapsed_time(e[3]) for e in phs])
+    # Context: a plain 256 MiB device-to-device copy on the same GPU (read + write bytes).
+    cbuf = torch.empty(1 << 28, dtype=torch.uint8, device=dev)
+    cdst = torch.empty_like(cbuf)
+    for _ in range(3):
+        cdst.copy_(cbuf)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(10):
+        cdst.copy_(cbuf)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * cbuf.numel() * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del cbuf, cdst
     if status is not None and int(status.item()) != 0:
         raise RuntimeError("the granted preemptible backward reported a yield")
     errs = [int(st["seg"].err.item()) + (int(st["seg_ft"].err.item()) if has_ft else 0) for st in sets]
@@ -544,6 +583,9 @@ def main():
         "host_enqueue_ms_per_step": (t_enq - t0) * 1e3 / K,
         "step_algorithmic_GBps": alg["step"]["bytes"] / (ms * 1e-3) / 1e9,
         "step_algorithmic_bytes": alg["step"]["bytes"],
+        "step_algorithmic_TFLOPs": alg["step"]["flops"] / (ms * 1e-3) / 1e12,
+        "step_timing_distribution": dist,
+        "copy_256MiB_GBps": copy_gbps,
         "roofline": {"bound": "hbm", "kernel": kern_name, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic() if args.workload == 3 and not args.fused else None,
