@@ -41,7 +41,7 @@ EVENT_EVERY = 5          # timed steps per sampled expand launch (events)
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--sets", type=int, default=4, help="rotating copies of every buffer")
     ap.add_argument("--workload", type=int, default=3, choices=(2, 3, 4, 5),
@@ -585,6 +585,7 @@ def main():
         "step_algorithmic_bytes": alg["step"]["bytes"],
         "step_algorithmic_TFLOPs": alg["step"]["flops"] / (ms * 1e-3) / 1e12,
         "step_timing_distribution": dist,
+        "inputs_sha256": wl.manifest(),
         "copy_256MiB_GBps": copy_gbps,
         "roofline": {"bound": "hbm", "kernel": kern_name, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
