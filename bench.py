@@ -213,9 +213,27 @@ def cpu_baseline(wl, min_seconds):
         el = time.perf_counter() - t0
         if el >= min_seconds or reps >= 50:
             break
-    return {"value": reps * wl.T / el, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+    cores = oracle.threads()
+    # the same batch once on one thread (plain loops, no OpenMP split)
+    oracle.set_threads(1)
+    t1 = time.perf_counter()
+    oracle.forward(ref["x"], ref["ids"], ref["ranks"], ref["scales"], ref["A"], ref["B"], ref["y0"])
+    if n > 0:
+        oracle.backward(ref["x"][s:s + n], ref["dy"], ref["ids"][s:s + n], ref["ranks"], ref["scales"],
+                        ref["A"], ref["B"])
+    el1 = time.perf_counter() - t1
+    oracle.set_threads(threads)
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:
+        pass
+    return {"value": reps * wl.T / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"the full batch ({wl.T} rows forward + {n} fine-tuning rows backward), "
-                      f"repeated {reps}x in {el:.1f} s, fp64 plain loops, OpenMP over rows"}
+                      f"repeated {reps}x in {el:.1f} s, fp64 plain loops, OpenMP over rows",
+            "single_thread_value": wl.T / el1, "single_thread_seconds": el1,
+            "host_cpu": model, "host_nproc": os.cpu_count()}
 
 
 def multi_slice_report(steps: int, warmup: int, n_sets: int):
