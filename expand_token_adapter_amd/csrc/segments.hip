@@ -224,31 +224,42 @@ __device__ __forceinline__ uint64_t same_id_lanes(int id, bool valid, int nbits)
 }
 
 
-// Exclusive scan of four ints per thread across the workgroup (one LDS
-// barrier; s_tot is used once).  Returns the exclusive prefixes and writes
-// the workgroup totals to *total.
-__device__ __forceinline__ int4 block_exclusive_scan4(int4 v, int4* s_tot, int4* total) {
-    constexpr int kWaves = kScanThreads / kWave;
-    const int w = wave_id();
-    const int lane = threadIdx.x & (kWave - 1);
+// Inclusive scan of four ints across the first n (a power of two) lanes of a wave.
+template <int n>
+__device__ __forceinline__ int4 wave_inclusive_scan4(int4 v, int lane) {
     int4 incl = v;
 #pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
+    for (int d = 1; d < n; d <<= 1) {
         const int4 o = make_int4(__shfl_up(incl.x, d, kWave), __shfl_up(incl.y, d, kWave),
                                  __shfl_up(incl.z, d, kWave), __shfl_up(incl.w, d, kWave));
         if (lane >= d) incl = incl + o;
     }
+    return incl;
+}
+
+// Exclusive scan of four ints per thread across the workgroup.  Each wave
+// scans its lanes; wave 0 then scans the wave totals (s_tot[0, W) in, their
+// exclusive prefixes to s_tot[W, 2W), the workgroup totals to s_tot[2W]),
+// and every wave reads back its own prefix and the totals: two LDS barriers
+// and two reads per wave, instead of every wave summing all W totals.
+// s_tot holds 2W + 1 entries (W waves) and is used once.  Returns the
+// exclusive prefixes and writes the workgroup totals to *total.
+__device__ __forceinline__ int4 block_exclusive_scan4(int4 v, int4* s_tot, int4* total) {
+    constexpr int kWaves = kScanThreads / kWave;
+    const int w = wave_id();
+    const int lane = threadIdx.x & (kWave - 1);
+    const int4 incl = wave_inclusive_scan4<kWave>(v, lane);
     if (lane == kWave - 1) s_tot[w] = incl;
     lds_barrier();
-    int4 before = make_int4(0, 0, 0, 0), all = make_int4(0, 0, 0, 0);
-#pragma unroll 4
-    for (int i = 0; i < kWaves; ++i) {
-        const int4 x = s_tot[i];
-        if (i < w) before = before + x;
-        all = all + x;
+    if (w == 0) {
+        const int4 t = lane < kWaves ? s_tot[lane] : make_int4(0, 0, 0, 0);
+        const int4 ti = wave_inclusive_scan4<kWaves>(t, lane);
+        if (lane < kWaves) s_tot[kWaves + lane] = ti - t;
+        if (lane == kWaves - 1) s_tot[2 * kWaves] = ti;
     }
-    *total = all;
-    return before + incl - v;
+    lds_barrier();
+    *total = s_tot[2 * kWaves];
+    return s_tot[kWaves + w] + incl - v;
 }
 
 constexpr int kSmallMaxA = 1024;
@@ -285,7 +296,7 @@ __global__ __launch_bounds__(kScanThreads) void seg_small_kernel(SegSmallJobs jo
     const int64_t active_off = job.active_off, tiles16_off = job.tiles16_off, tiles64_off = job.tiles64_off;
     __shared__ int s_hist[kSmallWaves][kSmallMaxA];
     __shared__ int4 s_info[kSmallMaxA];  // offset, count, 16-row tile prefix, 64-row tile prefix
-    __shared__ int4 s_tot[kSmallWaves];
+    __shared__ int4 s_tot[2 * kSmallWaves + 1];
     __shared__ int s_err[kSmallWaves];
     const int tid = threadIdx.x;
     const int w = wave_id();
@@ -352,8 +363,20 @@ __global__ __launch_bounds__(kScanThreads) void seg_small_kernel(SegSmallJobs jo
             c += h;
         }
     }
-    int4 tot;
-    const int4 ex = block_exclusive_scan4(make_int4(c, (c + 15) / 16, (c + 63) / 64, c > 0 ? 1 : 0), s_tot, &tot);
+    // (rows, 16-row tiles, 64-row tiles, active) of adapter a, scanned over the adapters
+    const int4 v4 = make_int4(c, (c + 15) / 16, (c + 63) / 64, c > 0 ? 1 : 0);
+    int4 tot = make_int4(0, 0, 0, 0), ex = make_int4(0, 0, 0, 0);
+    if (A <= kWave) {
+        // every adapter is a lane of wave 0: one wave-level scan, no barrier
+        if (w == 0) {
+            const int4 incl = wave_inclusive_scan4<kWave>(v4, lane);
+            ex = incl - v4;
+            tot = make_int4(__shfl(incl.x, kWave - 1, kWave), __shfl(incl.y, kWave - 1, kWave),
+                            __shfl(incl.z, kWave - 1, kWave), __shfl(incl.w, kWave - 1, kWave));
+        }
+    } else {
+        ex = block_exclusive_scan4(v4, s_tot, &tot);
+    }
     if (a < A) s_info[a] = make_int4(ex.x, c, ex.y, ex.z);
     lds_barrier();
     if (a < A) {
