@@ -323,7 +323,13 @@ __global__ __launch_bounds__(kScanThreads) void seg_small_kernel(SegSmallJobs jo
     // (bits 0-7), their number (bits 8-15), bit 16 set on the lowest of them;
     // 0 for a lane without a valid id.
     auto match = [&](int id, bool valid) {
-        const uint64_t m = same_id_lanes(id, valid, nbits);
+        // A group whose valid lanes all hold one id (a run of prefill or
+        // fine-tuning rows) matches on the valid lanes at once; only mixed
+        // groups take one ballot per id bit.  (Wave-uniform branch.)
+        const uint64_t vm = __ballot(valid);
+        const int l0 = vm ? __ffsll((long long)vm) - 1 : 0;
+        const int id0 = __builtin_amdgcn_readlane(id, l0);
+        const uint64_t m = __ballot(valid && id == id0) == vm ? (valid ? vm : 0ull) : same_id_lanes(id, valid, nbits);
         const int rank = __popcll(m & ((1ull << lane) - 1));
         return valid ? rank | (__popcll(m) << 8) | (rank == 0 ? 1 << 16 : 0) : 0;
     };
