@@ -39,7 +39,15 @@ def _dtype_code(t: torch.Tensor) -> int:
     return _DTYPES[t.dtype]
 
 
+# The current stream's raw handle, without building a torch Stream object per
+# call (that costs about as much as the rest of a call's marshalling); the
+# public query where this PyTorch build lacks the raw one.
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(dev: torch.device) -> int:
+    if _raw_stream is not None:
+        return _raw_stream(dev.index if dev.index is not None else torch.cuda.current_device())
     return torch.cuda.current_stream(dev).cuda_stream
 
 
@@ -170,11 +178,13 @@ class Segments:
         self.sched = torch.zeros(max(1, lib.lora_segments_sched_elems(T, num_adapters)), **i32)
         self.ws = torch.empty(max(1, lib.lora_segments_workspace_bytes(T, num_adapters)), dtype=torch.uint8,
                               device=device)
+        self._c = _abi.LoraSegments(self.counts.data_ptr(), self.offsets.data_ptr(), self.perm.data_ptr(),
+                                    self.err.data_ptr(), self.sched.data_ptr())
 
     @property
     def c(self) -> _abi.LoraSegments:
-        return _abi.LoraSegments(self.counts.data_ptr(), self.offsets.data_ptr(), self.perm.data_ptr(),
-                                 self.err.data_ptr(), self.sched.data_ptr())
+        """The C struct of device pointers (the tensors are allocated once, so it is built once)."""
+        return self._c
 
 
 def lora_segments_build(adapter_ids: torch.Tensor, num_adapters: int, out: Optional[Segments] = None) -> Segments:
