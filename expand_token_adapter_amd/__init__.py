@@ -235,9 +235,9 @@ def lora_shrink(x: torch.Tensor, adapters: AdapterTable, seg: Segments, v: Optio
         v = torch.zeros((T, (r_max + 7) // 8 * 8), dtype=torch.float32, device=x.device)
     pv, _, _, ldv = _rows(v, "v")
     lib = _abi.load()
-    need = lib.lora_shrink_workspace_bytes(_dtype_code(x), T, d_in, r_max)
-    if ws is None or ws.numel() < need:
-        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    if ws is None:  # a caller's workspace is size-checked by the library (LORA_ERR_WORKSPACE)
+        ws = torch.empty(max(lib.lora_shrink_workspace_bytes(_dtype_code(x), T, d_in, r_max), 1),
+                         dtype=torch.uint8, device=x.device)
     st = lib.lora_shrink(_dtype_code(x), px, ldx, T, d_in, adapters.ptr, len(adapters), r_max, seg.c,
                          pv, ldv, ws.data_ptr(), ws.numel(), _stream(x.device))
     _abi.check("lora_shrink", st)
@@ -350,9 +350,9 @@ def _backward(fn, x, dy, adapters, grads, seg_ft, dx, v_saved, r_max, ws, extra)
         raise ValueError("the gradient table must have one entry per adapter")
     r_max = adapters.r_max if r_max is None else r_max
     lib = _abi.load()
-    need = lib.lora_backward_workspace_bytes(_dtype_code(x), T, d_in, d_out, r_max)
-    if ws is None or ws.numel() < need:
-        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    if ws is None:  # a caller's workspace is size-checked by the library (LORA_ERR_WORKSPACE)
+        ws = torch.empty(max(lib.lora_backward_workspace_bytes(_dtype_code(x), T, d_in, d_out, r_max), 1),
+                         dtype=torch.uint8, device=x.device)
     st = getattr(lib, fn)(_dtype_code(x), px, ldx, pdy, lddy, pdx or None, lddx, T, d_in, d_out, adapters.ptr,
                           grads.ptr, len(adapters), r_max, seg_ft.c, pvs or None, ldv, ws.data_ptr(), ws.numel(),
                           *extra, _stream(x.device))

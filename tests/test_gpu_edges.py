@@ -85,3 +85,30 @@ def test_rows_without_adapters_are_left_alone():
     assert status.item() == 0
     assert rel_err(dx, dx_r) <= TOL["f32"] and rel_err(dA[1], dA_r[1]) <= TOL["f32"]
     assert rel_err(dB[1], dB_r[1]) <= TOL["f32"]
+
+
+def test_too_small_workspace_is_rejected_before_any_work():
+    """A caller's workspace smaller than the size query is refused with
+    LORA_ERR_WORKSPACE and nothing is written."""
+    from gpu_helpers import to_dev
+    wl = workloads.custom(np.array([0, 1, 0, -1, 1], dtype=np.int32), [8, 16], 64, 32, "bf16", seed=4,
+                          ft_start=0, ft_count=5)
+    dev = torch.device("cuda:0")
+    table = lb.AdapterTable([to_dev(a, "bf16", dev) for a in wl.A], [to_dev(b, "bf16", dev) for b in wl.B],
+                            wl.scales.tolist())
+    ids = torch.from_numpy(wl.ids).to(dev)
+    seg = lb.lora_segments_build(ids, 2)
+    x, dy = to_dev(wl.x, "bf16", dev), to_dev(wl.dy, "bf16", dev)
+    v = torch.full((5, 16), 7.0, dtype=torch.float32, device=dev)
+    need = lb.lora_shrink_workspace_bytes(torch.bfloat16, 5, 64, 16)
+    with pytest.raises(lb.LoraError, match="lora_shrink"):
+        lb.lora_shrink(x, table, seg, v=v, ws=torch.empty(need - 1, dtype=torch.uint8, device=dev))
+    dA = [torch.zeros(a.shape, dtype=torch.float32, device=dev) for a in table.A]
+    dB = [torch.zeros(b.shape, dtype=torch.float32, device=dev) for b in table.B]
+    need_b = lb.lora_backward_workspace_bytes(torch.bfloat16, 5, 64, 32, 16)
+    with pytest.raises(lb.LoraError, match="lora_backward"):
+        lb.lora_backward(x, dy, table, lb.GradTable(dA, dB), seg, ws=torch.empty(need_b - 1, dtype=torch.uint8,
+                                                                                     device=dev))
+    torch.cuda.synchronize()
+    assert torch.equal(v, torch.full_like(v, 7.0))
+    assert not any(t.any().item() for t in dA + dB)
