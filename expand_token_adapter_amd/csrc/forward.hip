@@ -18,12 +18,23 @@ namespace {
 constexpr int64_t kMaxGrid = 8192;
 constexpr int64_t kShrinkMaxGrid = 1024;
 
+template <int DT, int RB>
+void launch_shrink_rb(bool trans_w, const ShrinkParams& p, unsigned grid, hipStream_t st) {
+    if (trans_w)
+        hipLaunchKernelGGL((shrink_kernel<DT, true, RB>), dim3(grid), dim3(kShrinkThreads), 0, st, p);
+    else
+        hipLaunchKernelGGL((shrink_kernel<DT, false, RB>), dim3(grid), dim3(kShrinkThreads), 0, st, p);
+}
+
+// 16-rank blocks per task: 1 (r_max <= 16), 2 (<= 32), else 4 (64-rank groups)
 template <int DT>
 int launch_shrink_t(bool trans_w, const ShrinkParams& p, unsigned grid, hipStream_t st) {
-    if (trans_w)
-        hipLaunchKernelGGL((shrink_kernel<DT, true>), dim3(grid), dim3(kShrinkThreads), 0, st, p);
+    if (p.r_max <= 16)
+        launch_shrink_rb<DT, 1>(trans_w, p, grid, st);
+    else if (p.r_max <= 32)
+        launch_shrink_rb<DT, 2>(trans_w, p, grid, st);
     else
-        hipLaunchKernelGGL((shrink_kernel<DT, false>), dim3(grid), dim3(kShrinkThreads), 0, st, p);
+        launch_shrink_rb<DT, 4>(trans_w, p, grid, st);
     return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 

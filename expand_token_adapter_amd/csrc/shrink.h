@@ -95,7 +95,10 @@ __device__ __forceinline__ void shrink_slice_mma(f32x4_t* acc, const Frag<DT> (*
     }
 }
 
-template <int DT, bool TRANS_W>
+// RB: 16-rank blocks a task covers (1, 2 or 4, from r_max): the weight slice
+// in LDS (16 RB rank rows of 1 KB) and the accumulators are sized for it, so
+// small ranks leave room for more workgroups per CU.
+template <int DT, bool TRANS_W, int RB>
 __global__ __launch_bounds__(kShrinkThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void shrink_kernel(ShrinkParams p) {
     using F = Frag<DT>;
@@ -103,9 +106,10 @@ void shrink_kernel(ShrinkParams p) {
     constexpr int EPU = 16 / EB;                 // elements per 16-byte unit
     constexpr int SC = shrink_slice_chunks(DT);  // 64-element chunks per slice
     constexpr int SCH = SC / 2;                  // chunks per wave (half a slice)
-    constexpr int NU = 64 * 64 / kShrinkThreads; // row-major weight rows x units per thread
+    static_assert(RB == 1 || RB == 2 || RB == 4, "rank blocks per task");
+    constexpr int NU = 16 * RB * 64 / kShrinkThreads; // row-major weight rows x units per thread
     constexpr int kTB = 4;                       // transposed weight units per thread and batch
-    __shared__ __attribute__((aligned(16))) u32x4_t s_w[64 * 64];
+    __shared__ __attribute__((aligned(16))) u32x4_t s_w[16 * RB * 64];
     char* s_wb = reinterpret_cast<char*>(s_w);
     f32x4_t* s_red = reinterpret_cast<f32x4_t*>(s_w);  // reused after the MFMA pass
 
@@ -259,21 +263,21 @@ void shrink_kernel(ShrinkParams p) {
 
         // 4. MFMA over this wave's half-slice (row blocks past the tile skip it).
         const bool rows_ok = 16 * rb < nrows;
-        f32x4_t acc[4];
+        f32x4_t acc[RB];
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int mb = 0; mb < RB; ++mb) acc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         if (rows_ok) {
             switch (nmb) {
                 case 1: shrink_slice_mma<DT, SCH, 1>(acc, xr, s_w, kh * SCH, nch, klen, lr, lg); break;
-                case 2: shrink_slice_mma<DT, SCH, 2>(acc, xr, s_w, kh * SCH, nch, klen, lr, lg); break;
-                case 3: shrink_slice_mma<DT, SCH, 3>(acc, xr, s_w, kh * SCH, nch, klen, lr, lg); break;
-                default: shrink_slice_mma<DT, SCH, 4>(acc, xr, s_w, kh * SCH, nch, klen, lr, lg); break;
+                case 2: if constexpr (RB >= 2) shrink_slice_mma<DT, SCH, 2>(acc, xr, s_w, kh * SCH, nch, klen, lr, lg); break;
+                case 3: if constexpr (RB >= 4) shrink_slice_mma<DT, SCH, 3>(acc, xr, s_w, kh * SCH, nch, klen, lr, lg); break;
+                default: if constexpr (RB >= 4) shrink_slice_mma<DT, SCH, 4>(acc, xr, s_w, kh * SCH, nch, klen, lr, lg); break;
             }
         }
         __syncthreads();  // weight slice no longer read: its LDS holds the second half's tiles
         if (kh == 1 && rows_ok) {
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb) s_red[(rb * 4 + mb) * kWave + lane] = acc[mb];
+            for (int mb = 0; mb < RB; ++mb) s_red[(rb * RB + mb) * kWave + lane] = acc[mb];
         }
         __syncthreads();
         if (kh == 0 && rows_ok) {
@@ -281,9 +285,9 @@ void shrink_kernel(ShrinkParams p) {
             float* part = p.part + (int64_t)sl * p.slice_stride;
             const int row = 16 * rb + lr;
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {
+            for (int mb = 0; mb < RB; ++mb) {
                 const int rk = rank0 + 16 * mb + 4 * lg;
-                const f32x4_t sum = acc[mb] + s_red[(rb * 4 + mb) * kWave + lane];
+                const f32x4_t sum = acc[mb] + s_red[(rb * RB + mb) * kWave + lane];
                 if (mb < nmb && row < nrows && rk < r)
                     *gptr(reinterpret_cast<f32x4_t*>(part + (int64_t)(pos0 + row) * p.ldp + rk)) = sum;
             }
