@@ -197,10 +197,11 @@ __global__ __launch_bounds__(kChunk) void seg_scatter_kernel(const int32_t* __re
 // each lane's match inside its group (longer ranges load and match the rest
 // again in the second pass; the matching is most of the kernel's ALU work):
 //   1. wave w counts its ids into its own LDS histogram row hist[w][a], one
-//      update per distinct id of each 64-row group (lanes with equal ids are
-//      matched by one ballot per id bit);
+//      update per distinct id of each 64-row group (a group holding one id is
+//      matched by one ballot; other groups by one ballot per id bit);
 //   2. per adapter: counts = sum over w, hist[w][a] becomes the exclusive
-//      prefix over waves; one block scan of four values per adapter gives
+//      prefix over waves; one scan of four values per adapter (within wave 0
+//      when the adapters fit in one wave, else across the workgroup) gives
 //      offsets, both tile prefixes and the active list;
 //   3. wave w walks its rows in order, 64 at a time; inside a group the lanes
 //      that share an id are ranked by lane order (the same ballot match), and
