@@ -11,12 +11,17 @@ adapters with ranks drawn from {8, 16, 32, 64}, scale 2.0; d_in 4096 ->
 d_out 14336; bf16 elements (DeltaServe section 3.2, "Mixed forward batch").
 
 Inputs are resident in HBM before the timed region.  Consecutive steps use
-different copies of every buffer (weights included, `--sets` copies), so a
-step never finds the previous step's data in the 256 MB Infinity Cache.
+different copies of every buffer (weights included): as many copies as it
+takes to rotate through more than 1.2 GB, so a step never finds the previous
+step's data in the 256 MB Infinity Cache (the rotation size is reported).
 
 Prints one JSON line.  `value` = rows of the batch per second of step time.
 `roofline` is for the dominant kernel (lora_expand_add: the read-modify-write
 of y), timed with HIP events around its launch on the stream it runs on.
+`calls` gives each library call's GPU time per call, from captured HIP graphs
+of back-to-back calls over the rotating copies (no host launch overhead).
+`workloads` repeats the measurement on the decode, fine-tuning and many-adapter
+decode workloads (their forward path as the library's chooser picks it).
 `cpu_baseline` times the fp64 oracle on the host on the same batch.
 """
 from __future__ import annotations
@@ -43,7 +48,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--sets", type=int, default=4, help="rotating copies of every buffer")
+    ap.add_argument("--sets", type=int, default=0,
+                    help="rotating copies of every buffer (default: enough for a rotation above 1.2 GB, at least 4)")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="measure the headline workload only (no `workloads` block)")
+    ap.add_argument("--workload-steps", type=int, default=50, help="timed steps per workload of the block")
     ap.add_argument("--workload", type=int, default=3, choices=(2, 3, 4, 5),
                     help="synthetic workload (workloads.config index); 3 = the mixed co-serving batch")
     ap.add_argument("--graph", action="store_true", help="replay each step from a captured HIP graph")
@@ -347,6 +356,263 @@ def cost_model_report(reps: int = 10):
                               "predicted_us": pred * 1e6, "rel_err": pred / meas - 1.0}), flush=True)
 
 
+ROTATION_BYTES = 1.2e9  # more than the 256 MB Infinity Cache, several times over
+
+
+def per_set_bytes(wl) -> int:
+    """Device bytes of one rotating copy of a workload's buffers."""
+    e = 2
+    w = sum(a.size for a in wl.A) * e + sum(b.size for b in wl.B) * e
+    io = wl.T * wl.d_in * e + wl.T * wl.d_out * e + wl.T * ((wl.r_max + 7) // 8 * 8) * 4
+    ft = 0
+    if wl.ft_count:
+        ft = wl.ft_count * (wl.d_out + wl.d_in) * e + 2 * (w // e) * 4  # dy, dx, fp32 dA / dB of every adapter
+    return w + io + ft
+
+
+def auto_sets(wl) -> int:
+    import math
+    return max(4, int(math.ceil(ROTATION_BYTES / per_set_bytes(wl))))
+
+
+class Bench:
+    """One workload resident on the GPU in rotating copies, and its step."""
+
+    def __init__(self, wl, n_sets, fused=False, preemptible=False, adamw=False, overlap=False):
+        import torch
+        import expand_token_adapter_amd as lb
+        self.torch, self.lb = torch, lb
+        self.wl = wl
+        self.dev = dev = torch.device("cuda:0")
+        self.fused, self.adamw = fused, adamw
+        T, s, n = wl.T, wl.ft_start, wl.ft_count
+        self.has_ft = has_ft = n > 0
+
+        def dev_bf16(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+        base = dict(A=[dev_bf16(a) for a in wl.A], B=[dev_bf16(b) for b in wl.B], x=dev_bf16(wl.x),
+                    y=dev_bf16(wl.y0), dy=dev_bf16(wl.dy) if has_ft else None)
+        ids = torch.from_numpy(wl.ids).to(dev)
+        ft_ids = ids[s:s + n].contiguous()
+        self.sets = []
+        for k in range(n_sets):
+            c = (lambda t: t) if k == 0 else (lambda t: t.clone())
+            A = [c(a) for a in base["A"]]
+            B = [c(b) for b in base["B"]]
+            st = dict(A=A, B=B, table=lb.AdapterTable(A, B, wl.scales.tolist()), x=c(base["x"]), y=c(base["y"]),
+                      ids=ids.clone())
+            st["v"] = torch.zeros((T, (st["table"].r_max + 7) // 8 * 8), dtype=torch.float32, device=dev)
+            st["seg"] = lb.Segments(T, wl.num_adapters, dev)
+            if has_ft:
+                st["dy"] = c(base["dy"])
+                st["ft_ids"] = ft_ids.clone()
+                st["dx"] = torch.zeros((n, wl.d_in), dtype=torch.bfloat16, device=dev)
+                st["dA"] = [torch.zeros(a.shape, dtype=torch.float32, device=dev) for a in A]
+                st["dB"] = [torch.zeros(b.shape, dtype=torch.float32, device=dev) for b in B]
+                st["grads"] = lb.GradTable(st["dA"], st["dB"])
+                st["seg_ft"] = lb.Segments(n, wl.num_adapters, dev)
+                st["ws"] = torch.empty(lb.lora_backward_workspace_bytes(torch.bfloat16, n, wl.d_in, wl.d_out,
+                                                                        st["table"].r_max),
+                                       dtype=torch.uint8, device=dev)
+                if adamw:
+                    # AdamW state of the fine-tuning adapter's A and B: fp32 master copies and moments
+                    st["opt"] = [(w, gr, torch.zeros(w.shape, dtype=torch.float32, device=dev),
+                                  torch.zeros(w.shape, dtype=torch.float32, device=dev), w.float())
+                                 for a in sorted(set(int(i) for i in wl.ft_ids))
+                                 for w, gr in ((A[a], st["dA"][a]), (B[a], st["dB"][a]))]
+                    st["opt_step"] = 0
+            st["ws_shrink"] = torch.empty(lb.lora_shrink_workspace_bytes(torch.bfloat16, T, wl.d_in,
+                                                                         st["table"].r_max),
+                                          dtype=torch.uint8, device=dev)
+            self.sets.append(st)
+        del base
+        torch.cuda.synchronize()
+        self.side = torch.cuda.Stream(device=dev) if overlap else None  # default priority
+        self.grant = torch.ones(1, dtype=torch.int32, device=dev) if preemptible else None
+        self.status = torch.zeros(1, dtype=torch.int32, device=dev) if preemptible else None
+
+    # ---------------------------------------------------------------- the library calls of a step
+    def seg_build(self, st):
+        if self.has_ft:
+            # the batch's rows and its fine-tuning rows grouped in one launch
+            self.lb.lora_segments_build_batch([(st["ids"], st["seg"]), (st["ft_ids"], st["seg_ft"])],
+                                              self.wl.num_adapters)
+        else:
+            self.lb.lora_segments_build(st["ids"], self.wl.num_adapters, out=st["seg"])
+
+    def shrink(self, st):
+        self.lb.lora_shrink(st["x"], st["table"], st["seg"], v=st["v"], ws=st["ws_shrink"])
+
+    def expand(self, st):
+        self.lb.lora_expand_add(st["v"], st["table"], st["seg"], st["y"])
+
+    def forward_fused(self, st):
+        self.lb.lora_forward(st["x"], st["table"], st["seg"], st["y"], v=st["v"])
+
+    def backward(self, st, v_saved=True):
+        s, n = self.wl.ft_start, self.wl.ft_count
+        vs = st["v"][s:s + n] if v_saved else None
+        if self.grant is not None:
+            self.lb.lora_backward_preemptible(st["x"][s:s + n], st["dy"], st["table"], st["grads"], st["seg_ft"],
+                                              self.grant, self.status, dx=st["dx"], v_saved=vs, ws=st["ws"])
+            return
+        self.lb.lora_backward(st["x"][s:s + n], st["dy"], st["table"], st["grads"], st["seg_ft"], dx=st["dx"],
+                              v_saved=vs, ws=st["ws"])
+
+    def step(self, st, ev=None, ph=None):
+        # ev: events around the dominant kernel (and the optimizer); ph: events at
+        # the start, after the segment build, after the forward and at the end
+        torch = self.torch
+        if ph is not None:
+            ph[0].record()
+        side = self.side
+        if side is not None and self.has_ft:
+            side.wait_stream(torch.cuda.current_stream(self.dev))
+            with torch.cuda.stream(side):
+                self.lb.lora_segments_build(st["ft_ids"], self.wl.num_adapters, out=st["seg_ft"])
+                self.backward(st, v_saved=False)
+            self.lb.lora_segments_build(st["ids"], self.wl.num_adapters, out=st["seg"])
+        else:
+            self.seg_build(st)
+        if ph is not None:
+            ph[1].record()
+        if self.fused:
+            if ev is not None:
+                ev[0].record()
+            self.forward_fused(st)
+            if ev is not None:
+                ev[1].record()
+        else:
+            self.shrink(st)
+            if ev is not None:
+                ev[0].record()
+            self.expand(st)
+            if ev is not None:
+                ev[1].record()
+        if ph is not None:
+            ph[2].record()
+        if side is not None and self.has_ft:
+            torch.cuda.current_stream(self.dev).wait_stream(side)
+        elif self.has_ft:
+            self.backward(st)
+        if self.adamw and self.has_ft:
+            st["opt_step"] += 1
+            if ev is not None:
+                ev[2].record()
+            self.lb.lora_adamw_step(st["opt"], step=st["opt_step"], zero_grad=True)
+            if ev is not None:
+                ev[3].record()
+        if ph is not None:
+            ph[3].record()
+
+    # ---------------------------------------------------------------- measurements
+    def distribution(self, K, start):
+        """Per-step event times of K steps (outside any timed region)."""
+        torch = self.torch
+        phs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(K)]
+        for i in range(K):
+            self.step(self.sets[(start + i) % len(self.sets)], None, phs[i])
+        torch.cuda.synchronize()
+        pct = lambda a: {"p10": float(np.percentile(a, 10)), "median": float(np.median(a)),
+                         "p90": float(np.percentile(a, 90))}
+        dist = {"steps": K, "step_ms": pct([e[0].elapsed_time(e[3]) for e in phs]),
+                "forward_with_segment_build_ms": pct([e[0].elapsed_time(e[2]) for e in phs]),
+                "forward_without_segment_build_ms": pct([e[1].elapsed_time(e[2]) for e in phs])}
+        if self.has_ft:
+            dist["backward_ms"] = pct([e[2].elapsed_time(e[3]) for e in phs])
+        return dist
+
+    def call_times(self, names, reps=None):
+        """GPU time per call of each named library call: a captured HIP graph of the
+        call over every rotating copy (segments built first), replayed between events."""
+        torch = self.torch
+        ops = {"segments": self.seg_build, "shrink": self.shrink, "expand": self.expand,
+               "forward_fused": self.forward_fused, "backward": self.backward}
+        out = {}
+        for st in self.sets:
+            self.seg_build(st)
+            self.shrink(st)
+        torch.cuda.synchronize()
+        for name in names:
+            fn = ops[name]
+            cap = torch.cuda.Stream(device=self.dev)
+            cap.wait_stream(torch.cuda.current_stream(self.dev))
+            with torch.cuda.stream(cap):
+                for st in self.sets:
+                    fn(st)
+            torch.cuda.current_stream(self.dev).wait_stream(cap)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for st in self.sets:
+                    fn(st)
+            n_rep = reps or max(3, int(200 / len(self.sets)))
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(n_rep):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            out[name] = e0.elapsed_time(e1) * 1e3 / (n_rep * len(self.sets))  # us per call
+            del g
+        return out
+
+    def check_errors(self):
+        errs = [int(st["seg"].err.item()) + (int(st["seg_ft"].err.item()) if self.has_ft else 0) for st in self.sets]
+        if any(errs):
+            raise RuntimeError(f"device-side data errors reported: {errs}")
+        if self.status is not None and int(self.status.item()) != 0:
+            raise RuntimeError("the granted preemptible backward reported a yield")
+
+
+def call_report(wl, times, alg):
+    """Per-call GPU time with its algorithmic bytes and HBM fraction."""
+    out = {}
+    keymap = {"segments": "segments", "shrink": "shrink", "expand": "expand", "forward_fused": "forward_fused",
+              "backward": "backward"}
+    for name, us in times.items():
+        b = alg[keymap[name]]["bytes"]
+        out[name] = {"us_per_call": us, "algorithmic_bytes": b, "GBps": b / (us * 1e-6) / 1e9,
+                     "frac_of_hbm_peak": b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+    return out
+
+
+def workload_block(idx, steps, warmup):
+    """Step time and per-call GPU times of one more workload (its own rotation)."""
+    import torch
+    import workloads
+    wl = workloads.config(idx, seed=0)
+    n_sets = auto_sets(wl)
+    b = Bench(wl, n_sets)
+    alg = algorithmic(wl)
+    for i in range(warmup):
+        b.step(b.sets[i % n_sets])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        b.step(b.sets[(warmup + i) % n_sets])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    dist = b.distribution(steps, warmup + steps)
+    names = ["segments", "shrink", "expand", "forward_fused"] + (["backward"] if b.has_ft else [])
+    calls = call_report(wl, b.call_times(names), alg)
+    b.check_errors()
+    fwd_us = calls["shrink"]["us_per_call"] + calls["expand"]["us_per_call"]
+    fwd_b = alg["shrink"]["bytes"] + alg["expand"]["bytes"]
+    res = {"rows": wl.T, "ft_rows": wl.ft_count, "d_in": wl.d_in, "d_out": wl.d_out, "adapters": wl.num_adapters,
+           "ranks": RANKS_DESC[idx], "ms_per_step": ms, "rows_per_s": wl.T / (ms * 1e-3),
+           "step_timing_distribution": dist, "calls": calls,
+           "forward_split_us": fwd_us, "forward_split_algorithmic_bytes": fwd_b,
+           "forward_split_frac_of_hbm_peak": fwd_b / (fwd_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+           "input_sets": n_sets, "rotation_bytes": n_sets * per_set_bytes(wl), "steps": steps, "warmup": warmup}
+    del b
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -365,118 +631,23 @@ def main():
         cost_model_report()
         return
     if args.multi_slice:
-        multi_slice_report(args.steps, args.warmup, args.sets)
+        multi_slice_report(args.steps, args.warmup, args.sets or 4)
         return
     if args.traffic_from:
         traffic_from(*args.traffic_from)
         return
     import torch
-    import expand_token_adapter_amd as lb
     import workloads
 
     dev = torch.device("cuda:0")
     wl = workloads.config(args.workload, seed=0)
-    T, s, n = wl.T, wl.ft_start, wl.ft_count
+    T, n = wl.T, wl.ft_count
     has_ft = n > 0
     alg = algorithmic(wl)
-
-    def dev_bf16(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
-
-    base = dict(A=[dev_bf16(a) for a in wl.A], B=[dev_bf16(b) for b in wl.B], x=dev_bf16(wl.x),
-                y=dev_bf16(wl.y0), dy=dev_bf16(wl.dy) if has_ft else None)
-    ids = torch.from_numpy(wl.ids).to(dev)
-    ft_ids = ids[s:s + n].contiguous()
+    n_sets = args.sets or auto_sets(wl)
+    b = Bench(wl, n_sets, fused=args.fused, preemptible=args.preemptible, adamw=args.adamw, overlap=args.overlap)
+    sets = b.sets
     r_ft = int(wl.ranks[wl.ft_ids[0]]) if has_ft else None
-    sets = []
-    for k in range(args.sets):
-        c = (lambda t: t) if k == 0 else (lambda t: t.clone())
-        A = [c(a) for a in base["A"]]
-        B = [c(b) for b in base["B"]]
-        st = dict(A=A, B=B, table=lb.AdapterTable(A, B, wl.scales.tolist()), x=c(base["x"]), y=c(base["y"]),
-                  ids=ids.clone())
-        st["v"] = torch.zeros((T, (st["table"].r_max + 7) // 8 * 8), dtype=torch.float32, device=dev)
-        st["seg"] = lb.Segments(T, wl.num_adapters, dev)
-        if has_ft:
-            st["dy"] = c(base["dy"])
-            st["ft_ids"] = ft_ids.clone()
-            st["dx"] = torch.zeros((n, wl.d_in), dtype=torch.bfloat16, device=dev)
-            st["dA"] = [torch.zeros(a.shape, dtype=torch.float32, device=dev) for a in A]
-            st["dB"] = [torch.zeros(b.shape, dtype=torch.float32, device=dev) for b in B]
-            st["grads"] = lb.GradTable(st["dA"], st["dB"])
-            st["seg_ft"] = lb.Segments(n, wl.num_adapters, dev)
-            st["ws"] = torch.empty(lb.lora_backward_workspace_bytes(torch.bfloat16, n, wl.d_in, wl.d_out,
-                                                                    st["table"].r_max), dtype=torch.uint8, device=dev)
-            if args.adamw:
-                # AdamW state of the fine-tuning adapter's A and B: fp32 master copies and moments
-                st["opt"] = [(w, gr, torch.zeros(w.shape, dtype=torch.float32, device=dev),
-                              torch.zeros(w.shape, dtype=torch.float32, device=dev), w.float())
-                             for a in sorted(set(int(i) for i in wl.ft_ids))
-                             for w, gr in ((A[a], st["dA"][a]), (B[a], st["dB"][a]))]
-                st["opt_step"] = 0
-        st["ws_shrink"] = torch.empty(lb.lora_shrink_workspace_bytes(torch.bfloat16, T, wl.d_in, st["table"].r_max),
-                                      dtype=torch.uint8, device=dev)
-        sets.append(st)
-    torch.cuda.synchronize()
-
-    side = torch.cuda.Stream(device=dev) if args.overlap else None  # default priority
-
-    grant = torch.ones(1, dtype=torch.int32, device=dev) if args.preemptible else None
-    status = torch.zeros(1, dtype=torch.int32, device=dev) if args.preemptible else None
-
-    def backward(st, v_saved):
-        if grant is not None:
-            lb.lora_backward_preemptible(st["x"][s:s + n], st["dy"], st["table"], st["grads"], st["seg_ft"], grant,
-                                         status, dx=st["dx"], v_saved=v_saved, ws=st["ws"])
-            return
-        lb.lora_backward(st["x"][s:s + n], st["dy"], st["table"], st["grads"], st["seg_ft"], dx=st["dx"],
-                         v_saved=v_saved, ws=st["ws"])
-
-    def step(st, ev=None, ph=None):
-        # ph: events recorded at the start, after the segment build, after the
-        # forward and at the end of the step (the timing-distribution pass)
-        if ph is not None:
-            ph[0].record()
-        if side is not None and has_ft:
-            side.wait_stream(torch.cuda.current_stream(dev))
-            with torch.cuda.stream(side):
-                lb.lora_segments_build(st["ft_ids"], wl.num_adapters, out=st["seg_ft"])
-                backward(st, None)
-        if has_ft and side is None:
-            # the batch's rows and its fine-tuning rows grouped in one launch
-            lb.lora_segments_build_batch([(st["ids"], st["seg"]), (st["ft_ids"], st["seg_ft"])], wl.num_adapters)
-        else:
-            lb.lora_segments_build(st["ids"], wl.num_adapters, out=st["seg"])
-        if ph is not None:
-            ph[1].record()
-        if args.fused:
-            if ev is not None:
-                ev[0].record()
-            lb.lora_forward(st["x"], st["table"], st["seg"], st["y"], v=st["v"])
-            if ev is not None:
-                ev[1].record()
-        else:
-            lb.lora_shrink(st["x"], st["table"], st["seg"], v=st["v"], ws=st["ws_shrink"])
-            if ev is not None:
-                ev[0].record()
-            lb.lora_expand_add(st["v"], st["table"], st["seg"], st["y"])
-            if ev is not None:
-                ev[1].record()
-        if ph is not None:
-            ph[2].record()
-        if side is not None and has_ft:
-            torch.cuda.current_stream(dev).wait_stream(side)
-        elif has_ft:
-            backward(st, st["v"][s:s + n])
-        if args.adamw and has_ft:
-            st["opt_step"] += 1
-            if ev is not None:
-                ev[2].record()
-            lb.lora_adamw_step(st["opt"], step=st["opt_step"], zero_grad=True)
-            if ev is not None:
-                ev[3].record()
-        if ph is not None:
-            ph[3].record()
 
     graphs = None
     if args.graph:
@@ -484,14 +655,14 @@ def main():
         warm.wait_stream(torch.cuda.current_stream(dev))
         with torch.cuda.stream(warm):
             for st in sets:
-                step(st)
+                b.step(st)
         torch.cuda.current_stream(dev).wait_stream(warm)
         torch.cuda.synchronize()
         graphs = []
         for st in sets:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                step(st)
+                b.step(st)
             graphs.append(g)
         torch.cuda.synchronize()
 
@@ -499,7 +670,7 @@ def main():
         if graphs is not None:
             graphs[i % len(sets)].replay()
         else:
-            step(sets[i % len(sets)], ev)
+            b.step(sets[i % len(sets)], ev)
 
     for i in range(args.warmup):
         run(i)
@@ -508,8 +679,7 @@ def main():
     K = args.steps
     # Events around the expand launch of every EVENT_EVERY-th timed step (an
     # event record drains the stream for a few microseconds, so not every
-    # step carries one; with 4 input sets and a stride of 5 every set is
-    # sampled).
+    # step carries one).
     sampled = [i for i in range(K) if i % EVENT_EVERY == 0]
     evs = {i: tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for i in sampled}
     torch.cuda.synchronize()
@@ -531,32 +701,20 @@ def main():
     else:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         for i in range(3):
-            st = sets[i % len(sets)]
-            lb.lora_expand_add(st["v"], st["table"], st["seg"], st["y"])
+            b.expand(sets[i % len(sets)])
         e0.record()
         for i in range(K):
-            st = sets[i % len(sets)]
-            lb.lora_expand_add(st["v"], st["table"], st["seg"], st["y"])
+            b.expand(sets[i % len(sets)])
         e1.record()
         torch.cuda.synchronize()
         kern_ms = e0.elapsed_time(e1) / K
         kern_how = "events around back-to-back launches"
-    # Distribution of step times, outside the timed region above: a second
-    # pass of K steps with events at the start, after the segment build, after
-    # the forward and at the end of every step.
-    dist = None
-    if graphs is None:
-        phs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(K)]
-        for i in range(K):
-            step(sets[(args.warmup + K + i) % len(sets)], None, phs[i])
-        torch.cuda.synchronize()
-        pct = lambda a: {"p10": float(np.percentile(a, 10)), "median": float(np.median(a)),
-                         "p90": float(np.percentile(a, 90))}
-        dist = {"steps": K, "step_ms": pct([e[0].elapsed_time(e[3]) for e in phs]),
-                "forward_with_segment_build_ms": pct([e[0].elapsed_time(e[2]) for e in phs]),
-                "forward_without_segment_build_ms": pct([e[1].elapsed_time(e[2]) for e in phs])}
-        if has_ft:
-            dist["backward_ms"] = pct([e[2].elapsed_time(e[3]) for e in phs])
+    # Distribution of step times, outside the timed region above.
+    dist = b.distribution(K, args.warmup + K) if graphs is None else None
+    # Per-call GPU times from captured graphs (outside the timed region).
+    names = ["segments"] + (["forward_fused"] if args.fused else ["shrink", "expand"]) + \
+        (["backward"] if has_ft and not args.preemptible and not args.overlap else [])
+    calls = call_report(wl, b.call_times(names), alg) if not args.adamw else None
     # Context: a plain 256 MiB device-to-device copy on the same GPU (read + write bytes).
     cbuf = torch.empty(1 << 28, dtype=torch.uint8, device=dev)
     cdst = torch.empty_like(cbuf)
@@ -570,11 +728,7 @@ def main():
     torch.cuda.synchronize()
     copy_gbps = 2 * cbuf.numel() * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del cbuf, cdst
-    if status is not None and int(status.item()) != 0:
-        raise RuntimeError("the granted preemptible backward reported a yield")
-    errs = [int(st["seg"].err.item()) + (int(st["seg_ft"].err.item()) if has_ft else 0) for st in sets]
-    if any(errs):
-        raise RuntimeError(f"device-side data errors reported: {errs}")
+    b.check_errors()
 
     ex = alg["forward_fused"] if args.fused else alg["expand"]
     kern_name = "lora_forward (fused_forward_kernel)" if args.fused else "lora_expand_add (expand_kernel)"
@@ -594,7 +748,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": workloads.CONFIG_NAMES[args.workload], "rows": T, "ft_rows": n, "d_in": wl.d_in,
                    "d_out": wl.d_out, "adapters": wl.num_adapters, "ranks": RANKS_DESC[args.workload],
-                   "ft_adapter_rank": r_ft, "seed": 0, "input_sets": args.sets,
+                   "ft_adapter_rank": r_ft, "seed": 0, "input_sets": n_sets,
+                   "rotation_bytes": n_sets * per_set_bytes(wl),
                    "launch": "graph" if graphs is not None else "eager",
                    "streams": 2 if args.overlap else 1, "forward": "fused" if args.fused else "split",
                    "backward": "preemptible" if args.preemptible else "plain"},
@@ -603,6 +758,7 @@ def main():
         "step_algorithmic_bytes": alg["step"]["bytes"],
         "step_algorithmic_TFLOPs": alg["step"]["flops"] / (ms * 1e-3) / 1e12,
         "step_timing_distribution": dist,
+        "calls": calls,
         "inputs_sha256": wl.manifest(),
         "copy_256MiB_GBps": copy_gbps,
         "roofline": {"bound": "hbm", "kernel": kern_name, "achieved": achieved,
@@ -621,6 +777,16 @@ def main():
             opt_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs.values()]))
             line["adamw"] = {"elements": n_el, "algorithmic_bytes_per_launch": opt_bytes, "avg_launch_ms": opt_ms,
                              "achieved_GBps": opt_bytes / (opt_ms * 1e-3) / 1e9}
+    del b, sets, graphs
+    torch.cuda.empty_cache()
+    default_run = (args.workload == 3 and not (args.fused or args.graph or args.overlap or args.preemptible
+                                               or args.adamw))
+    if default_run and not args.no_workloads:
+        block = {}
+        for idx in (2, 4, 5):
+            print(f"bench: workload {workloads.CONFIG_NAMES[idx]}", file=sys.stderr, flush=True)
+            block[workloads.CONFIG_NAMES[idx]] = workload_block(idx, args.workload_steps, args.warmup)
+        line["workloads"] = block
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_min_seconds)
     print(json.dumps(line), flush=True)

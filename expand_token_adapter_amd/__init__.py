@@ -64,6 +64,45 @@ def _rows(t: torch.Tensor, name: str):
     return t.data_ptr(), t.shape[0], t.shape[1], t.stride(0)
 
 
+def _check_batch(name: str, adapters: "AdapterTable", seg: "Segments", T: int, *, x=None, y=None,
+                 v=None, r_max: int = 0) -> None:
+    """Raise ValueError unless the arguments of one compute call describe one batch.
+
+    The C side sizes its offsets and strides from T, the adapter count, the
+    dtype and r_max; arguments from different batches would make the kernels
+    index outside the buffers, so they are rejected here, before any enqueue."""
+    if seg.T != T:
+        raise ValueError(f"{name}: the segments were built for {seg.T} rows, the call has {T}")
+    if seg.num_adapters != len(adapters):
+        raise ValueError(f"{name}: the segments were built for {seg.num_adapters} adapters, "
+                         f"the table has {len(adapters)}")
+    if x is not None:
+        if x.dtype != adapters.dtype:
+            raise ValueError(f"{name}: x is {x.dtype}, the adapters are {adapters.dtype}")
+        if x.shape[1] != adapters.d_in:
+            raise ValueError(f"{name}: x has {x.shape[1]} columns, the adapters' d_in is {adapters.d_in}")
+        if x.device != adapters.device:
+            raise ValueError(f"{name}: x and the adapters are on different devices")
+    if y is not None:
+        if y.dtype != adapters.dtype:
+            raise ValueError(f"{name}: y is {y.dtype}, the adapters are {adapters.dtype}")
+        if y.shape[1] != adapters.d_out:
+            raise ValueError(f"{name}: y has {y.shape[1]} columns, the adapters' d_out is {adapters.d_out}")
+        if y.shape[0] != T:
+            raise ValueError(f"{name}: y has {y.shape[0]} rows, the call has {T}")
+        if y.device != adapters.device:
+            raise ValueError(f"{name}: y and the adapters are on different devices")
+    if v is not None:
+        if v.dtype != torch.float32:
+            raise ValueError(f"{name}: v must be float32")
+        if v.dim() != 2 or v.shape[0] != T:
+            raise ValueError(f"{name}: v must have one row per row of the call ({T})")
+        if v.shape[1] < (r_max + 7) // 8 * 8:
+            raise ValueError(f"{name}: v needs at least round_up(r_max, 8) = {(r_max + 7) // 8 * 8} columns")
+        if v.device != adapters.device:
+            raise ValueError(f"{name}: v and the adapters are on different devices")
+
+
 def lora_abi_version() -> int:
     return _abi.load().lora_abi_version()
 
@@ -111,6 +150,10 @@ class AdapterTable:
                 raise ValueError("adapter weights must share one dtype and be contiguous")
             if a.dim() != 2 or b.dim() != 2 or b.shape[1] != a.shape[0]:
                 raise ValueError("A must be [r, d_in] and B [d_out, r]")
+            if a.shape[1] != self.A[0].shape[1] or b.shape[0] != self.B[0].shape[0]:
+                raise ValueError("every A must have the same d_in and every B the same d_out")
+            if a.device != self.device or b.device != self.device:
+                raise ValueError("adapter weights must live on one device")
             host[i] = _abi.LoraAdapter(a.data_ptr(), b.data_ptr(), a.shape[0], s)
             ranks.append(int(a.shape[0]))
         self.ranks = ranks
@@ -234,6 +277,7 @@ def lora_shrink(x: torch.Tensor, adapters: AdapterTable, seg: Segments, v: Optio
     if v is None:
         v = torch.zeros((T, (r_max + 7) // 8 * 8), dtype=torch.float32, device=x.device)
     pv, _, _, ldv = _rows(v, "v")
+    _check_batch("lora_shrink", adapters, seg, T, x=x, v=v, r_max=r_max)
     lib = _abi.load()
     if ws is None:  # a caller's workspace is size-checked by the library (LORA_ERR_WORKSPACE)
         ws = torch.empty(max(lib.lora_shrink_workspace_bytes(_dtype_code(x), T, d_in, r_max), 1),
@@ -253,6 +297,7 @@ def lora_expand_add(v: torch.Tensor, adapters: AdapterTable, seg: Segments, y: t
     if Ty != T:
         raise ValueError("v and y must have the same number of rows")
     r_max = adapters.r_max if r_max is None else r_max
+    _check_batch("lora_expand_add", adapters, seg, T, y=y, v=v, r_max=r_max)
     st = _abi.load().lora_expand_add(_dtype_code(y), pv, ldv, T, d_out, adapters.ptr, len(adapters), r_max,
                                      seg.c, py, ldy, _stream(y.device))
     _abi.check("lora_expand_add", st)
@@ -275,6 +320,7 @@ def lora_forward(x: torch.Tensor, adapters: AdapterTable, seg: Segments, y: torc
         if Tv != T or v.dtype != torch.float32:
             raise ValueError("v must be fp32 with one row per row of x")
     r_max = adapters.r_max if r_max is None else r_max
+    _check_batch("lora_forward", adapters, seg, T, x=x, y=y, v=v, r_max=r_max)
     st = _abi.load().lora_forward(_dtype_code(x), px, ldx, T, d_in, d_out, adapters.ptr, len(adapters), r_max,
                                   seg.c, py, ldy, pv or None, ldv, _stream(x.device))
     _abi.check("lora_forward", st)
@@ -308,6 +354,8 @@ def lora_forward_multi(x: torch.Tensor, slices, seg: Segments, r_max: Optional[i
         arr[i] = _abi.LoraSlice(table.ptr, py, ldy, pv or None, ldv, d_out, 0)
     if r_max is None:
         r_max = max(e[0].r_max for e in entries)
+    for table, y, v in entries:
+        _check_batch("lora_forward_multi", table, seg, T, x=x, y=y, v=v, r_max=r_max)
     st = _abi.load().lora_forward_multi(_dtype_code(x), px, ldx, T, d_in, arr, len(entries), n_adapters, r_max,
                                         seg.c, _stream(x.device))
     _abi.check("lora_forward_multi", st)
@@ -324,12 +372,22 @@ def lora_backward_preemptible(x: torch.Tensor, dy: torch.Tensor, adapters: Adapt
                               seg_ft: Segments, grant: torch.Tensor, status: torch.Tensor,
                               dx: Optional[torch.Tensor] = None, v_saved: Optional[torch.Tensor] = None,
                               r_max: Optional[int] = None, ws: Optional[torch.Tensor] = None) -> None:
-    """lora_backward that yields while grant[0] == 0; status[0] becomes 0 (ran) or 1 (yielded, outputs untouched)."""
-    for name, t in (("grant", grant), ("status", status)):
-        if not t.is_cuda or t.dtype != torch.int32 or t.numel() < 1:
-            raise ValueError(f"{name} must be an int32 tensor on the GPU")
+    """lora_backward that yields while grant[0] == 0; status[0] becomes 0 (ran) or 1 (yielded, outputs untouched).
+
+    grant: int32 tensor on the GPU, or in pinned host memory (``pin_memory=True``), which the
+    host may change while the call is queued: the device reads it when the call's gates run."""
+    if not status.is_cuda or status.dtype != torch.int32 or status.numel() < 1:
+        raise ValueError("status must be an int32 tensor on the GPU")
+    if grant.dtype != torch.int32 or grant.numel() < 1:
+        raise ValueError("grant must be an int32 tensor")
+    if grant.is_cuda:
+        grant_ptr = grant.data_ptr()
+    elif grant.is_pinned():
+        grant_ptr = _abi.host_device_pointer(grant.data_ptr())
+    else:
+        raise ValueError("grant must be on the GPU or in pinned host memory")
     _backward("lora_backward_preemptible", x, dy, adapters, grads, seg_ft, dx, v_saved, r_max, ws,
-              (grant.data_ptr(), status.data_ptr()))
+              (grant_ptr, status.data_ptr()))
 
 
 def _backward(fn, x, dy, adapters, grads, seg_ft, dx, v_saved, r_max, ws, extra) -> None:
@@ -349,6 +407,16 @@ def _backward(fn, x, dy, adapters, grads, seg_ft, dx, v_saved, r_max, ws, extra)
     if len(grads.dA) != len(adapters):
         raise ValueError("the gradient table must have one entry per adapter")
     r_max = adapters.r_max if r_max is None else r_max
+    _check_batch(fn, adapters, seg_ft, T, x=x, v=v_saved, r_max=r_max)
+    if dy.dtype != adapters.dtype or dy.shape[1] != adapters.d_out or dy.device != adapters.device:
+        raise ValueError(f"{fn}: dy must be {adapters.dtype} with d_out = {adapters.d_out} columns on the adapters' device")
+    for i, (ga, gb) in enumerate(zip(grads.dA, grads.dB)):
+        if ga is None:
+            continue
+        if tuple(ga.shape) != tuple(adapters.A[i].shape) or tuple(gb.shape) != tuple(adapters.B[i].shape):
+            raise ValueError(f"{fn}: gradient entry {i} must have the shapes of A[{i}] and B[{i}]")
+        if ga.device != adapters.device or gb.device != adapters.device:
+            raise ValueError(f"{fn}: gradient entry {i} is on another device")
     lib = _abi.load()
     if ws is None:  # a caller's workspace is size-checked by the library (LORA_ERR_WORKSPACE)
         ws = torch.empty(max(lib.lora_backward_workspace_bytes(_dtype_code(x), T, d_in, d_out, r_max), 1),

@@ -120,6 +120,25 @@ def load() -> ctypes.CDLL:
     return lib
 
 
+_hip = None
+
+
+def host_device_pointer(host_ptr: int) -> int:
+    """Device address of pinned host memory (hipHostGetDevicePointer of the
+    HIP runtime already loaded by this process; never a second copy of it)."""
+    global _hip
+    load()
+    if _hip is None:
+        _hip = ctypes.CDLL("libamdhip64.so.7", mode=os.RTLD_NOLOAD | os.RTLD_LAZY)
+        _hip.hipHostGetDevicePointer.restype = ctypes.c_int
+        _hip.hipHostGetDevicePointer.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_uint]
+    out = ctypes.c_void_p()
+    rc = _hip.hipHostGetDevicePointer(ctypes.byref(out), ctypes.c_void_p(host_ptr), 0)
+    if rc != 0 or not out.value:
+        raise ValueError(f"hipHostGetDevicePointer failed ({rc}): the memory is not pinned host memory")
+    return out.value
+
+
 def status_string(status: int) -> str:
     return load().lora_status_string(int(status)).decode()
 

@@ -40,7 +40,7 @@ constexpr int kShrinkThreads = kShrinkWaves * kWave;
 // 64-element K chunks per slice (the slice's rank rows, up to 64, fill up to 64 KB of LDS).
 __host__ __device__ constexpr int shrink_slice_chunks(int dtype) { return dtype == LORA_BF16 ? 8 : 4; }
 __host__ __device__ constexpr int shrink_slices(int dtype, int K) {
-    return ((K + 63) / 64 + shrink_slice_chunks(dtype) - 1) / shrink_slice_chunks(dtype);
+    return (int)((((int64_t)K + 63) / 64 + shrink_slice_chunks(dtype) - 1) / shrink_slice_chunks(dtype));
 }
 
 struct ShrinkParams {

@@ -201,10 +201,11 @@ def test_fused_forward_small_mixed(dtype, y0_zero):
 
 
 @pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
-def test_fused_forward_configs_full_size(idx):
+@pytest.mark.parametrize("y0_zero", [False, True])
+def test_fused_forward_configs_full_size(idx, y0_zero):
     wl = _config(idx)
-    print(f"fused forward {wl.name} T={wl.T}", flush=True)
-    case = GpuCase(wl, y0_zero=idx == 2)
+    print(f"fused forward {wl.name} T={wl.T} y0_zero={y0_zero}", flush=True)
+    case = GpuCase(wl, y0_zero=y0_zero)
     _check_forward(case, TOL[wl.dtype], fused=True)
 
 

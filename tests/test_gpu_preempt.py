@@ -101,3 +101,58 @@ def test_reissued_after_yield_equals_one_granted_call():
     assert status.item() == 0
     dx_r, dA_r, dB_r, _ = c.backward()
     assert torch.equal(dx, dx_r) and _same(dA, dA_r) and _same(dB, dB_r)
+
+
+# ---------------------------------------------------------------- grant word in pinned host memory
+
+def _pinned_word(v):
+    w = torch.empty(1, dtype=torch.int32, pin_memory=True)
+    w[0] = v
+    return w
+
+
+def _queued_call(c, grant_value_at_enqueue, grant_value_later):
+    """Enqueue lora_backward_preemptible behind a long bounded spin kernel, then change
+    the pinned host grant word while the spin still runs (checked with an event that
+    completes only when the spin has ended, i.e. before the call's first gate runs)."""
+    import expand_token_adapter_amd as lb
+    from gpu_helpers import to_dev
+    wl = c.wl
+    s, n = wl.ft_start, wl.ft_count
+    dev = c.dev
+    dx0, dA0, dB0 = _initial(wl, 8)
+    dA = [torch.from_numpy(a).to(dev) for a in dA0]
+    dB = [torch.from_numpy(b).to(dev) for b in dB0]
+    grads = lb.GradTable(dA, dB)
+    seg_ft = lb.lora_segments_build(c.ids[s:s + n].contiguous(), wl.num_adapters)
+    dx = to_dev(dx0, wl.dtype, dev)
+    dy = to_dev(wl.dy, wl.dtype, dev)
+    grant, status = _pinned_word(grant_value_at_enqueue), _word(7)
+    torch.cuda.synchronize()
+    spun = torch.cuda.Event()
+    torch.cuda._sleep(400_000_000)  # bounded: a few hundred ms of clock cycles
+    spun.record()
+    lb.lora_backward_preemptible(c.x[s:s + n], dy, c.table, grads, seg_ft, grant, status, dx=dx)
+    grant[0] = grant_value_later  # from the host, while the call is queued
+    still_spinning = not spun.query()
+    torch.cuda.synchronize()
+    assert still_spinning, "the spin ended before the grant changed: the test did not test a queued call"
+    return dx, dA, dB, status, (dx0, dA0, dB0)
+
+
+def test_pinned_grant_withdrawn_while_queued_yields():
+    c = GpuCase(_config(4))
+    dx, dA, dB, status, (dx0, dA0, dB0) = _queued_call(c, 1, 0)
+    from gpu_helpers import to_dev
+    assert status.item() == 1
+    assert torch.equal(dx, to_dev(dx0, c.wl.dtype, dx.device))
+    assert _same(dA, [torch.from_numpy(a).cuda() for a in dA0])
+    assert _same(dB, [torch.from_numpy(b).cuda() for b in dB0])
+
+
+def test_pinned_grant_given_while_queued_runs():
+    c = GpuCase(_config(4))
+    dx, dA, dB, status, (dx0, dA0, dB0) = _queued_call(c, 0, 1)
+    assert status.item() == 0
+    dx_r, dA_r, dB_r, _ = c.backward(None, dx0, dA0, dB0)
+    assert torch.equal(dx, dx_r) and _same(dA, dA_r) and _same(dB, dB_r)
