@@ -23,7 +23,8 @@ from ._abi import LORA_BF16, LORA_F32, LORA_MAX_RANK, LoraError
 
 __all__ = [
     "AdapterTable", "GradTable", "Segments", "LoraError",
-    "lora_segments_build", "lora_segments_build_batch", "lora_shrink", "lora_expand_add", "lora_forward",
+    "lora_segments_build", "lora_segments_build_batch", "lora_shrink", "lora_shrink_noalloc", "lora_expand_add",
+    "lora_forward",
     "lora_forward_multi", "lora_backward", "lora_backward_preemptible", "lora_adamw_step",
     "lora_abi_version", "lora_status_string",
     "lora_segments_workspace_bytes", "lora_shrink_workspace_bytes", "lora_backward_workspace_bytes",
@@ -285,6 +286,22 @@ def lora_shrink(x: torch.Tensor, adapters: AdapterTable, seg: Segments, v: Optio
     st = lib.lora_shrink(_dtype_code(x), px, ldx, T, d_in, adapters.ptr, len(adapters), r_max, seg.c,
                          pv, ldv, ws.data_ptr(), ws.numel(), _stream(x.device))
     _abi.check("lora_shrink", st)
+    return v
+
+
+def lora_shrink_noalloc(x: torch.Tensor, adapters: AdapterTable, seg: Segments, v: torch.Tensor,
+                        r_max: Optional[int] = None) -> torch.Tensor:
+    """lora_shrink into the caller's v with the library's static device scratch as its
+    workspace: neither the library nor this binding allocates anything.  Calls that
+    overlap on one GPU share that scratch and must be ordered by the caller."""
+    _on_gpu(x, v)
+    px, T, d_in, ldx = _rows(x, "x")
+    r_max = adapters.r_max if r_max is None else r_max
+    pv, _, _, ldv = _rows(v, "v")
+    _check_batch("lora_shrink_noalloc", adapters, seg, T, x=x, v=v, r_max=r_max)
+    st = _abi.load().lora_shrink_noalloc(_dtype_code(x), px, ldx, T, d_in, adapters.ptr, len(adapters), r_max, seg.c,
+                                         pv, ldv, _stream(x.device))
+    _abi.check("lora_shrink_noalloc", st)
     return v
 
 

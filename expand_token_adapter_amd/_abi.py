@@ -16,6 +16,8 @@ LORA_ERR_INVALID_ARG = -1
 LORA_ERR_UNSUPPORTED = -2
 LORA_ERR_WORKSPACE = -3
 LORA_ERR_HIP = -4
+LORA_ERR_TOO_LARGE = -5
+LORA_NOALLOC_SCRATCH_BYTES = 32 << 20
 LORA_BF16 = 0
 LORA_F32 = 1
 LORA_MAX_RANK = 128
@@ -76,6 +78,8 @@ SIGNATURES = {
     "lora_segments_build_batch": (ctypes.c_int, [_vp, _i32, _i32, _vp]),
     "lora_shrink": (ctypes.c_int, [ctypes.c_int, _vp, _i64, _i32, _i32, _vp, _i32, _i32, LoraSegments,
                                    _vp, _i64, _vp, _sz, _vp]),
+    "lora_shrink_noalloc": (ctypes.c_int, [ctypes.c_int, _vp, _i64, _i32, _i32, _vp, _i32, _i32, LoraSegments,
+                                           _vp, _i64, _vp]),
     "lora_expand_add": (ctypes.c_int, [ctypes.c_int, _vp, _i64, _i32, _i32, _vp, _i32, _i32, LoraSegments,
                                        _vp, _i64, _vp]),
     "lora_forward": (ctypes.c_int, [ctypes.c_int, _vp, _i64, _i32, _i32, _i32, _vp, _i32, _i32, LoraSegments,

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblora_batch.so")
-SOURCES = ["segments.hip", "forward.hip", "fused.hip", "backward.hip", "optimizer.hip", "abi.hip"]
+SOURCES = ["segments.hip", "forward.hip", "fused.hip", "backward.hip", "optimizer.hip", "noalloc.hip", "abi.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -13,6 +13,7 @@ extern "C" const char* lora_status_string(int status) {
         case LORA_ERR_UNSUPPORTED: return "unsupported shape (row lengths and pitches must be multiples of 8)";
         case LORA_ERR_WORKSPACE: return "workspace missing or too small";
         case LORA_ERR_HIP: return "HIP launch failed";
+        case LORA_ERR_TOO_LARGE: return "the call needs more than the static scratch of a no-allocation entry point";
         default: return "unknown status";
     }
 }

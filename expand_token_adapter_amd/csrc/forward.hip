@@ -216,15 +216,25 @@ extern "C" size_t lora_shrink_workspace_bytes(int dtype, int32_t T, int32_t d_in
     return (size_t)shrink_part_floats(dtype, T, d_in, r_max) * sizeof(float);
 }
 
-extern "C" int lora_shrink(int dtype, const void* x, int64_t ldx, int32_t T, int32_t d_in,
-                           const lora_adapter* adapters, int32_t num_adapters, int32_t r_max, lora_segments seg,
-                           float* v, int64_t ldv, void* ws, size_t ws_bytes, void* stream) {
+namespace lora {
+// lora_shrink with its workspace given; shared with the entry point whose
+// workspace is the library's static device scratch.
+// Every check of lora_shrink except the workspace's (T == 0 passes).
+int shrink_check(int dtype, const void* x, int64_t ldx, int32_t T, int32_t d_in, const lora_adapter* adapters,
+                 int32_t num_adapters, int32_t r_max, const lora_segments& seg, const float* v, int64_t ldv) {
     int rc = check_common(dtype, T, num_adapters, r_max, adapters, seg);
     if (rc != LORA_OK) return rc;
     if (d_in < 1) return LORA_ERR_INVALID_ARG;
     if (T == 0) return LORA_OK;
     if ((rc = check_matrix(x, d_in, ldx)) != LORA_OK) return rc;
-    if ((rc = check_f32_rows(v, ldv, r_max)) != LORA_OK) return rc;
+    return check_f32_rows(v, ldv, r_max);
+}
+
+int shrink_entry(int dtype, const void* x, int64_t ldx, int32_t T, int32_t d_in, const lora_adapter* adapters,
+                 int32_t num_adapters, int32_t r_max, lora_segments seg, float* v, int64_t ldv, void* ws,
+                 size_t ws_bytes, void* stream) {
+    const int rc = shrink_check(dtype, x, ldx, T, d_in, adapters, num_adapters, r_max, seg, v, ldv);
+    if (rc != LORA_OK || T == 0) return rc;
     if (!ws || !aligned16(ws) || ws_bytes < (size_t)shrink_part_floats(dtype, T, d_in, r_max) * sizeof(float))
         return LORA_ERR_WORKSPACE;
     const SchedLayout sl = SchedLayout::make(T, num_adapters);
@@ -259,6 +269,13 @@ extern "C" int lora_shrink(int dtype, const void* x, int64_t ldx, int32_t T, int
     rp.outT = nullptr;
     rp.ldT = 0;
     return run_shrink(dtype, false, p, rp, T, num_adapters, static_cast<hipStream_t>(stream));
+}
+}  // namespace lora
+
+extern "C" int lora_shrink(int dtype, const void* x, int64_t ldx, int32_t T, int32_t d_in,
+                           const lora_adapter* adapters, int32_t num_adapters, int32_t r_max, lora_segments seg,
+                           float* v, int64_t ldv, void* ws, size_t ws_bytes, void* stream) {
+    return shrink_entry(dtype, x, ldx, T, d_in, adapters, num_adapters, r_max, seg, v, ldv, ws, ws_bytes, stream);
 }
 
 extern "C" int lora_expand_add(int dtype, const float* v, int64_t ldv, int32_t T, int32_t d_out,

@@ -40,7 +40,8 @@
  *   - Ownership: the caller allocates and owns every buffer, including
  *     workspaces (sized by the *_workspace_bytes queries) and the
  *     device-resident adapter and gradient tables.  The library allocates no
- *     memory and keeps no mutable global state; calls on different streams are
+ *     memory and keeps no mutable global state (the one exception is the
+ *     static scratch of lora_shrink_noalloc); calls on different streams are
  *     independent when they use different output and workspace buffers.
  *   - Requirements checked on the host before anything is enqueued (a failing
  *     check returns a negative status and enqueues nothing):
@@ -81,7 +82,8 @@ enum {
     LORA_ERR_INVALID_ARG = -1, /* bad pointer, size, pitch or enum */
     LORA_ERR_UNSUPPORTED = -2, /* valid but outside what the kernels cover */
     LORA_ERR_WORKSPACE = -3,   /* workspace missing or too small */
-    LORA_ERR_HIP = -4          /* a HIP launch failed */
+    LORA_ERR_HIP = -4,         /* a HIP launch failed */
+    LORA_ERR_TOO_LARGE = -5    /* needs more than a no-allocation entry point's static scratch */
 };
 
 /* Element type of x, y, dY, dX, A and B. */
@@ -197,6 +199,29 @@ int lora_segments_build_batch(const lora_segments_job* jobs, int32_t n_jobs, int
 int lora_shrink(int dtype, const void* x, int64_t ldx, int32_t T, int32_t d_in,
                 const lora_adapter* adapters, int32_t num_adapters, int32_t r_max,
                 lora_segments seg, float* v, int64_t ldv, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * lora_shrink without a workspace argument, for callers that cannot allocate
+ * device memory: code under graph capture, tight serving loops, harnesses that
+ * forbid allocation.  The split-K partials live in a static device array of
+ * the library, LORA_NOALLOC_SCRATCH_BYTES bytes, one per GPU the library runs
+ * on, held until the process ends; its device address is looked up once per
+ * device (on the first call that runs on it, that device made current and the
+ * caller's current device restored afterwards).  This call allocates nothing.
+ *   Arguments, results and errors as for lora_shrink (the kernels are the
+ *   same, so results are bit-identical to lora_shrink's); additionally
+ *   LORA_ERR_TOO_LARGE when lora_shrink_workspace_bytes(dtype, T, d_in, r_max)
+ *   exceeds LORA_NOALLOC_SCRATCH_BYTES, before anything is enqueued.
+ * Every call on one GPU shares that GPU's scratch: calls that may overlap on
+ * one GPU (other streams, other threads) race on it and must be ordered by
+ * the caller.  Nothing in the scratch needs to start at zero (every partial
+ * is written before it is read); it keeps the last call's contents.
+ */
+#define LORA_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+int lora_shrink_noalloc(int dtype, const void* x, int64_t ldx, int32_t T, int32_t d_in,
+                        const lora_adapter* adapters, int32_t num_adapters, int32_t r_max,
+                        lora_segments seg, float* v, int64_t ldv, void* stream);
 
 /*
  * Expand-add: y_t += s_{a(t)} B_{a(t)} v_t, computed in fp32 and rounded once to

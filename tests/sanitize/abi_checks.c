@@ -97,6 +97,11 @@ static void shrink_expand(void) {
     EXPECT(lora_shrink(0, FAKE, 256, 64, 256, ad, 4, 8, seg_of(1), v, 8, FAKE, need - 1, NULL) == LORA_ERR_WORKSPACE);
     EXPECT(lora_shrink(0, FAKE, 256, 64, 256, ad, 4, 8, seg_of(1), v, 8, FAKEB(4), need, NULL) == LORA_ERR_WORKSPACE);
     EXPECT(lora_shrink(0, NULL, 0, 0, 256, ad, 4, 8, seg_of(1), NULL, 0, NULL, 0, NULL) == LORA_OK);
+    EXPECT(lora_shrink_noalloc(5, FAKE, 256, 64, 256, ad, 4, 8, seg_of(1), v, 8, NULL) == LORA_ERR_INVALID_ARG);
+    EXPECT(lora_shrink_noalloc(0, FAKE, 256, 64, 256, ad, 4, 8, seg_of(1), v, 4, NULL) == LORA_ERR_INVALID_ARG);
+    EXPECT(lora_shrink_noalloc(0, NULL, 0, 0, 256, ad, 4, 8, seg_of(1), NULL, 0, NULL) == LORA_OK);
+    EXPECT(lora_shrink_noalloc(0, FAKE, 8192, 1 << 20, 8192, ad, 4, 128, seg_of(1), v, 128, NULL) ==
+           LORA_ERR_TOO_LARGE);
     EXPECT(lora_expand_add(5, v, 8, 64, 256, ad, 4, 8, seg_of(1), FAKE, 256, NULL) == LORA_ERR_INVALID_ARG);
     EXPECT(lora_expand_add(0, v, 8, 64, 0, ad, 4, 8, seg_of(1), FAKE, 256, NULL) == LORA_ERR_INVALID_ARG);
     EXPECT(lora_expand_add(0, v, 8, 64, 256, ad, 4, 8, seg_of(1), FAKEB(8), 256, NULL) == LORA_ERR_INVALID_ARG);

@@ -294,3 +294,23 @@ def test_backward_rejects(lib):
     assert call(wsb=need - 1) == _abi.LORA_ERR_WORKSPACE
     assert call(ws=FAKE + 8) == _abi.LORA_ERR_WORKSPACE
     assert call(seg=_seg(False)) == _abi.LORA_ERR_INVALID_ARG
+
+
+def test_shrink_noalloc_rejects_before_touching_the_gpu(lib):
+    bad = _abi.LORA_ERR_INVALID_ARG
+    args = dict(dtype=0, x=FAKE, ldx=256, T=64, d_in=256, adapters=FAKE, A=4, r_max=8, seg=_seg(), v=FAKE, ldv=8)
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return lib.lora_shrink_noalloc(a["dtype"], a["x"], a["ldx"], a["T"], a["d_in"], a["adapters"], a["A"],
+                                       a["r_max"], a["seg"], a["v"], a["ldv"], None)
+
+    assert call(dtype=3) == bad and call(T=-1) == bad and call(A=0) == bad and call(r_max=129) == bad
+    assert call(x=0) == bad and call(x=FAKE + 4) == bad and call(v=0) == bad and call(ldv=4) == bad
+    assert call(seg=_seg(False)) == bad
+    assert call(d_in=100, ldx=100) == _abi.LORA_ERR_UNSUPPORTED
+    assert call(T=0, x=0, v=0) == _abi.LORA_OK                               # nothing to do
+    # 16 slices x 2^20 rows x 128 ranks of fp32 partials: beyond the static scratch
+    assert call(T=1 << 20, d_in=8192, ldx=8192, r_max=128, ldv=128) == _abi.LORA_ERR_TOO_LARGE
+    assert lib.lora_shrink_workspace_bytes(0, 1 << 20, 8192, 128) > _abi.LORA_NOALLOC_SCRATCH_BYTES
