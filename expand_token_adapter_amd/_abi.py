@@ -9,7 +9,9 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "liblora_batch.so")
+# LORA_BATCH_LIB: another build of the library (e.g. one compiled with tuning
+# defines by build.build(out=..., defines=...)); the in-tree build otherwise.
+LIB_PATH = os.environ.get("LORA_BATCH_LIB") or os.path.join(_PKG, "liblora_batch.so")
 
 LORA_OK = 0
 LORA_ERR_INVALID_ARG = -1

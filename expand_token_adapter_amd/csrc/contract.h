@@ -115,11 +115,6 @@ __device__ __forceinline__ ContractAct contract_act_uniform(const ContractParams
     return c;
 }
 
-__device__ __forceinline__ int64_t wave_sum64(int64_t v) {
-#pragma unroll
-    for (int d = kWave / 2; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
-    return v;
-}
 
 template <int DT>
 struct ContractLds {

@@ -66,6 +66,13 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
     return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
+// Sum over the wave's lanes (every lane gets it).
+__device__ __forceinline__ int64_t wave_sum64(int64_t v) {
+#pragma unroll
+    for (int d = kWave / 2; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
+    return v;
+}
+
 // ---------------------------------------------------------------- MFMA
 
 __device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
@@ -340,6 +347,24 @@ __device__ __forceinline__ void lds_dma16_async(const void* src, void* lds_row) 
         :
         : "s"(m0), "v"(src)
         : "memory", "m0");
+}
+
+// Buffer resources (raw, untyped): loads through them take a 32-bit byte
+// offset from a wave-uniform base, and the hardware returns zeros for bytes at
+// or past num_records instead of touching memory there.
+typedef __amdgpu_buffer_rsrc_t buf_rsrc_t;
+constexpr int kBufDword3 = 0x00020000;  // gfx9 family: raw buffer, no format conversion
+__device__ __forceinline__ buf_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufDword3);
+}
+// A byte offset past every buffer the kernels build (they all hold fewer than
+// 2^31 bytes): a load at it returns zeros and touches no memory.
+constexpr uint32_t kBufOff = 0x80000000u;
+// 16 bytes at base + soff + voff (soff wave-uniform).  The range check
+// covers voff and the instruction's immediate offset, not soff: offsets that
+// may fall past the buffer go in voff.
+__device__ __forceinline__ u32x4_t buf_load16(buf_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
 }
 
 // s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding:

@@ -10,6 +10,13 @@
 #include "host_checks.h"
 #include "shrink.h"
 #include "expand.h"
+#include "decode.h"
+
+// Batches with at most this many rows per adapter (T <= this * num_adapters)
+// take the 16-row-tile kernels of decode.h; others the 64-row-tile kernels.
+#ifndef LORA_DECODE_ROWS_PER_ADAPTER
+#define LORA_DECODE_ROWS_PER_ADAPTER 32
+#endif
 
 using namespace lora;
 
@@ -50,9 +57,97 @@ int launch_expand_t(int ks, const ExpandParams& p, unsigned grid, hipStream_t st
     return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
+constexpr int64_t kDecMaxGrid = 2048;
+// One task per workgroup up to this many tasks: the hardware dispatcher then
+// hands out tasks of very different sizes (and the empty ones) as slots free
+// up, instead of each workgroup walking a fixed share.
+constexpr int64_t kDecShrinkMaxGrid = 1 << 16;
+
+template <int DT>
+void launch_dec_shrink(const DecShrinkParams& p, int64_t tasks, hipStream_t st) {
+    const unsigned grid = grid_for(tasks, 1, kDecShrinkMaxGrid);
+    // few tasks: more waves per workgroup (each takes a shorter run of d_in)
+    if (tasks < 512)
+        hipLaunchKernelGGL((dec_shrink_kernel<DT, 16>), dim3(grid), dim3(16 * kWave), 0, st, p);
+    else if (tasks < 1024)
+        hipLaunchKernelGGL((dec_shrink_kernel<DT, 8>), dim3(grid), dim3(8 * kWave), 0, st, p);
+    else
+        hipLaunchKernelGGL((dec_shrink_kernel<DT, 4>), dim3(grid), dim3(4 * kWave), 0, st, p);
+}
+
 }  // namespace
 
 namespace lora {
+
+// The 16-row-tile kernels address x, A_a and B_a through buffer resources
+// with 32-bit byte offsets, and use offsets from 2^31 up as "past the
+// buffer": every buffer they address must hold fewer than 2^31 bytes.
+bool dec_offsets_fit(int64_t rows_bytes, int64_t d, int32_t r_max) {
+    const int64_t lim = ((int64_t)1 << 31) - 65536;
+    return rows_bytes < lim && d * r_max * 2 < lim;
+}
+
+bool use_decode_path(int dtype, int32_t T, int32_t num_adapters) {
+    return dtype == LORA_BF16 && (int64_t)T <= (int64_t)LORA_DECODE_ROWS_PER_ADAPTER * num_adapters;
+}
+
+// v = A x on 16-row tiles (decode.h), written straight to v.
+int run_dec_shrink(int dtype, const void* x, int64_t ldx, int32_t T, int32_t d_in, const lora_adapter* adapters,
+                   int32_t num_adapters, int32_t r_max, const lora_segments& seg, float* v, int64_t ldv,
+                   int32_t v_by_pos, hipStream_t st) {
+    DecShrinkParams p{};
+    p.x = x;
+    p.ldx = ldx;
+    p.x_bytes = (uint32_t)(((int64_t)(T - 1) * ldx + d_in) * 2);
+    p.K = d_in;
+    p.adapters = adapters;
+    p.r_max = r_max;
+    p.perm = seg.perm;
+    p.sched = seg.sched;
+    p.tiles16_off = SchedLayout::make(T, num_adapters).tiles16;
+    p.v = v;
+    p.ldv = ldv;
+    p.v_by_pos = v_by_pos;
+    p.rblocks = (r_max + 15) / 16;
+    p.err = seg.err;
+    const int64_t tasks = SchedLayout::max_tiles16(T, num_adapters) * p.rblocks;
+    if (dtype != LORA_BF16) return LORA_ERR_UNSUPPORTED;
+    launch_dec_shrink<LORA_BF16>(p, tasks, st);
+    return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
+// y += s B v on 16-row tiles (decode.h): one launch of a fixed grid, each
+// workgroup a byte-balanced share of the (tile, chunk) units.
+constexpr int kDecExpandGrid = 256 * 3;  // three workgroups per CU (the kernel's occupancy)
+
+int run_dec_expand(int dtype, const float* v, int64_t ldv, int32_t v_by_pos, int32_t T, int32_t d_out,
+                   const lora_adapter* adapters, int32_t num_adapters, int32_t r_max, const lora_segments& seg,
+                   void* y, int64_t ldy, hipStream_t st) {
+    if (dtype != LORA_BF16) return LORA_ERR_UNSUPPORTED;
+    DecExpandParams p{};
+    p.v = v;
+    p.ldv = ldv;
+    p.v_by_pos = v_by_pos;
+    p.adapters = adapters;
+    p.r_max = r_max;
+    p.perm = seg.perm;
+    p.sched = seg.sched;
+    p.tiles16_off = SchedLayout::make(T, num_adapters).tiles16;
+    p.y = y;
+    p.ldy = ldy;
+    p.y_bytes = (uint32_t)(((int64_t)(T - 1) * ldy + d_out) * 2);
+    p.N = d_out;
+    p.err = seg.err;
+    // small batches (or more tiles than the plan holds): one tile slice per
+    // workgroup; otherwise a fixed grid with byte-balanced ranges
+    const int64_t nch = (d_out + kDecChunk - 1) / kDecChunk;
+    const int64_t tiles = SchedLayout::max_tiles16(T, num_adapters);
+    p.balanced = tiles * nch > 8192 && tiles <= kPlanMaxTiles;
+    const unsigned grid = p.balanced ? (unsigned)kDecExpandGrid
+                                     : grid_for(tiles * ((nch + kDirectChunks - 1) / kDirectChunks), 1, INT32_MAX);
+    hipLaunchKernelGGL(dec_expand_kernel<LORA_BF16>, dim3(grid), dim3(kDecExpWaves * kWave), 0, st, p);
+    return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
 
 // Fixed-order sum of the K-slice partials of one 16-row tile per workgroup.
 // Lane (n, q) = (lane % 16, lane / 16) holds ranks 16 j + 4 q .. + 3 of row
@@ -237,6 +332,9 @@ int shrink_entry(int dtype, const void* x, int64_t ldx, int32_t T, int32_t d_in,
     if (rc != LORA_OK || T == 0) return rc;
     if (!ws || !aligned16(ws) || ws_bytes < (size_t)shrink_part_floats(dtype, T, d_in, r_max) * sizeof(float))
         return LORA_ERR_WORKSPACE;
+    if (use_decode_path(dtype, T, num_adapters) && dec_offsets_fit((int64_t)T * ldx * 2, d_in, r_max))
+        return run_dec_shrink(dtype, x, ldx, T, d_in, adapters, num_adapters, r_max, seg, v, ldv, 0,
+                              static_cast<hipStream_t>(stream));
     const SchedLayout sl = SchedLayout::make(T, num_adapters);
     ShrinkParams p{};
     p.x = x;
@@ -299,6 +397,9 @@ extern "C" int lora_expand_add(int dtype, const float* v, int64_t ldv, int32_t T
     p.ldy = ldy;
     p.N = d_out;
     p.err = seg.err;
+    if (use_decode_path(dtype, T, num_adapters) && dec_offsets_fit((int64_t)T * ldy * 2, d_out, r_max))
+        return run_dec_expand(dtype, v, ldv, 0, T, d_out, adapters, num_adapters, r_max, seg, y, ldy,
+                              static_cast<hipStream_t>(stream));
     return run_expand(dtype, false, p, T, num_adapters, r_max, static_cast<hipStream_t>(stream));
 }
 

@@ -138,6 +138,61 @@ def _small_mixed(dtype, seed=0):
                             scales=[2.0, 0.5, 1.0, -1.5, 2.0, 3.0, 0.25])
 
 
+def _small_decode(dtype, seed=0, d_out=1032):
+    """Few rows per adapter (the 16-row-tile kernels for bf16): 40 adapters with ranks
+    1..128 (several not a multiple of 8 or 16), rows without adapters, 1..16-row tiles,
+    and 1032 output columns (two 1024-column ranges, the second one ragged)."""
+    rng = np.random.default_rng(100 + seed)
+    A = 40
+    ranks = [8, 24, 5, 40, 128, 16, 64, 1, 12, 32, 96, 8, 16, 72, 3, 48, 128, 20, 56, 8] * 2
+    ids = np.concatenate([rng.integers(-1, A, size=260), np.full(19, 7), np.full(33, 4)]).astype(np.int32)
+    ids = ids[rng.permutation(len(ids))]
+    scales = rng.choice([2.0, 0.5, -1.25, 3.0], size=A)
+    return workloads.custom(ids, ranks, 328, d_out, dtype, seed=seed, name="small-decode", scales=scales)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("y0_zero", [False, True])
+@pytest.mark.parametrize("d_out", [1032, 200])
+def test_forward_small_decode(dtype, y0_zero, d_out):
+    case = GpuCase(_small_decode(dtype, d_out=d_out), y0_zero=y0_zero)
+    _check_forward(case, TOL[dtype])
+
+
+def test_forward_decode_deterministic_and_b_zero_identity():
+    wl = _small_decode("bf16")
+    case = GpuCase(wl, y0_zero=True)
+    y1, v1, _ = case.forward()
+    y2, v2, _ = case.forward()
+    assert torch.equal(y1, y2) and torch.equal(v1, v2)
+    wl0 = _small_decode("bf16")
+    wl0.B = [np.zeros_like(b) for b in wl0.B]
+    c0 = GpuCase(wl0)
+    y, _, _ = c0.forward()
+    assert torch.equal(y, c0.y0)
+    # columns r_a .. round_up(r_a, 8) - 1 of v are zero
+    for a, r in enumerate(wl.ranks):
+        rows = torch.from_numpy(wl.ids == a).cuda()
+        hi = (r + 7) // 8 * 8
+        if rows.any() and hi > r:
+            assert not v1[rows][:, r:hi].any()
+
+
+def test_forward_decode_bad_table_entries_are_skipped_and_counted():
+    wl = _small_decode("bf16")
+    case = GpuCase(wl)
+    y = case.y0.clone()
+    seg = lb.lora_segments_build(case.ids, wl.num_adapters)
+    v = lb.lora_shrink(case.x, case.table, seg, r_max=64)
+    lb.lora_expand_add(v, case.table, seg, y, r_max=64)
+    torch.cuda.synchronize()
+    assert int(seg.err.item()) > 0
+    big = torch.from_numpy(np.isin(wl.ids, [a for a, r in enumerate(wl.ranks) if r > 64])).cuda()
+    assert torch.equal(y[big], case.y0[big])
+    ok = torch.from_numpy(wl.ids == 3).cuda()  # rank 40
+    assert not torch.equal(y[ok], case.y0[ok])
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("y0_zero", [False, True])
 def test_forward_small_mixed(dtype, y0_zero):
