@@ -387,6 +387,9 @@ class Bench:
         self.fused, self.adamw = fused, adamw
         T, s, n = wl.T, wl.ft_start, wl.ft_count
         self.has_ft = has_ft = n > 0
+        # The fine-tuning job knows the adapters it trains (the reserved
+        # adapter), so its backward passes their largest rank as r_max.
+        self.r_ft = max(int(wl.ranks[a]) for a in set(wl.ft_ids.tolist())) if has_ft else 0
 
         def dev_bf16(a):
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -413,7 +416,7 @@ class Bench:
                 st["grads"] = lb.GradTable(st["dA"], st["dB"])
                 st["seg_ft"] = lb.Segments(n, wl.num_adapters, dev)
                 st["ws"] = torch.empty(lb.lora_backward_workspace_bytes(torch.bfloat16, n, wl.d_in, wl.d_out,
-                                                                        st["table"].r_max),
+                                                                        self.r_ft),
                                        dtype=torch.uint8, device=dev)
                 if adamw:
                     # AdamW state of the fine-tuning adapter's A and B: fp32 master copies and moments
@@ -455,10 +458,11 @@ class Bench:
         vs = st["v"][s:s + n] if v_saved else None
         if self.grant is not None:
             self.lb.lora_backward_preemptible(st["x"][s:s + n], st["dy"], st["table"], st["grads"], st["seg_ft"],
-                                              self.grant, self.status, dx=st["dx"], v_saved=vs, ws=st["ws"])
+                                              self.grant, self.status, dx=st["dx"], v_saved=vs, r_max=self.r_ft,
+                                              ws=st["ws"])
             return
         self.lb.lora_backward(st["x"][s:s + n], st["dy"], st["table"], st["grads"], st["seg_ft"], dx=st["dx"],
-                              v_saved=vs, ws=st["ws"])
+                              v_saved=vs, r_max=self.r_ft, ws=st["ws"])
 
     def step(self, st, ev=None, ph=None):
         # ev: events around the dominant kernel (and the optimizer); ph: events at

@@ -10,12 +10,19 @@
 // The workspace holds g (by sorted position, row- and rank-major), v
 // (rank-major), the shrinks' split-K partials and the contraction's partial
 // tiles of tiles cut between workgroups.
+//
+// For bf16 calls with r_max <= 16 and dY the wider stream (d_out >= 2 d_in)
+// the two products that read dY run in one pass over it (dy_pass_kernel: g
+// partials and dB); g's partials are summed by the shrink's reduce kernel,
+// the contraction computes dA only, and the dB tiles cut between workgroups
+// are added in the launch of the dX expand.
 #include <algorithm>
 
 #include "host_checks.h"
 #include "shrink.h"
 #include "expand.h"
 #include "contract.h"
+#include "bwd_stream.h"
 
 using namespace lora;
 
@@ -26,13 +33,17 @@ int64_t shrink_part_ld(int32_t r_max);
 int64_t shrink_part_floats(int dtype, int32_t T, int32_t K, int32_t r_max);
 int expand_plan(const ExpandParams& p, int32_t T, int32_t num_adapters, int32_t r_max, ExpandParams* q,
                 unsigned* grid);
+int launch_shrink_reduce(int32_t r_max, const ReduceParams& rp, int32_t T, int32_t num_adapters, hipStream_t st);
 
 // Workspace layout of lora_backward (fp32 elements): g by sorted position
-// (row-major and rank-major), v rank-major, and the split-K partials of the
-// shrinks (reused by the g and v passes, which run one after the other).
+// (row-major and rank-major), v rank-major (two-pass path) or by sorted
+// position (streaming path, recomputed v), the split-K partials of the shrinks
+// or the streaming path's g partials (reused by the passes, which run one
+// after the other), and the partial tiles of the stream-K kernels.
 struct BwdWs {
     int64_t ldg, ldT;               // pitch of g rows; pitch of the rank-major arrays
-    int64_t g, gT, vT, part, fix, fix_meta, total; // offsets
+    int64_t g, gT, vT, vpos, part, fix, fix_meta, dyfix, dymeta, total; // offsets
+    static int32_t dy_slices(int64_t d_out) { return (int32_t)((d_out + kDyCols - 1) / kDyCols); }
     static BwdWs make(int dtype, int64_t T, int64_t d_in, int64_t d_out, int64_t r_max) {
         BwdWs w;
         w.ldg = round_up(r_max, 8);
@@ -40,41 +51,50 @@ struct BwdWs {
         w.g = 0;
         w.gT = round_up(w.g + T * w.ldg, 64);
         w.vT = round_up(w.gT + r_max * w.ldT, 64);
-        w.part = round_up(w.vT + r_max * w.ldT, 64);
-        const int64_t np = std::max(shrink_part_floats(dtype, (int32_t)T, (int32_t)d_in, (int32_t)r_max),
-                                    shrink_part_floats(dtype, (int32_t)T, (int32_t)d_out, (int32_t)r_max));
+        w.vpos = round_up(w.vT + r_max * w.ldT, 64);
+        w.part = round_up(w.vpos + T * w.ldg, 64);
+        int64_t np = std::max(shrink_part_floats(dtype, (int32_t)T, (int32_t)d_in, (int32_t)r_max),
+                              shrink_part_floats(dtype, (int32_t)T, (int32_t)d_out, (int32_t)r_max));
+        np = std::max(np, (int64_t)dy_slices(d_out) * (T > 0 ? T : 1) * 16);
         w.fix = round_up(w.part + np, 64);
         w.fix_meta = w.fix + (int64_t)kContractGrid * 2 * kFixFloats;
-        w.total = round_up(w.fix_meta + (int64_t)kContractGrid * 2 * kFixMeta, 64);
+        w.dyfix = round_up(w.fix_meta + (int64_t)kContractGrid * 2 * kFixMeta, 64);
+        w.dymeta = w.dyfix + (int64_t)kStGrid * 2 * kDyFixFloats;
+        w.total = round_up(w.dymeta + (int64_t)kStGrid * 2 * kStFixMeta, 64);
         return w;
     }
 };
 }  // namespace lora
 
 namespace {
-// dX += s A^T g on the first n_expand workgroups and the contraction's fix-up
-// of cut tiles on the kContractGrid after them: one launch for two
-// independent steps (the fix-up's few, latency-bound workgroups run beside
+// dX += s A^T g on the first n_expand workgroups, the contraction's fix-up of
+// cut tiles on the kContractGrid after them and (streaming path) the fix-up
+// of the dB tiles cut by dy_pass_kernel on n_dy more: one launch for
+// independent steps (the fix-ups' few, latency-bound workgroups run beside
 // the expand's).
 template <int DT, int KS>
 __global__ __launch_bounds__(kExpandWaves * kWave) __attribute__((amdgpu_waves_per_eu(KS == 4 ? 2 : 3)))
-void dx_fixup_kernel(ExpandParams ep, ContractParams cp, int n_expand) {
-    static_assert(kExpandWaves == 4, "the fix-up runs on 4-wave workgroups");
-    if ((int)blockIdx.x < n_expand)
-        expand_body<DT, true, KS>(ep, blockIdx.x, n_expand);
+void dx_fixup_kernel(ExpandParams ep, ContractParams cp, DyParams dp, int n_expand) {
+    static_assert(kExpandWaves == 4, "the fix-ups run on 4-wave workgroups");
+    const int b = (int)blockIdx.x;
+    if (b < n_expand)
+        expand_body<DT, true, KS>(ep, b, n_expand);
+    else if (b < n_expand + kContractGrid)
+        contract_fixup_body(cp, kContractGrid, b - n_expand);
     else
-        contract_fixup_body(cp, kContractGrid, (int)blockIdx.x - n_expand);
+        dy_fixup_body(dp, b - n_expand - kContractGrid);
 }
 
 template <int DT>
-void launch_dx_fixup(int ks, const ExpandParams& ep, const ContractParams& cp, unsigned n_expand, hipStream_t st) {
-    const dim3 grid(n_expand + kContractGrid), block(kExpandWaves * kWave);
+void launch_dx_fixup(int ks, const ExpandParams& ep, const ContractParams& cp, const DyParams& dp, unsigned n_expand,
+                     unsigned n_dy, hipStream_t st) {
+    const dim3 grid(n_expand + kContractGrid + n_dy), block(kExpandWaves * kWave);
     if (ks == 1)
-        hipLaunchKernelGGL((dx_fixup_kernel<DT, 1>), grid, block, 0, st, ep, cp, (int)n_expand);
+        hipLaunchKernelGGL((dx_fixup_kernel<DT, 1>), grid, block, 0, st, ep, cp, dp, (int)n_expand);
     else if (ks == 2)
-        hipLaunchKernelGGL((dx_fixup_kernel<DT, 2>), grid, block, 0, st, ep, cp, (int)n_expand);
+        hipLaunchKernelGGL((dx_fixup_kernel<DT, 2>), grid, block, 0, st, ep, cp, dp, (int)n_expand);
     else
-        hipLaunchKernelGGL((dx_fixup_kernel<DT, 4>), grid, block, 0, st, ep, cp, (int)n_expand);
+        hipLaunchKernelGGL((dx_fixup_kernel<DT, 4>), grid, block, 0, st, ep, cp, dp, (int)n_expand);
 }
 }  // namespace
 
@@ -97,6 +117,20 @@ __global__ __launch_bounds__(kWave) void bwd_gate_kernel(const int32_t* grant, i
     __hip_atomic_store(status, (before != 0 || g == 0) ? 1 : 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// The streaming pass over dY (dy_pass_kernel) for bf16 calls whose adapters
+// all have rank <= 16 and whose dY rows are at least twice as wide as their x
+// rows, when its 32-bit buffer offsets cover dY, v and the g partials.  (It
+// replaces the g shrink and the dB half of the contraction; measured on one
+// MI355X it wins where dY is the dominant stream, e.g. 4096 -> 14336, and
+// loses where the two halves are equal, e.g. 5120 -> 5120, to its fixed
+// per-workgroup latency.)
+bool use_stream_path(int dtype, int32_t T, int64_t lddy, int32_t d_in, int32_t d_out, int32_t r_max,
+                     const float* v_saved, int64_t ldv) {
+    const int64_t lim = (int64_t)1 << 31;
+    return dtype == LORA_BF16 && r_max <= kStMaxRank && d_out >= 2 * (int64_t)d_in && (int64_t)T * lddy * 2 < lim &&
+           (int64_t)BwdWs::dy_slices(d_out) * T * 64 < lim && (!v_saved || (int64_t)T * ldv * 4 < lim);
+}
+
 int backward_impl(int dtype, const void* x, int64_t ldx, const void* dy, int64_t lddy, void* dx, int64_t lddx,
                   int32_t T_ft, int32_t d_in, int32_t d_out, const lora_adapter* adapters,
                   const lora_adapter_grad* grads, int32_t num_adapters, int32_t r_max, lora_segments seg_ft,
@@ -117,21 +151,22 @@ int backward_impl(int dtype, const void* x, int64_t ldx, const void* dy, int64_t
     hipStream_t st = static_cast<hipStream_t>(stream);
     const SchedLayout sl = SchedLayout::make(T_ft, num_adapters);
     float* wsf = static_cast<float*>(ws);
-    // preemption: gate before the skinny part (whose kernels then skip their
-    // work if it yielded) and before the output part (all or nothing)
+    const bool one_pass = use_stream_path(dtype, T_ft, lddy, d_in, d_out, r_max, v_saved, ldv);
+    // Preemption: a gate at the start, and one more after a recompute of v;
+    // everything after the last gate (every kernel that writes dA, dB or dX)
+    // runs completely or skips its work.
     if (grant) {
         hipLaunchKernelGGL(bwd_gate_kernel, dim3(1), dim3(kWave), 0, st, grant, status, 1);
         if (hipGetLastError() != hipSuccess) return LORA_ERR_HIP;
     }
+    const int32_t* stop = grant ? status : nullptr;
     float* g = wsf + w.g;
     float* gT = wsf + w.gT;
     float* vT = wsf + w.vT;
+    float* vpos = wsf + w.vpos;
 
-    // 1. g = B^T dy, written by sorted position (row-major for dX, rank-major for dA).
+    // Split-K shrink over the rows' sorted positions (g = B^T dy, or v = A x).
     ShrinkParams sp{};
-    sp.x = dy;
-    sp.ldx = lddy;
-    sp.K = d_out;
     sp.adapters = adapters;
     sp.r_max = r_max;
     sp.perm = seg_ft.perm;
@@ -140,34 +175,24 @@ int backward_impl(int dtype, const void* x, int64_t ldx, const void* dy, int64_t
     sp.part = wsf + w.part;
     sp.ldp = shrink_part_ld(r_max);
     sp.slice_stride = (int64_t)T_ft * sp.ldp;
-    sp.nslices = shrink_slices(dtype, d_out);
     sp.err = seg_ft.err;
     sp.rgroups = rank_groups(r_max);
-    sp.stop = grant ? status : nullptr;
+    sp.stop = stop;
     ReduceParams rp{};
     rp.part = sp.part;
     rp.ldp = sp.ldp;
     rp.slice_stride = sp.slice_stride;
-    rp.nslices = sp.nslices;
     rp.adapters = adapters;
     rp.r_max = r_max;
     rp.perm = seg_ft.perm;
     rp.sched = seg_ft.sched;
     rp.tiles16_off = sl.tiles16;
-    rp.out = g;
-    rp.ldo = w.ldg;
     rp.out_by_pos = 1;
-    rp.outT = gT;
     rp.ldT = w.ldT;
-    rp.stop = sp.stop;
-    // 2. v = A x, rank-major by sorted position: the caller's v, copied by the
-    //    reduce of g, or a second shrink.
-    if (v_saved) {
-        rp.vsrc = v_saved;
-        rp.ldvsrc = ldv;
-        rp.vT = vT;
-    }
-    if ((rc = run_shrink(dtype, true, sp, rp, T_ft, num_adapters, st)) != LORA_OK) return rc;
+    rp.stop = stop;
+
+    // v = A x when the caller did not save it: by sorted position for the
+    // one-pass kernel, rank-major for the contraction.
     if (!v_saved) {
         ShrinkParams vp = sp;
         vp.x = x;
@@ -176,17 +201,75 @@ int backward_impl(int dtype, const void* x, int64_t ldx, const void* dy, int64_t
         vp.nslices = shrink_slices(dtype, d_in);
         ReduceParams vr = rp;
         vr.nslices = vp.nslices;
-        vr.out = nullptr;
-        vr.outT = vT;
-        vr.vsrc = nullptr;
+        vr.out = one_pass ? vpos : nullptr;
+        vr.ldo = w.ldg;
+        vr.outT = one_pass ? nullptr : vT;
         if ((rc = run_shrink(dtype, false, vp, vr, T_ft, num_adapters, st)) != LORA_OK) return rc;
+        if (grant) {
+            hipLaunchKernelGGL(bwd_gate_kernel, dim3(1), dim3(kWave), 0, st, grant, status, 0);
+            if (hipGetLastError() != hipSuccess) return LORA_ERR_HIP;
+        }
     }
 
-    // 3. dA += s g^T x, dB += s dy^T v.
-    if (grant) {
-        hipLaunchKernelGGL(bwd_gate_kernel, dim3(1), dim3(kWave), 0, st, grant, status, 0);
+    DyParams dp{};
+    if (one_pass) {
+        // g partials and dB from one read of dY, then g = the sum of the partials.
+        dp.dy = dy;
+        dp.lddy = lddy;
+        dp.dy_bytes = (uint32_t)(((int64_t)(T_ft - 1) * lddy + d_out) * 2);
+        dp.d_out = d_out;
+        dp.v = v_saved ? v_saved : vpos;
+        dp.ldv = v_saved ? ldv : w.ldg;
+        dp.v_bytes = (uint32_t)(((int64_t)(T_ft - 1) * dp.ldv + r_max) * 4);
+        dp.v_by_pos = v_saved ? 0 : 1;
+        dp.grads = grads;
+        dp.perm = seg_ft.perm;
+        dp.T = T_ft;
+        dp.gpart = wsf + w.part;
+        dp.fix = wsf + w.dyfix;
+        dp.walk.sched = seg_ft.sched;
+        dp.walk.active_off = sl.active;
+        dp.walk.adapters = adapters;
+        dp.walk.offsets = seg_ft.offsets;
+        dp.walk.r_max = r_max;
+        dp.walk.nslices = BwdWs::dy_slices(d_out);
+        dp.walk.fix_meta = reinterpret_cast<int32_t*>(wsf + w.dymeta);
+        dp.gpart_bytes = (uint32_t)((int64_t)dp.walk.nslices * T_ft * 64);
+        dp.err = seg_ft.err;
+        dp.stop = stop;
+        hipLaunchKernelGGL(dy_pass_kernel, dim3(kStGrid), dim3(kStWaves * kWave), 0, st, dp);
         if (hipGetLastError() != hipSuccess) return LORA_ERR_HIP;
+        ReduceParams gr = rp;
+        gr.part = dp.gpart;
+        gr.ldp = 16;
+        gr.slice_stride = (int64_t)T_ft * 16;
+        gr.nslices = dp.walk.nslices;
+        gr.out = g;
+        gr.ldo = w.ldg;
+        gr.outT = gT;
+        if ((rc = launch_shrink_reduce(r_max, gr, T_ft, num_adapters, st)) != LORA_OK) return rc;
+    } else {
+        // g = B^T dy by the split-K shrink; its reduce also lays out a saved v
+        // rank-major for the contraction.
+        ShrinkParams gp = sp;
+        gp.x = dy;
+        gp.ldx = lddy;
+        gp.K = d_out;
+        gp.nslices = shrink_slices(dtype, d_out);
+        ReduceParams gr = rp;
+        gr.nslices = gp.nslices;
+        gr.out = g;
+        gr.ldo = w.ldg;
+        gr.outT = gT;
+        if (v_saved) {
+            gr.vsrc = v_saved;
+            gr.ldvsrc = ldv;
+            gr.vT = vT;
+        }
+        if ((rc = run_shrink(dtype, true, gp, gr, T_ft, num_adapters, st)) != LORA_OK) return rc;
     }
+
+    // dA += s g^T x (and, on the two-pass path, dB += s dy^T v).
     ContractParams cp{};
     cp.x = x;
     cp.ldx = ldx;
@@ -205,12 +288,12 @@ int backward_impl(int dtype, const void* x, int64_t ldx, const void* dy, int64_t
     cp.d_in = d_in;
     cp.d_out = d_out;
     cp.ncb_in = (d_in + 63) / 64;
-    cp.ncb_out = (d_out + 63) / 64;
+    cp.ncb_out = one_pass ? 0 : (d_out + 63) / 64;
     cp.rgroups = (r_max + 16 * kContractMB - 1) / (16 * kContractMB);
     cp.err = seg_ft.err;
     cp.fix = wsf + w.fix;
     cp.fix_meta = reinterpret_cast<int32_t*>(wsf + w.fix_meta);
-    cp.stop = grant ? status : nullptr;
+    cp.stop = stop;
     // kContractGrid workgroups (a multiple of the 8 XCDs) split the work evenly
     if (dtype == LORA_BF16)
         hipLaunchKernelGGL(contract_kernel<LORA_BF16>, dim3(kContractGrid), dim3(contract_waves<LORA_BF16>() * kWave),
@@ -220,7 +303,11 @@ int backward_impl(int dtype, const void* x, int64_t ldx, const void* dy, int64_t
                            st, cp);
     if (hipGetLastError() != hipSuccess) return LORA_ERR_HIP;
 
-    // 4. dX += s A^T g, in the launch of the contraction's fix-up.
+    // dX += s A^T g and the fix-ups, in one launch.
+    const unsigned n_dy = one_pass ? kStGrid * kDyFixParts : 0;
+    ExpandParams q{};
+    unsigned n_expand = 0;
+    int ks = 1;
     if (dx) {
         ExpandParams ep{};
         ep.v = g;
@@ -234,16 +321,15 @@ int backward_impl(int dtype, const void* x, int64_t ldx, const void* dy, int64_t
         ep.ldy = lddx;
         ep.N = d_in;
         ep.err = seg_ft.err;
-        ep.stop = cp.stop;
-        ExpandParams q;
-        unsigned n_expand;
-        const int ks = expand_plan(ep, T_ft, num_adapters, r_max, &q, &n_expand);
-        if (dtype == LORA_BF16)
-            launch_dx_fixup<LORA_BF16>(ks, q, cp, n_expand, st);
-        else
-            launch_dx_fixup<LORA_F32>(ks, q, cp, n_expand, st);
-    } else {
+        ep.stop = stop;
+        ks = expand_plan(ep, T_ft, num_adapters, r_max, &q, &n_expand);
+    }
+    if (!dx && !one_pass) {
         hipLaunchKernelGGL(contract_fixup_kernel, dim3(kContractGrid), dim3(4 * kWave), 0, st, cp, (int)kContractGrid);
+    } else if (dtype == LORA_BF16) {
+        launch_dx_fixup<LORA_BF16>(ks, q, cp, dp, n_expand, n_dy, st);
+    } else {
+        launch_dx_fixup<LORA_F32>(ks, q, cp, dp, n_expand, n_dy, st);
     }
     return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }

@@ -251,6 +251,8 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void shrink_reduce_kernel(Red
     }
 }
 
+int launch_shrink_reduce(int32_t r_max, const ReduceParams& rp, int32_t T, int32_t num_adapters, hipStream_t st);
+
 // Shared by the forward and the backward (declared in backward.hip): the
 // split-K shrink into partials, then their fixed-order sum.
 int run_shrink(int dtype, bool trans_w, const ShrinkParams& p, const ReduceParams& rp, int32_t T, int32_t num_adapters,
@@ -262,13 +264,18 @@ int run_shrink(int dtype, bool trans_w, const ShrinkParams& p, const ReduceParam
     const int rc = dtype == LORA_BF16 ? launch_shrink_t<LORA_BF16>(trans_w, p, grid, st)
                                       : launch_shrink_t<LORA_F32>(trans_w, p, grid, st);
     if (rc != LORA_OK) return rc;
+    return launch_shrink_reduce(rp.r_max, rp, T, num_adapters, st);
+}
+
+// The fixed-order sum of split-K partials (one workgroup per 16-row tile).
+int launch_shrink_reduce(int32_t r_max, const ReduceParams& rp, int32_t T, int32_t num_adapters, hipStream_t st) {
     const unsigned rgrid = (unsigned)std::min<int64_t>(SchedLayout::max_tiles16(T, num_adapters), kMaxGrid);
     const dim3 rb(kReduceWaves * kWave);
-    if (rp.r_max <= 16)
+    if (r_max <= 16)
         hipLaunchKernelGGL(shrink_reduce_kernel<1>, dim3(rgrid), rb, 0, st, rp);
-    else if (rp.r_max <= 32)
+    else if (r_max <= 32)
         hipLaunchKernelGGL(shrink_reduce_kernel<2>, dim3(rgrid), rb, 0, st, rp);
-    else if (rp.r_max <= 64)
+    else if (r_max <= 64)
         hipLaunchKernelGGL(shrink_reduce_kernel<4>, dim3(rgrid), rb, 0, st, rp);
     else
         hipLaunchKernelGGL(shrink_reduce_kernel<8>, dim3(rgrid), rb, 0, st, rp);

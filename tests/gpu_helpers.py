@@ -56,8 +56,12 @@ class GpuCase:
         torch.cuda.synchronize()
         return y, v, seg
 
-    def backward(self, v_saved=None, dx0=None, dA0=None, dB0=None, with_dx=True, grant=None, status=None):
-        """lora_backward, or lora_backward_preemptible when a grant word is given."""
+    def backward(self, v_saved=None, dx0=None, dA0=None, dB0=None, with_dx=True, grant=None, status=None,
+                 r_max=None, grads_none=()):
+        """lora_backward, or lora_backward_preemptible when a grant word is given.
+
+        r_max: passed to the call (None: the table's); grads_none: adapters given no
+        gradient entry."""
         wl = self.wl
         s, n = wl.ft_start, wl.ft_count
         dev = self.dev
@@ -65,17 +69,18 @@ class GpuCase:
               else torch.from_numpy(dA0[i]).float().to(dev) for i, a in enumerate(wl.A)]
         dB = [torch.zeros(b.shape, dtype=torch.float32, device=dev) if dB0 is None
               else torch.from_numpy(dB0[i]).float().to(dev) for i, b in enumerate(wl.B)]
-        grads = lb.GradTable(dA, dB)
+        grads = lb.GradTable([None if i in grads_none else t for i, t in enumerate(dA)],
+                             [None if i in grads_none else t for i, t in enumerate(dB)])
         seg_ft = lb.lora_segments_build(self.ids[s:s + n].contiguous(), wl.num_adapters)
         dx = None
         if with_dx:
             dx = torch.zeros((n, wl.d_in), dtype=self.x.dtype, device=dev) if dx0 is None else to_dev(dx0, wl.dtype, dev)
         dy = to_dev(wl.dy, wl.dtype, dev)
         if grant is None:
-            lb.lora_backward(self.x[s:s + n], dy, self.table, grads, seg_ft, dx=dx, v_saved=v_saved)
+            lb.lora_backward(self.x[s:s + n], dy, self.table, grads, seg_ft, dx=dx, v_saved=v_saved, r_max=r_max)
         else:
             lb.lora_backward_preemptible(self.x[s:s + n], dy, self.table, grads, seg_ft, grant, status, dx=dx,
-                                         v_saved=v_saved)
+                                         v_saved=v_saved, r_max=r_max)
         torch.cuda.synchronize()
         return dx, dA, dB, seg_ft
 
