@@ -322,15 +322,16 @@ int lora_backward(int dtype, const void* x, int64_t ldx, const void* dy, int64_t
  * prefill through a shared GPU-grant flag that the backward checks at every
  * layer boundary: the inference side clears the flag before a step with
  * prefill rows and sets it again afterwards.  Here the flag is checked on the
- * device at two points of the call: before the skinny part (g = B^T dy, v) and
- * before the output part (dA, dB, dX).
+ * device at the start of the call and, when v_saved is NULL, again after the
+ * recompute of v; every kernel that writes dA, dB or dX runs after the last
+ * check.
  *   grant: int32 readable by the device (device memory, or host memory mapped
  *          for the device), read with system-scope loads; nonzero = granted.
  *   status: device int32, written by the call: 0 = the backward ran to the
- *          end; 1 = it yielded: the grant was zero at one of the two points,
- *          and dA, dB and dX are left exactly as they were (the output part
- *          runs completely or not at all; the kernels of a yielded part skip
- *          their work).  The caller re-issues the call once granted again.
+ *          end; 1 = it yielded: the grant was zero at a check, and dA, dB and
+ *          dX are left exactly as they were (the kernels after a check that
+ *          yielded skip their work, so the outputs are written completely or
+ *          not at all).  The caller re-issues the call once granted again.
  *          Read it after the call has completed on the stream.
  * Other arguments, results and errors as for lora_backward; additionally
  * LORA_ERR_INVALID_ARG for a NULL or misaligned grant / status.  With
