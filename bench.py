@@ -307,7 +307,7 @@ def cost_model_report(reps: int = 10):
     samples = cm.calibrate(reps=reps)
     model = cm.fit_samples(samples)
     errs = cm.relative_errors(model, samples)
-    for op in cm.OPS:
+    for op in sorted(errs):
         e = np.abs(errs[op])
         print(json.dumps({"cost_model": op, "coef": dict(zip(cm.FEATURES, model.coef[op].tolist())),
                           "calibration_samples": int(e.size), "median_abs_rel_err": float(np.median(e)),
@@ -337,10 +337,12 @@ def cost_model_report(reps: int = 10):
             dy, dx = dev_e(wl.dy), torch.zeros((n, wl.d_in), dtype=torch.bfloat16, device=dev)
             grads = lb.GradTable([torch.zeros(a.shape, dtype=torch.float32, device=dev) for a in A],
                                  [torch.zeros(b.shape, dtype=torch.float32, device=dev) for b in B])
-            bws = torch.empty(lb.lora_backward_workspace_bytes(torch.bfloat16, n, wl.d_in, wl.d_out, table.r_max),
+            r_ft = max(int(wl.ranks[a]) for a in set(wl.ft_ids.tolist()))
+            bws = torch.empty(lb.lora_backward_workspace_bytes(torch.bfloat16, n, wl.d_in, wl.d_out, r_ft),
                               dtype=torch.uint8, device=dev)
             calls["backward"] = (lambda: lb.lora_backward(x[s:s + n], dy, table, grads, seg_ft, dx=dx,
-                                                          v_saved=v[s:s + n], ws=bws), wl.ids[s:s + n])
+                                                          v_saved=v[s:s + n], r_max=r_ft, ws=bws),
+                                 wl.ids[s:s + n])
         for op, (f, op_ids) in calls.items():
             f()
             torch.cuda.synchronize()
@@ -351,7 +353,8 @@ def cost_model_report(reps: int = 10):
             e1.record()
             torch.cuda.synchronize()
             meas = e0.elapsed_time(e1) * 1e-3 / reps
-            pred = model.predict(op, op_ids, wl.ranks, wl.d_in, wl.d_out)
+            pred = model.predict(op, op_ids, wl.ranks, wl.d_in, wl.d_out,
+                                 r_max=r_ft if op == "backward" else 0)
             print(json.dumps({"workload": workloads.CONFIG_NAMES[w], "op": op, "measured_us": meas * 1e6,
                               "predicted_us": pred * 1e6, "rel_err": pred / meas - 1.0}), flush=True)
 

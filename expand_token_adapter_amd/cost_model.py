@@ -8,14 +8,18 @@ page models the adapters' overhead as linear in the number of adapters and
 fits its constants to profiled data by non-linear least squares.  This module
 does the same for the LoRA delta itself: for each entry point,
 
-    t = c + k_row * T (d_in + d_out) + k_w * sum_{a in U} r_a (d_in + d_out)
-          + k_r * sum_t r_{a(t)} + k_a * |U|
+    t = c + k_t * T + k_row * T (d_in + d_out) + k_w * sum_{a in U} r_a (d_in + d_out)
+          + k_r * sum_t r_{a(t)} + k_a * |U| + k_tile * sum_{a in U} ceil(n_a / 16)
+          + k_g * sum_t ceil(r_{a(t)} / 16) (d_in + d_out)
 
-(U = adapters with at least one row; T (d_in + d_out) = row elements read and
-written; sum_U r_a (d_in + d_out) = weight elements read; sum_t r = the
-rank-wide intermediate per row; |U| = per-adapter work starts), with
-non-negative coefficients fitted by bounded least squares on relative
-residuals, so that a 10 us and a 1 ms call weigh alike.
+(U = adapters with at least one row, n_a = rows of adapter a; T = rows, the
+segment build's work; T (d_in + d_out) = row elements read and written;
+sum_U r_a (d_in + d_out) = weight elements read; sum_t r = the rank-wide
+intermediate per row; |U| = per-adapter work starts; sum_U ceil(n_a / 16) =
+16-row tiles, each a chain of dependent loads in the kernels that walk
+them; sum_t ceil(r / 16) (d_in + d_out) = row elements once per 16-rank group,
+as the backward's token contraction reads them), with non-negative coefficients fitted by bounded least squares on
+relative residuals, so that a 10 us and a 1 ms call weigh alike.
 
 ``features`` and ``fit`` / ``predict`` run on the host; ``calibrate`` times the
 library's calls on synthetic batches on the GPU (random ids, ranks and
@@ -30,8 +34,31 @@ from typing import Dict, Iterable, List, Sequence, Tuple
 
 import numpy as np
 
-FEATURES = ("const", "row_elems", "weight_elems", "rank_rows", "adapters")
+FEATURES = ("const", "rows", "row_elems", "weight_elems", "rank_rows", "adapters", "tiles16", "group_elems")
 OPS = ("segments", "forward", "forward_fused", "backward")
+
+# The terms each model entry is fitted with (the others stay zero): the
+# segment build handles rows and adapters only; the forwards read rows and
+# weights; the two-pass backward also re-reads rows per 16-rank group.
+_OP_FEATURES = {
+    "segments": ("const", "rows", "adapters", "tiles16"),
+    "forward": ("const", "row_elems", "weight_elems", "rank_rows", "adapters", "tiles16"),
+    "forward_fused": ("const", "row_elems", "weight_elems", "rank_rows", "adapters", "tiles16"),
+    "backward": ("const", "row_elems", "weight_elems", "rank_rows", "adapters", "tiles16", "group_elems"),
+    "backward_stream": ("const", "row_elems", "weight_elems", "rank_rows", "adapters", "tiles16"),
+}
+
+
+def route(op: str, ranks: Sequence[int], d_in: int, d_out: int, r_max: int = 0) -> str:
+    """The model entry of a bf16 call: the backward takes its streaming route
+    ('backward_stream': one pass over dY) when every adapter has rank <= 16
+    (r_max, default max(ranks)) and d_out >= 2 d_in, as the library does;
+    other entry points have one model each."""
+    if op == "backward":
+        r = r_max or (max(ranks) if len(ranks) else 0)
+        if r <= 16 and d_out >= 2 * d_in:
+            return "backward_stream"
+    return op
 
 
 def features(ids: Sequence[int], ranks: Sequence[int], d_in: int, d_out: int) -> np.ndarray:
@@ -39,13 +66,16 @@ def features(ids: Sequence[int], ranks: Sequence[int], d_in: int, d_out: int) ->
     ids = np.asarray(ids, dtype=np.int64)
     ranks = np.asarray(ranks, dtype=np.int64)
     valid = ids[(ids >= 0) & (ids < len(ranks))]
-    used = np.unique(valid)
+    used, counts = np.unique(valid, return_counts=True)
     T = ids.size
     return np.array([1.0,
+                     float(T),
                      float(T) * (d_in + d_out),
                      float(ranks[used].sum()) * (d_in + d_out),
                      float(ranks[valid].sum()),
-                     float(used.size)])
+                     float(used.size),
+                     float(((counts + 15) // 16).sum()),
+                     float(((ranks[valid] + 15) // 16).sum()) * (d_in + d_out)])
 
 
 def fit(X: np.ndarray, t: np.ndarray) -> np.ndarray:
@@ -69,8 +99,9 @@ class CostModel:
     def __init__(self, coef: Dict[str, Sequence[float]]):
         self.coef = {op: np.asarray(c, dtype=np.float64) for op, c in coef.items()}
 
-    def predict(self, op: str, ids, ranks, d_in: int, d_out: int) -> float:
-        return float(features(ids, ranks, d_in, d_out) @ self.coef[op])
+    def predict(self, op: str, ids, ranks, d_in: int, d_out: int, r_max: int = 0) -> float:
+        key = route(op, ranks, d_in, d_out, r_max)
+        return float(features(ids, ranks, d_in, d_out) @ self.coef[key if key in self.coef else op])
 
     def to_json(self) -> str:
         return json.dumps({op: {f: float(v) for f, v in zip(FEATURES, c)} for op, c in self.coef.items()})
@@ -93,7 +124,11 @@ def fit_samples(samples: List[dict]) -> CostModel:
     coef = {}
     for op in sorted({s["op"] for s in samples}):
         rows = [s for s in samples if s["op"] == op]
-        coef[op] = fit(np.array([s["features"] for s in rows]), np.array([s["seconds"] for s in rows]))
+        cols = [FEATURES.index(f) for f in _OP_FEATURES.get(op, FEATURES)]
+        X = np.array([s["features"] for s in rows])
+        c = np.zeros(len(FEATURES))
+        c[cols] = fit(X[:, cols], np.array([s["seconds"] for s in rows]))
+        coef[op] = c
     return CostModel(coef)
 
 
@@ -167,7 +202,7 @@ def calibrate(shapes=None, reps: int = 10, ops: Iterable[str] = OPS, seed: int =
             e1.record()
             torch.cuda.synchronize()
             sec = e0.elapsed_time(e1) * 1e-3 / reps
-            samples.append({"op": op, "features": feats.tolist(), "seconds": sec,
+            samples.append({"op": route(op, ranks, d_in, d_out), "features": feats.tolist(), "seconds": sec,
                             "shape": {"T": T, "d_in": d_in, "d_out": d_out, "adapters": len(ranks), "dist": dist}})
         if progress:
             progress(k, T, d_in, d_out, len(ranks), dist)

@@ -13,24 +13,31 @@ def test_features_by_brute_force():
     f = cm.features(ids, ranks, d_in, d_out)
     rows = [i for i in ids if 0 <= i < len(ranks)]
     used = sorted(set(rows))
-    want = [1.0, len(ids) * (d_in + d_out), sum(ranks[a] for a in used) * (d_in + d_out),
-            sum(ranks[i] for i in rows), len(used)]
+    tiles = sum(-(-rows.count(a) // 16) for a in used)
+    groups = sum(-(-ranks[i] // 16) for i in rows) * (d_in + d_out)
+    want = [1.0, len(ids), len(ids) * (d_in + d_out), sum(ranks[a] for a in used) * (d_in + d_out),
+            sum(ranks[i] for i in rows), len(used), tiles, groups]
     assert f.tolist() == want
-    assert cm.features([], ranks, d_in, d_out).tolist() == [1.0, 0.0, 0.0, 0.0, 0.0]
+    assert cm.features([], ranks, d_in, d_out).tolist() == [1.0] + [0.0] * 7
+    # tiles: 17 rows of one adapter and 16 of another are 2 + 1 tiles of 16 rows
+    assert cm.features([0] * 17 + [1] * 16, [4, 4], 8, 8)[6] == 3.0
+    # rank groups: ranks 16 and 17 are one and two groups of 16
+    assert cm.features([0, 1], [16, 17], 8, 8)[7] == 3 * 16
 
 
 def _design(rng, n):
     # feature columns with the magnitudes of real calls
     T = rng.integers(16, 8192, size=n)
     d = rng.choice([4096, 8192, 18432], size=n)
-    return np.stack([np.ones(n), T * d, rng.integers(16, 4096, size=n) * d, T * rng.integers(8, 64, size=n),
-                     rng.integers(1, 320, size=n)], axis=1).astype(np.float64)
+    return np.stack([np.ones(n), T, T * d, rng.integers(16, 4096, size=n) * d, T * rng.integers(8, 64, size=n),
+                     rng.integers(1, 320, size=n), T // 16 + rng.integers(1, 320, size=n),
+                     T * rng.integers(1, 8, size=n) * d], axis=1).astype(np.float64)
 
 
 def test_fit_recovers_exact_coefficients():
     rng = np.random.default_rng(0)
     X = _design(rng, 60)
-    c = np.array([8e-6, 2.5e-13, 2.6e-13, 1e-11, 3e-8])
+    c = np.array([8e-6, 1e-10, 2.5e-13, 2.6e-13, 1e-11, 3e-8, 2e-9, 5e-14])
     got = cm.fit(X, X @ c)
     np.testing.assert_allclose(got, c, rtol=1e-5)
 
@@ -38,23 +45,23 @@ def test_fit_recovers_exact_coefficients():
 def test_fit_with_noise_and_a_zero_coefficient():
     rng = np.random.default_rng(1)
     X = _design(rng, 200)
-    c = np.array([5e-6, 3e-13, 0.0, 2e-11, 1e-8])
+    c = np.array([5e-6, 0.0, 3e-13, 0.0, 2e-11, 1e-8, 1e-9, 0.0])
     t = X @ c * (1.0 + 0.01 * rng.standard_normal(200))
     got = cm.fit(X, t)
     assert np.all(got >= 0.0)
-    np.testing.assert_allclose(got[[0, 1, 3]], c[[0, 1, 3]], rtol=0.1)
-    assert got[2] * X[:, 2].max() < 0.05 * t.min()   # the absent term stays negligible
+    np.testing.assert_allclose(got[[0, 2, 4]], c[[0, 2, 4]], rtol=0.1)
+    assert got[3] * X[:, 3].max() < 0.05 * t.min()   # the absent term stays negligible
     rel = X @ got / t - 1.0
     assert np.median(np.abs(rel)) < 0.02
 
 
 def test_fit_needs_enough_samples():
     with pytest.raises(ValueError):
-        cm.fit(np.ones((3, 5)), np.ones(3))
+        cm.fit(np.ones((3, 8)), np.ones(3))
 
 
 def test_model_json_round_trip_and_predict():
-    m = cm.CostModel({"forward": [1e-6, 1e-12, 2e-12, 3e-11, 4e-9]})
+    m = cm.CostModel({"forward": [1e-6, 1e-10, 1e-12, 2e-12, 3e-11, 4e-9, 5e-9, 1e-13]})
     m2 = cm.CostModel.from_json(m.to_json())
     ids, ranks = [0, 1, 1], [8, 16]
     assert m2.predict("forward", ids, ranks, 64, 32) == pytest.approx(m.predict("forward", ids, ranks, 64, 32))
