@@ -76,6 +76,9 @@ def parse():
     ap.add_argument("--cpu-min-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only time a plain device copy of 256 MiB (reference for counter scaling)")
+    ap.add_argument("--kernel-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="print every kernel's read / write bytes per dispatch from counter files of a run "
+                         "and of --copy-calibration")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="rocprofv3 counter_collection.csv files of FETCH_SIZE / WRITE_SIZE passes over this "
                          "bench and over --copy-calibration: write the measured HBM traffic of the expand kernel")
@@ -135,6 +138,23 @@ def traffic_from(fetch, write, cfetch, cwrite):
         json.dump(out, f, indent=1)
         f.write("\n")
     print(json.dumps(out))
+
+
+def kernel_traffic(fetch, write, cfetch, cwrite):
+    """Print, for every kernel of a FETCH_SIZE / WRITE_SIZE counter pair, its mean
+    read and write bytes per dispatch, scaled by the copy calibration's counters."""
+    fm, wm = _counter_means(fetch, "FETCH_SIZE"), _counter_means(write, "WRITE_SIZE")
+    cf = [m for k, m in _counter_means(cfetch, "FETCH_SIZE").items() if "copy" in k.lower()]
+    cw = [m for k, m in _counter_means(cwrite, "WRITE_SIZE").items() if "copy" in k.lower()]
+    if not cf or not cw:
+        raise SystemExit("no copy dispatches in the calibration counter files")
+    f_fetch = COPY_BYTES / (max(cf, key=lambda m: m[1])[0] * 1024.0)
+    f_write = COPY_BYTES / (max(cw, key=lambda m: m[1])[0] * 1024.0)
+    for k in sorted(set(fm) | set(wm)):
+        rd = fm[k][0] * 1024.0 * f_fetch if k in fm else None
+        wb = wm[k][0] * 1024.0 * f_write if k in wm else None
+        print(json.dumps({"kernel": k, "dispatches": [fm.get(k, (0, 0))[1], wm.get(k, (0, 0))[1]],
+                          "read_bytes": rd, "write_bytes": wb, "fetch_scale": f_fetch, "write_scale": f_write}))
 
 
 def measured_traffic():
@@ -639,6 +659,9 @@ def main():
         return
     if args.multi_slice:
         multi_slice_report(args.steps, args.warmup, args.sets or 4)
+        return
+    if args.kernel_traffic:
+        kernel_traffic(*args.kernel_traffic)
         return
     if args.traffic_from:
         traffic_from(*args.traffic_from)
