@@ -36,15 +36,18 @@ namespace lora {
 
 // ============================================================== shrink
 //
-// A wave reads its run of d_in in groups of 128 elements (4 MFMA steps): the
-// group's 16 rank rows of A_a and 16 x rows are 256-byte pieces of rows, read
-// with coalesced loads (16 neighbouring lanes take the 16 consecutive 16-byte
-// units of one row piece, 4 rows per load), two groups in flight in
-// registers.  An arrived group is written to the wave's own LDS region, unit u
-// of row j at slot u ^ j, and read back in MFMA operand layout (lane (lr, lg)
-// takes unit 4 t + lg of row lr at step t), which the XOR spreads over
-// distinct banks.  Loads of rows past the adapter's rank or the tile fetch
-// nothing (their offsets lie past the buffer).
+// Workgroups of 8 or 16 waves (few tasks): a wave reads its run of d_in in
+// groups of 128 elements (4 MFMA steps): the group's 16 rank rows of A_a and
+// 16 x rows are 256-byte pieces of rows, read with coalesced loads (16
+// neighbouring lanes take the 16 consecutive 16-byte units of one row piece,
+// 4 rows per load), two groups in flight in registers.  An arrived group is
+// written to the wave's own LDS region, unit u of row j at slot u ^ j, and
+// read back in MFMA operand layout (lane (lr, lg) takes unit 4 t + lg of row
+// lr at step t), which the XOR spreads over distinct banks.  Workgroups of 4
+// waves (many tasks) share 512-element groups: every load is one contiguous
+// 1 KB piece of a row (the same LDS layout, 64 units per row).  Loads of rows
+// past the adapter's rank or the tile fetch nothing (their offsets lie past
+// the buffer).
 
 constexpr int kShrGS = 4;                   // MFMA steps (of 32 elements) per group
 constexpr int kShrUnits = 2 * kShrGS * 2;   // 16-byte units per row piece (16)
@@ -64,8 +67,117 @@ struct DecShrinkParams {
     int64_t ldv;
     int32_t v_by_pos;
     int32_t rblocks;      // ceil(r_max / 16)
+    int32_t balanced;     // 1: cost-balanced task ranges (plan); 0: one task per workgroup
     int32_t* err;
 };
+
+// Balanced mode (many tasks): workgroup w of G (numbered XCD by XCD) takes the
+// tasks whose start falls in [w C / G, (w + 1) C / G) of the total cost C, in
+// task order; a task (tile t, rank block b) costs its A rows plus its x rows,
+// min(16, r - 16 b) + rows(t) rows of d_in elements.  Wave 0 builds the
+// tiles' cost prefix in LDS as the expand's plan does; each XCD then holds
+// one contiguous eighth of the work, so the tiles of an adapter share A_a
+// through one L2 and the rank blocks of a tile share its x rows.  Direct
+// mode (few tasks): workgroups take tasks by index, XCD by XCD.
+constexpr int kShrPlanMaxTiles = 2048;  // tiles per call in balanced mode (LDS prefix)
+#ifndef LORA_SHR_DEPTH
+#define LORA_SHR_DEPTH 2
+#endif
+constexpr int kShrDepth = LORA_SHR_DEPTH;  // 4-wave kernel: 512-element groups in flight per wave
+
+// Records of tiles t0 + 64 i + lane (i < NB; tile 0 past n16) and their
+// table entries: the records' loads all in flight, then the entries' loads.
+// Each record (16 bytes, one word unused) and entry (the scale unused) is
+// read whole by an empty asm statement: no register of a value is reused
+// while its load is in flight, which would make every load wait for the
+// previous one.
+template <int NB>
+__device__ __forceinline__ void plan_loads(const int32_t* sched, int64_t off, const lora_adapter* table, int t0,
+                                           int n16, int lane, TileRec (&rec)[NB], lora_adapter (&ads)[NB]) {
+    u32x4_t raw[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        const int t = t0 + kWave * i + lane;
+        raw[i] = *cptr(reinterpret_cast<const u32x4_t*>(sched + off + 4 * (int64_t)(t < n16 ? t : 0)));
+    }
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        asm volatile("" ::"v"(raw[i]));
+        rec[i] = TileRec{(int)raw[i][0], (int)raw[i][1], (int)raw[i][2]};
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) ads[i] = load_adapter(table, rec[i].adapter);
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < NB; ++i) asm volatile("" ::"v"(ads[i].scale));
+}
+
+// Returns {first tile, first rank block, end tile, end rank block} (end
+// exclusive).  s_pre / s_inf: LDS arrays of n16 entries.
+__device__ __forceinline__ int4 dec_shrink_plan(const DecShrinkParams& p, int n16, int lane, uint32_t* s_pre,
+                                                uint32_t* s_inf) {
+    constexpr int kBlocks = 8;
+    for (int t0 = 0; t0 < n16; t0 += kBlocks * kWave) {
+        // every record, then every table entry, in flight together: two
+        // memory round trips per round of 512 tiles
+        TileRec rec[kBlocks];
+        lora_adapter ads[kBlocks];
+        plan_loads<kBlocks>(p.sched, p.tiles16_off, p.adapters, t0, n16, lane, rec, ads);
+        uint32_t carry = t0 > 0 ? s_pre[t0 - 1] : 0u;
+#pragma unroll
+        for (int i = 0; i < kBlocks; ++i) {
+            const int t = t0 + kWave * i + lane;
+            const lora_adapter& ad = ads[i];
+            const bool ok = t < n16 && adapter_ok(ad, p.r_max);
+            if (t < n16 && !ok && blockIdx.x == 0) atomicAdd(p.err, 1);
+            const uint32_t nrb = ok ? (uint32_t)(ad.rank + 15) / 16 : 0u;
+            const uint32_t c = ok ? (uint32_t)ad.rank + nrb * (uint32_t)rec[i].rows : 0u;
+            uint32_t incl = c;
+#pragma unroll
+            for (int d = 1; d < kWave; d <<= 1) {
+                const uint32_t o = __shfl_up(incl, d, kWave);
+                if (lane >= d) incl += o;
+            }
+            if (t < n16) {
+                s_pre[t] = carry + incl;
+                s_inf[t] = (uint32_t)rec[i].rows | (nrb << 8);
+            }
+            carry += __shfl(incl, kWave - 1, kWave);
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    const uint64_t total = n16 > 0 ? s_pre[n16 - 1] : 0;
+    const uint64_t G = gridDim.x;
+    const uint64_t w = (uint64_t)(blockIdx.x % kNumXcd) * (G / kNumXcd) + blockIdx.x / kNumXcd;
+    const uint64_t lo = total * w / G, hi = total * (w + 1) / G;
+    // first task whose start is at or past x: tile = first with prefix > x;
+    // its tasks start at st + b (16 + rows), b < nrb
+    auto locate = [&](uint64_t x, int& tt, int& bb) {
+        int l = 0, h = n16;
+        while (l < h) {
+            const int m = (l + h) >> 1;
+            if ((uint64_t)s_pre[m] > x) h = m;
+            else l = m + 1;
+        }
+        if (l >= n16) {
+            tt = n16;
+            bb = 0;
+            return;
+        }
+        const uint64_t st = l > 0 ? s_pre[l - 1] : 0;
+        const uint32_t inf = s_inf[l];
+        const uint64_t q = 16 + (inf & 255u);
+        const uint64_t b = (x - st + q - 1) / q;
+        tt = b < (inf >> 8) ? l : l + 1;
+        bb = b < (inf >> 8) ? (int)b : 0;
+    };
+    int4 plan;
+    locate(lo, plan.x, plan.y);
+    locate(hi, plan.z, plan.w);
+    if (hi >= total) plan.z = n16, plan.w = 0;
+    return plan;
+}
 
 // NW: waves per workgroup (4, 8 or 16).
 template <int DT, int NW>
@@ -84,39 +196,98 @@ __global__ __launch_bounds__(NW * kWave) void dec_shrink_kernel(DecShrinkParams 
     const int cu = lane & (kShrUnits - 1);  // coalesced load: unit of the row piece
     const int cr = lane / kShrUnits;        // coalesced load: row within the load's 4 rows
     const int n16 = p.sched[0];
-    const int64_t ntasks = (int64_t)n16 * p.rblocks;
-    const TaskSlice ts = xcd_slice(ntasks, 1, 0);
     // wave w takes groups w, w + NW, w + 2 NW, ...: at any time the waves of a
     // workgroup read neighbouring pieces of the same rows
     const int ngroups = (p.K + 32 * kShrGS - 1) / (32 * kShrGS);
     u32x4_t* sA = &s_grp[wave][0][0];
     u32x4_t* sX = &s_grp[wave][1][0];
 
-    for (int64_t task = ts.begin; task < ts.end; task += ts.stride) {
-        const int tile = (int)(task / p.rblocks);
-        const int rb = (int)(task % p.rblocks);
-        const TileRec rec = load_tile(p.sched, p.tiles16_off, tile);
-        const lora_adapter ad = load_adapter(p.adapters, rec.adapter);
-        if (!adapter_ok(ad, p.r_max)) {
-            if (rb == 0 && threadIdx.x == 0) atomicAdd(p.err, 1);
-            continue;
-        }
+    // one task: rank block rb of tile rec (adapter ad, a valid entry)
+    auto task = [&](const TileRec& rec, const lora_adapter& ad, int rb) {
         const int r = ad.rank;
         const int rank0 = 16 * rb;
-        if (rank0 >= r) continue;  // wave-uniform: the whole workgroup skips
+        if (rank0 >= r) return;  // wave-uniform: the whole workgroup skips
         const int nrows = rec.rows;
         const int nranks = min(16, r - rank0);
-        // Coalesced loads: load i covers rows 4 i + cr (A: rank rows of the
-        // block; x: rows of the tile), unit cu of the group's row piece.  Byte
-        // offsets inside the x and A_a buffers stay below 2^31 (checked on the
-        // host); a piece that runs past K reads the next row (or zeros past
-        // the buffer) and is zeroed where it is used.
+        // Byte offsets inside the x and A_a buffers stay below 2^31 (checked
+        // on the host); a piece that runs past K reads the next row (or zeros
+        // past the buffer) and is zeroed where it is used.  Rows past the tile
+        // or the rank take an offset past the end of the buffer: the hardware
+        // returns zeros without touching memory, and no branch splits the
+        // loads (a branch would make the compiler wait for every load at its
+        // join).  Row indices come through scalar loads: no vector load may
+        // sit between the buffer loads, or the compiler's waits lose their
+        // count.
         const buf_rsrc_t xr = make_rsrc(p.x, p.x_bytes);
         const buf_rsrc_t ar = make_rsrc(ad.A, (uint32_t)((int64_t)r * p.K * EB));
-        // The tile's row indices (16 consecutive perm entries, rows past the
-        // tile repeat its first) through scalar loads: no vector load may sit
-        // between the buffer loads, or the compiler's waits lose their count.
-        int32_t prow[16];
+        f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if constexpr (NW == 4) {
+            // Four waves share each group of 512 elements (16 MFMA steps):
+            // wave w loads rows w, w + 4, w + 8, w + 12 of A's block and of the
+            // tile, one contiguous 1 KB piece of a row per load (lane l: unit
+            // l), and writes them to the workgroup's LDS group (unit u of row j
+            // at slot u ^ j); after a barrier each wave multiplies its quarter
+            // of the steps (4 w .. 4 w + 3) for all 16 rows.  kShrDepth
+            // groups are in flight in registers.
+            constexpr int kU = 64;  // 16-byte units per 1 KB row piece
+            u32x4_t* gA = &s_grp[0][0][0];
+            u32x4_t* gX = gA + 16 * kU;
+            const int ng = (p.K + 511) / 512;
+            uint32_t xo[4], ao[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = wave + 4 * i;
+                const int32_t xrow = *cptr(p.perm + rec.pos0 + (row < nrows ? row : 0));
+                xo[i] = row < nrows ? (uint32_t)((int64_t)xrow * p.ldx * EB) + 16u * lane : kBufOff;
+                ao[i] = row < nranks ? (uint32_t)((int64_t)(rank0 + row) * p.K * EB) + 16u * lane : kBufOff;
+            }
+            constexpr int D = kShrDepth;  // groups in flight
+            u32x4_t xq[D][4], wq[D][4];
+            auto issue4 = [&](int b, int g) {
+                const uint32_t kb = (uint32_t)g * 1024u;
+                const bool in = g < ng;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    xq[b][i] = buf_load16(xr, in && xo[i] != kBufOff ? xo[i] + kb : kBufOff, 0);
+                    wq[b][i] = buf_load16(ar, in && ao[i] != kBufOff ? ao[i] + kb : kBufOff, 0);
+                }
+            };
+#pragma unroll
+            for (int b = 0; b < D; ++b) {
+                issue4(b, b);
+                asm volatile("" ::: "memory");
+            }
+            for (int g = 0; g < ng; g += D) {
+#pragma unroll
+                for (int b = 0; b < D; ++b) {
+                    const int gg = g + b;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = wave + 4 * i;
+                        gA[row * kU + (lane ^ row)] = wq[b][i];
+                        gX[row * kU + (lane ^ row)] = xq[b][i];
+                    }
+                    issue4(b, gg + D);
+                    asm volatile("" ::: "memory");
+                    lds_barrier();
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const int step = 4 * wave + t;
+                        const int u = 4 * step + lg;
+                        const bool ok = gg < ng && 512 * gg + 32 * step + 8 * lg < p.K;
+                        const F wf{gA[lr * kU + (u ^ lr)]};
+                        const F xf{gX[lr * kU + (u ^ lr)]};
+                        acc = mma(wf, xf.masked(ok), acc);
+                    }
+                    lds_barrier();
+                }
+            }
+        } else {
+        // Each wave takes its own 128-element groups.  Coalesced loads: load i
+        // covers rows 4 i + cr (A: rank rows of the block; x: rows of the
+        // tile), unit cu of the group's row piece.  Registers of two groups
+        // in flight.
+        int32_t prow[16];  // the tile's rows (rows past it repeat its first)
 #pragma unroll
         for (int j = 0; j < 16; ++j) prow[j] = *cptr(p.perm + rec.pos0 + (j < nrows ? j : 0));
         uint32_t xoff[kShrLoads], aoff[kShrLoads];
@@ -131,10 +302,6 @@ __global__ __launch_bounds__(NW * kWave) void dec_shrink_kernel(DecShrinkParams 
             xoff[i] = (uint32_t)((int64_t)xrow * p.ldx * EB) + 16u * cu;
             aoff[i] = (uint32_t)((int64_t)(rank0 + (aon[i] ? row : 0)) * p.K * EB) + 16u * cu;
         }
-        // Registers of two groups in flight.  Rows past the tile or the rank
-        // take an offset past the end of the buffer: the hardware returns
-        // zeros without touching memory, and no branch splits the loads (a
-        // branch would make the compiler wait for every load at its join).
         u32x4_t xa[2][kShrLoads], wa[2][kShrLoads];
         auto issue = [&](int b, int g) {
             const uint32_t kb = (uint32_t)g * (32 * kShrGS * EB);
@@ -151,7 +318,6 @@ __global__ __launch_bounds__(NW * kWave) void dec_shrink_kernel(DecShrinkParams 
         // wait for all loads where the paths join).
         // (the empty asm statements keep the two groups' loads in issue order:
         // the waits below count on group g0's loads being the older ones)
-        f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
         issue(0, wave);
         asm volatile("" ::: "memory");
         issue(1, wave + NW);
@@ -182,6 +348,7 @@ __global__ __launch_bounds__(NW * kWave) void dec_shrink_kernel(DecShrinkParams 
                 __builtin_amdgcn_wave_barrier();
             }
         }
+        }
 
         // waves' tiles in wave order: D rows 4 lg + e = ranks, column lr = row
         s_red[wave][lane] = acc;
@@ -201,6 +368,42 @@ __global__ __launch_bounds__(NW * kWave) void dec_shrink_kernel(DecShrinkParams 
             }
         }
         lds_barrier();  // s_red is rewritten by the next task
+    };
+
+    if (p.balanced) {
+        // the plan's prefix arrays live in the group buffers until the tasks start
+        static_assert(sizeof(s_grp) >= 2 * kShrPlanMaxTiles * sizeof(uint32_t), "plan arrays fit the group buffers");
+        __shared__ int4 s_plan;
+        if (wave == 0) {
+            uint32_t* s_pre = reinterpret_cast<uint32_t*>(&s_grp[0][0][0]);
+            const int4 pl = dec_shrink_plan(p, min(n16, kShrPlanMaxTiles), lane, s_pre, s_pre + kShrPlanMaxTiles);
+            if (lane == 0) s_plan = pl;
+        }
+        __syncthreads();
+        const int4 plan = s_plan;
+        __syncthreads();  // the group buffers are rewritten by the tasks
+        for (int t = plan.x; t <= plan.z && t < n16; ++t) {
+            const TileRec rec = load_tile(p.sched, p.tiles16_off, t);
+            const lora_adapter ad = load_adapter(p.adapters, rec.adapter);
+            if (!adapter_ok(ad, p.r_max)) continue;  // counted by the plan
+            const int b0 = t == plan.x ? plan.y : 0;
+            const int b1 = t == plan.z ? plan.w : (ad.rank + 15) / 16;
+            for (int rb = b0; rb < b1; ++rb) task(rec, ad, rb);
+        }
+        return;
+    }
+    const int64_t ntasks = (int64_t)n16 * p.rblocks;
+    const TaskSlice ts = xcd_slice(ntasks, 1, 0);
+    for (int64_t i = ts.begin; i < ts.end; i += ts.stride) {
+        const int tile = (int)(i / p.rblocks);
+        const int rb = (int)(i % p.rblocks);
+        const TileRec rec = load_tile(p.sched, p.tiles16_off, tile);
+        const lora_adapter ad = load_adapter(p.adapters, rec.adapter);
+        if (!adapter_ok(ad, p.r_max)) {
+            if (rb == 0 && threadIdx.x == 0) atomicAdd(p.err, 1);
+            continue;
+        }
+        task(rec, ad, rb);
     }
 }
 
@@ -465,10 +668,11 @@ __device__ __forceinline__ int64_t dec_chunk_cost(int r, int rows) {
 // Balanced mode: workgroup w of G takes the units whose first byte falls in
 // [w C / G, (w + 1) C / G) of the total cost C, so every workgroup moves the
 // same number of bytes whatever the ranks and row counts of the tiles it
-// meets.  Wave 0 loads every tile record and table entry (kPlanBlocks x 64
-// tiles per round, all loads of a round in flight together), writes the
-// inclusive prefix of the tiles' costs (in units of kPlanUnit bytes) to LDS,
-// and the range's ends are found there by binary search.  Bad table entries
+// meets; w numbers the workgroups XCD by XCD.  Wave 0 loads every tile
+// record and table entry (kPlanBlocks x 64 tiles per round: the records
+// together, then the entries together), writes the inclusive prefix of the
+// tiles' costs (in units of kPlanUnit bytes) to LDS, and the range's ends
+// are found there by binary search.  Bad table entries
 // cost nothing (workgroup 0 counts them).  Direct mode (small batches, where
 // the plan's latency would dominate): workgroup w takes chunks
 // [16 c, 16 c + 16) of tile w / ncr, c = w % ncr.
@@ -482,16 +686,13 @@ __device__ __forceinline__ int4 dec_expand_plan(const DecExpandParams& p, int n1
                                                 uint32_t* s_pre) {
     for (int t0 = 0; t0 < n16; t0 += kPlanBlocks * kWave) {
         TileRec rec[kPlanBlocks];
-#pragma unroll
-        for (int i = 0; i < kPlanBlocks; ++i) {
-            const int t = t0 + kWave * i + lane;
-            rec[i] = load_tile(p.sched, p.tiles16_off, t < n16 ? t : 0);
-        }
+        lora_adapter ads[kPlanBlocks];
+        plan_loads<kPlanBlocks>(p.sched, p.tiles16_off, p.adapters, t0, n16, lane, rec, ads);
         uint32_t carry = t0 > 0 ? s_pre[t0 - 1] : 0u;
 #pragma unroll
         for (int i = 0; i < kPlanBlocks; ++i) {
             const int t = t0 + kWave * i + lane;
-            const lora_adapter ad = load_adapter(p.adapters, rec[i].adapter);
+            const lora_adapter& ad = ads[i];
             const bool ok = t < n16 && adapter_ok(ad, p.r_max);
             if (t < n16 && !ok && blockIdx.x == 0) atomicAdd(p.err, 1);
             uint32_t c = ok ? (uint32_t)((nch * dec_chunk_cost(ad.rank, rec[i].rows) + kPlanUnit - 1) / kPlanUnit) : 0u;
@@ -507,8 +708,12 @@ __device__ __forceinline__ int4 dec_expand_plan(const DecExpandParams& p, int n1
     }
     __builtin_amdgcn_wave_barrier();
     const uint64_t total = n16 > 0 ? s_pre[n16 - 1] : 0;
+    // ranges in XCD order: the workgroups of one XCD (same blockIdx % 8) take
+    // one contiguous eighth of the cost, so the tiles of an adapter share its
+    // B_a blocks through one L2 (the grid is a multiple of 8)
     const uint64_t G = gridDim.x;
-    const uint64_t lo = total * blockIdx.x / G, hi = total * (blockIdx.x + 1) / G;
+    const uint64_t w = (uint64_t)(blockIdx.x % kNumXcd) * (G / kNumXcd) + blockIdx.x / kNumXcd;
+    const uint64_t lo = total * w / G, hi = total * (w + 1) / G;
     // first unit whose start is at or past x: tile = first with prefix > x,
     // chunk = ceil((x - tile's start) / unit cost)
     auto locate = [&](uint64_t x, int& tt, int& cc) {

@@ -57,14 +57,25 @@ int launch_expand_t(int ks, const ExpandParams& p, unsigned grid, hipStream_t st
     return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
-constexpr int64_t kDecMaxGrid = 2048;
 // One task per workgroup up to this many tasks: the hardware dispatcher then
 // hands out tasks of very different sizes (and the empty ones) as slots free
 // up, instead of each workgroup walking a fixed share.
 constexpr int64_t kDecShrinkMaxGrid = 1 << 16;
 
+// Balanced mode: at least this many tasks (bound from the row and adapter
+// counts), on a grid of four 4-wave workgroups per CU.  (At most three per CU
+// were found resident at once; a grid of three per CU, or a smaller LDS
+// footprint, measured no faster on the zipf-320 decode batch.)
+constexpr int64_t kDecShrinkPlanTasks = 2048;
+constexpr unsigned kDecShrinkPlanGrid = 256 * 4;
+static_assert(kDecShrinkPlanGrid % kNumXcd == 0, "balanced ranges are numbered XCD by XCD");
+
 template <int DT>
 void launch_dec_shrink(const DecShrinkParams& p, int64_t tasks, hipStream_t st) {
+    if (p.balanced) {
+        hipLaunchKernelGGL((dec_shrink_kernel<DT, 4>), dim3(kDecShrinkPlanGrid), dim3(4 * kWave), 0, st, p);
+        return;
+    }
     const unsigned grid = grid_for(tasks, 1, kDecShrinkMaxGrid);
     // few tasks: more waves per workgroup (each takes a shorter run of d_in)
     if (tasks < 512)
@@ -110,7 +121,9 @@ int run_dec_shrink(int dtype, const void* x, int64_t ldx, int32_t T, int32_t d_i
     p.v_by_pos = v_by_pos;
     p.rblocks = (r_max + 15) / 16;
     p.err = seg.err;
-    const int64_t tasks = SchedLayout::max_tiles16(T, num_adapters) * p.rblocks;
+    const int64_t tiles = SchedLayout::max_tiles16(T, num_adapters);
+    const int64_t tasks = tiles * p.rblocks;
+    p.balanced = tasks >= kDecShrinkPlanTasks && tiles <= kShrPlanMaxTiles;
     if (dtype != LORA_BF16) return LORA_ERR_UNSUPPORTED;
     launch_dec_shrink<LORA_BF16>(p, tasks, st);
     return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
@@ -119,6 +132,7 @@ int run_dec_shrink(int dtype, const void* x, int64_t ldx, int32_t T, int32_t d_i
 // y += s B v on 16-row tiles (decode.h): one launch of a fixed grid, each
 // workgroup a byte-balanced share of the (tile, chunk) units.
 constexpr int kDecExpandGrid = 256 * 3;  // three workgroups per CU (the kernel's occupancy)
+static_assert(kDecExpandGrid % kNumXcd == 0, "balanced ranges are numbered XCD by XCD");
 
 int run_dec_expand(int dtype, const float* v, int64_t ldv, int32_t v_by_pos, int32_t T, int32_t d_out,
                    const lora_adapter* adapters, int32_t num_adapters, int32_t r_max, const lora_segments& seg,

@@ -193,6 +193,50 @@ def test_forward_decode_bad_table_entries_are_skipped_and_counted():
     assert not torch.equal(y[ok], case.y0[ok])
 
 
+def _many_decode(seed=0, A=600, T=2000, d_out=2056):
+    """Many adapters with few rows each and a Zipf-like head (an adapter with
+    hundreds of rows, several with tens): enough 16-row tiles x rank blocks for
+    the shrink's cost-balanced plan and enough tiles x chunks for the expand's;
+    ranks 1..128, d_in = 264 (a ragged K group), rows without adapters."""
+    rng = np.random.default_rng(200 + seed)
+    k = np.arange(1, A + 1, dtype=np.float64)
+    p = k ** -1.1
+    ids = rng.choice(A, size=T, p=p / p.sum()).astype(np.int32)
+    ids[rng.random(T) < 0.03] = -1
+    ranks = rng.choice(np.array([1, 5, 8, 12, 16, 24, 32, 40, 64, 72, 96, 128]), size=A).astype(np.int32)
+    scales = rng.choice([2.0, 0.5, -1.25, 3.0], size=A)
+    return workloads.custom(ids, ranks, 264, d_out, "bf16", seed=seed, name="many-decode", scales=scales)
+
+
+@pytest.mark.parametrize("y0_zero", [False, True])
+def test_forward_decode_balanced_plans(y0_zero):
+    """Shrink and expand both in their cost-balanced modes (parity with the oracle)."""
+    case = GpuCase(_many_decode(), y0_zero=y0_zero)
+    _check_forward(case, TOL["bf16"])
+
+
+def test_forward_decode_balanced_bad_entries_are_skipped_and_counted():
+    """r_max = 64 makes the adapters of rank 72..128 bad entries: the plans give
+    them no work and count them; every other row matches the oracle."""
+    wl = _many_decode(seed=1)
+    case = GpuCase(wl)
+    y = case.y0.clone()
+    seg = lb.lora_segments_build(case.ids, wl.num_adapters)
+    v = lb.lora_shrink(case.x, case.table, seg, r_max=64)
+    lb.lora_expand_add(v, case.table, seg, y, r_max=64)
+    torch.cuda.synchronize()
+    ranks = np.asarray(wl.ranks)
+    bad_ids = [a for a in range(wl.num_adapters) if ranks[a] > 64]
+    used_bad = set(np.unique(wl.ids[np.isin(wl.ids, bad_ids)]).tolist())
+    assert used_bad and int(seg.err.item()) > 0
+    bad = np.isin(wl.ids, bad_ids)
+    assert torch.equal(y[torch.from_numpy(bad).cuda()], case.y0[torch.from_numpy(bad).cuda()])
+    y_ref, _ = case.oracle_forward()
+    good = ~bad
+    e = rel_err(y[torch.from_numpy(good).cuda()], y_ref[good])
+    assert e <= TOL["bf16"], e
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("y0_zero", [False, True])
 def test_forward_small_mixed(dtype, y0_zero):
