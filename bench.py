@@ -59,9 +59,11 @@ def parse():
     ap.add_argument("--overlap", action="store_true",
                     help="run the fine-tuning backward (v recomputed) on a second stream, concurrently with the "
                          "forward, joining at the end of each step")
-    ap.add_argument("--fused", action="store_true",
-                    help="forward as one lora_forward launch (v written for the backward) instead of "
-                         "lora_shrink + lora_expand_add")
+    ap.add_argument("--forward", choices=("auto", "split", "fused"), default="auto",
+                    help="forward of a step: lora_shrink + lora_expand_add (split), one lora_forward launch "
+                         "(fused; v written for the backward), or whichever of the two has the shorter GPU "
+                         "time per call on the workload (auto, measured before the timed steps)")
+    ap.add_argument("--fused", action="store_true", help="same as --forward fused")
     ap.add_argument("--preemptible", action="store_true",
                     help="run the backward through lora_backward_preemptible with a granted grant word")
     ap.add_argument("--adamw", action="store_true",
@@ -82,7 +84,10 @@ def parse():
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="rocprofv3 counter_collection.csv files of FETCH_SIZE / WRITE_SIZE passes over this "
                          "bench and over --copy-calibration: write the measured HBM traffic of the expand kernel")
-    return ap.parse_args()
+    args = ap.parse_args()
+    if args.fused:
+        args.forward = "fused"
+    return args
 
 
 # HBM traffic of the dominant kernel, measured with rocprofv3 counters and
@@ -587,6 +592,18 @@ class Bench:
             del g
         return out
 
+    def pick_forward(self, mode):
+        """Set the step's forward: 'split', 'fused', or for 'auto' the one whose
+        GPU time per call (captured graphs, outside any timed region) is shorter."""
+        if mode != "auto":
+            self.fused = mode == "fused"
+            return {"mode": mode, "chosen": mode}
+        t = self.call_times(["shrink", "expand", "forward_fused"], reps=20)
+        split_us = t["shrink"] + t["expand"]
+        self.fused = t["forward_fused"] < split_us
+        return {"mode": "auto", "chosen": "fused" if self.fused else "split", "split_us_per_call": split_us,
+                "fused_us_per_call": t["forward_fused"]}
+
     def check_errors(self):
         errs = [int(st["seg"].err.item()) + (int(st["seg_ft"].err.item()) if self.has_ft else 0) for st in self.sets]
         if any(errs):
@@ -607,7 +624,7 @@ def call_report(wl, times, alg):
     return out
 
 
-def workload_block(idx, steps, warmup):
+def workload_block(idx, steps, warmup, forward="auto"):
     """Step time and per-call GPU times of one more workload (its own rotation)."""
     import torch
     import workloads
@@ -615,6 +632,7 @@ def workload_block(idx, steps, warmup):
     n_sets = auto_sets(wl)
     b = Bench(wl, n_sets)
     alg = algorithmic(wl)
+    choice = b.pick_forward(forward)
     for i in range(warmup):
         b.step(b.sets[i % n_sets])
     torch.cuda.synchronize()
@@ -630,7 +648,8 @@ def workload_block(idx, steps, warmup):
     fwd_us = calls["shrink"]["us_per_call"] + calls["expand"]["us_per_call"]
     fwd_b = alg["shrink"]["bytes"] + alg["expand"]["bytes"]
     res = {"rows": wl.T, "ft_rows": wl.ft_count, "d_in": wl.d_in, "d_out": wl.d_out, "adapters": wl.num_adapters,
-           "ranks": RANKS_DESC[idx], "ms_per_step": ms, "rows_per_s": wl.T / (ms * 1e-3),
+           "ranks": RANKS_DESC[idx], "forward": choice["chosen"], "forward_choice": choice,
+           "ms_per_step": ms, "rows_per_s": wl.T / (ms * 1e-3),
            "step_timing_distribution": dist, "calls": calls,
            "forward_split_us": fwd_us, "forward_split_algorithmic_bytes": fwd_b,
            "forward_split_frac_of_hbm_peak": fwd_b / (fwd_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
@@ -675,7 +694,9 @@ def main():
     has_ft = n > 0
     alg = algorithmic(wl)
     n_sets = args.sets or auto_sets(wl)
-    b = Bench(wl, n_sets, fused=args.fused, preemptible=args.preemptible, adamw=args.adamw, overlap=args.overlap)
+    b = Bench(wl, n_sets, preemptible=args.preemptible, adamw=args.adamw, overlap=args.overlap)
+    choice = b.pick_forward(args.forward)
+    fused = b.fused
     sets = b.sets
     r_ft = int(wl.ranks[wl.ft_ids[0]]) if has_ft else None
 
@@ -742,7 +763,7 @@ def main():
     # Distribution of step times, outside the timed region above.
     dist = b.distribution(K, args.warmup + K) if graphs is None else None
     # Per-call GPU times from captured graphs (outside the timed region).
-    names = ["segments"] + (["forward_fused"] if args.fused else ["shrink", "expand"]) + \
+    names = ["segments"] + (["forward_fused"] if fused else ["shrink", "expand"]) + \
         (["backward"] if has_ft and not args.preemptible and not args.overlap else [])
     calls = call_report(wl, b.call_times(names), alg) if not args.adamw else None
     # Context: a plain 256 MiB device-to-device copy on the same GPU (read + write bytes).
@@ -760,8 +781,8 @@ def main():
     del cbuf, cdst
     b.check_errors()
 
-    ex = alg["forward_fused"] if args.fused else alg["expand"]
-    kern_name = "lora_forward (fused_forward_kernel)" if args.fused else "lora_expand_add (expand_kernel)"
+    ex = alg["forward_fused"] if fused else alg["expand"]
+    kern_name = "lora_forward (fused_forward_kernel)" if fused else "lora_expand_add (expand_kernel)"
     achieved = ex["bytes"] / (kern_ms * 1e-3) / 1e9
     line = {
         "metric": "LoRA delta tokens/s + achieved HBM GB/s (or MFMA %) vs peak, mixed multi-LoRA batch",
@@ -781,7 +802,7 @@ def main():
                    "ft_adapter_rank": r_ft, "seed": 0, "input_sets": n_sets,
                    "rotation_bytes": n_sets * per_set_bytes(wl),
                    "launch": "graph" if graphs is not None else "eager",
-                   "streams": 2 if args.overlap else 1, "forward": "fused" if args.fused else "split",
+                   "streams": 2 if args.overlap else 1, "forward": choice["chosen"],
                    "backward": "preemptible" if args.preemptible else "plain"},
         "host_enqueue_ms_per_step": (t_enq - t0) * 1e3 / K,
         "step_algorithmic_GBps": alg["step"]["bytes"] / (ms * 1e-3) / 1e9,
@@ -789,11 +810,12 @@ def main():
         "step_algorithmic_TFLOPs": alg["step"]["flops"] / (ms * 1e-3) / 1e12,
         "step_timing_distribution": dist,
         "calls": calls,
+        "forward_choice": choice,
         "inputs_sha256": wl.manifest(),
         "copy_256MiB_GBps": copy_gbps,
         "roofline": {"bound": "hbm", "kernel": kern_name, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic() if args.workload == 3 and not args.fused else None,
+                     "traffic": measured_traffic() if args.workload == 3 and not fused else None,
                      "algorithmic_bytes_per_launch": ex["bytes"], "avg_launch_ms": kern_ms, "timing": kern_how,
                      "mfma_frac": ex["flops"] / (kern_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
     }
@@ -809,13 +831,14 @@ def main():
                              "achieved_GBps": opt_bytes / (opt_ms * 1e-3) / 1e9}
     del b, sets, graphs
     torch.cuda.empty_cache()
-    default_run = (args.workload == 3 and not (args.fused or args.graph or args.overlap or args.preemptible
-                                               or args.adamw))
+    default_run = (args.workload == 3 and args.forward == "auto" and not (args.graph or args.overlap
+                                                                          or args.preemptible or args.adamw))
     if default_run and not args.no_workloads:
         block = {}
         for idx in (2, 4, 5):
             print(f"bench: workload {workloads.CONFIG_NAMES[idx]}", file=sys.stderr, flush=True)
-            block[workloads.CONFIG_NAMES[idx]] = workload_block(idx, args.workload_steps, args.warmup)
+            block[workloads.CONFIG_NAMES[idx]] = workload_block(idx, args.workload_steps, args.warmup,
+                                                                args.forward)
         line["workloads"] = block
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_min_seconds)

@@ -240,12 +240,21 @@ int lora_expand_add(int dtype, const float* v, int64_t ldv, int32_t T, int32_t d
  * whole h(x) = W x + B A x delta of MOLT section 2.1 for every row with an
  * adapter, without v passing through HBM and without a workspace.  One
  * workgroup carries each 64-row tile from x to y (v = A x over all of d_in
- * into LDS, then all of d_out), so it suits batches whose adapters have few
- * rows each (decode; many adapters): there the weights and launch latency
- * dominate.  Batches of long row groups (prefill, fine-tuning) run faster on
- * lora_shrink + lora_expand_add, which spread each tile's y traffic over the
- * whole chip.  Results equal lora_shrink + lora_expand_add up to the order of
- * the fp32 sum over d_in (a fixed order: bit-reproducible).
+ * into LDS, then a range of d_out's columns).
+ * Where it wins (measured on one MI355X, GPU time per call): only where
+ * launch latency dominates and each tile's weights are small -- a few rows
+ * per adapter, ranks <= 16, d_in and d_out <= 4096 (256 decode rows over 64
+ * rank-16 adapters, 4096 -> 4096: 17.3 us against 18.5 us for lora_shrink +
+ * lora_expand_add) -- and for projections that share x (lora_forward_multi,
+ * against three split calls).  Everywhere else the split calls are faster
+ * (1.7x on 4096 fine-tuning rows at 5120 -> 5120, 2.4x on the mixed
+ * prefill / decode / fine-tuning batch at 4096 -> 14336, 2.8x on 2048 decode
+ * rows over 320 adapters of ranks 8..128 at 8192 -> 8192): their 16-row-tile
+ * decode kernels and split-K shrink spread every adapter's weights over the
+ * whole chip, while here each tile's workgroup walks all of d_in.  Callers
+ * pick per batch shape, e.g. by timing both once.  Results equal lora_shrink +
+ * lora_expand_add up to the order of the fp32 sum over d_in (a fixed order:
+ * bit-reproducible).
  *   x [T, ldx], y [T, ldy] in/out (dtype); adapters, seg as for lora_shrink.
  *   v: optional [T, ldv] fp32 output (ldv >= r_max, multiple of 8), written as
  *   lora_shrink writes it (columns r_a..round_up(r_a, 8)-1 zero; rows without
