@@ -1,4 +1,4 @@
-"""GPU tests of properties the definition fixes at any size (SURVEY section 4):
+"""GPU tests of properties the definition fixes at any size:
 
 * row-permutation equivariance: permuting the rows of a batch (x, ids, y0)
   permutes y and v the same way, bit for bit (each row's delta depends only on
