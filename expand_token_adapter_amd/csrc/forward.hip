@@ -12,11 +12,6 @@
 #include "expand.h"
 #include "decode.h"
 
-// Batches with at most this many rows per adapter (T <= this * num_adapters)
-// take the 16-row-tile kernels of decode.h; others the 64-row-tile kernels.
-#ifndef LORA_DECODE_ROWS_PER_ADAPTER
-#define LORA_DECODE_ROWS_PER_ADAPTER 32
-#endif
 
 using namespace lora;
 
@@ -90,17 +85,6 @@ void launch_dec_shrink(const DecShrinkParams& p, int64_t tasks, hipStream_t st) 
 
 namespace lora {
 
-// The 16-row-tile kernels address x, A_a and B_a through buffer resources
-// with 32-bit byte offsets, and use offsets from 2^31 up as "past the
-// buffer": every buffer they address must hold fewer than 2^31 bytes.
-bool dec_offsets_fit(int64_t rows_bytes, int64_t d, int32_t r_max) {
-    const int64_t lim = ((int64_t)1 << 31) - 65536;
-    return rows_bytes < lim && d * r_max * 2 < lim;
-}
-
-bool use_decode_path(int dtype, int32_t T, int32_t num_adapters) {
-    return dtype == LORA_BF16 && (int64_t)T <= (int64_t)LORA_DECODE_ROWS_PER_ADAPTER * num_adapters;
-}
 
 // v = A x on 16-row tiles (decode.h), written straight to v.
 int run_dec_shrink(int dtype, const void* x, int64_t ldx, int32_t T, int32_t d_in, const lora_adapter* adapters,

@@ -5,6 +5,7 @@
 #include <algorithm>
 
 #include "fused.h"
+#include "fused_decode.h"
 #include "host_checks.h"
 #include "lora_batch.h"
 
@@ -39,6 +40,59 @@ void launch_fused_s(int n_slices, int nmb, const FusedParams& p, unsigned grid, 
         launch_fused<DT, 3>(nmb, p, grid, st);
 }
 
+static_assert(LORA_MAX_SLICES <= kFdMaxSlices && LORA_MAX_SLICES <= kFusedMaxSlices, "slices per launch");
+
+// Column ranges per tile of the decode kernel (0: from the batch's bounds).
+#ifndef LORA_FD_NSPLIT
+#define LORA_FD_NSPLIT 0
+#endif
+
+// Decode batches (at most 32 rows per adapter on average) of rank <= 16
+// adapters take fused_decode_kernel: enough column ranges per tile for about
+// one 16-wave workgroup per CU, at least 16 output chunks per range.
+bool fused_decode_fits(int dtype, int32_t T, int32_t num_adapters, int32_t r_max) {
+    return r_max <= kFdMaxRank && use_decode_path(dtype, T, num_adapters);
+}
+
+int fused_decode_run(const void* x, int64_t ldx, int32_t T, int32_t d_in, const lora_slice* slices, int32_t n_slices,
+                     int32_t num_adapters, int32_t r_max, const lora_segments& seg, hipStream_t st) {
+    FdParams p{};
+    p.x = x;
+    p.ldx = ldx;
+    p.x_bytes = (uint32_t)(((int64_t)(T - 1) * ldx + d_in) * 2);
+    p.K = d_in;
+    p.r_max = r_max;
+    p.perm = seg.perm;
+    p.sched = seg.sched;
+    p.tiles16_off = SchedLayout::make(T, num_adapters).tiles16;
+    const int64_t max_tiles = SchedLayout::max_tiles16(T, num_adapters);
+    p.max_tiles = (int32_t)max_tiles;
+    int64_t nch = 0;
+    for (int32_t q = 0; q < n_slices; ++q) {
+        const lora_slice& sl = slices[q];
+        p.sl[q] = FdSlice{sl.adapters, sl.y, sl.ldy, (uint32_t)(((int64_t)(T - 1) * sl.ldy + sl.d_out) * 2),
+                          sl.d_out, sl.v, sl.ldv, (int32_t)nch};
+        nch += (sl.d_out + kFdChunk - 1) / kFdChunk;
+    }
+    p.nch = (int32_t)nch;
+    const int64_t ns = LORA_FD_NSPLIT > 0 ? LORA_FD_NSPLIT
+                                          : std::min<int64_t>((kNumCus + max_tiles - 1) / max_tiles, nch / kFdWaves);
+    p.nsplit = (int32_t)std::max<int64_t>(1, std::min<int64_t>(ns, nch));
+    if (nch * (p.nsplit + 1) > 0x7fffffff) return LORA_ERR_UNSUPPORTED;
+    p.err = seg.err;
+    // tile t -> XCD t % 8: 8 x nsplit workgroups per 8 tiles
+    const int64_t grid = kNumXcd * p.nsplit * ((max_tiles + kNumXcd - 1) / kNumXcd);
+    if (grid > 0x7fffffff) return LORA_ERR_UNSUPPORTED;
+    const dim3 g((unsigned)grid), block(kFdThreads);
+    if (n_slices == 1)
+        hipLaunchKernelGGL(fused_decode_kernel<1>, g, block, 0, st, p);
+    else if (n_slices == 2)
+        hipLaunchKernelGGL(fused_decode_kernel<2>, g, block, 0, st, p);
+    else
+        hipLaunchKernelGGL(fused_decode_kernel<3>, g, block, 0, st, p);
+    return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
 int fused_run(int dtype, const void* x, int64_t ldx, int32_t T, int32_t d_in, const lora_slice* slices,
               int32_t n_slices, int32_t num_adapters, int32_t r_max, const lora_segments& seg, void* stream) {
     if (n_slices < 1 || n_slices > LORA_MAX_SLICES || !slices) return LORA_ERR_INVALID_ARG;
@@ -64,6 +118,11 @@ int fused_run(int dtype, const void* x, int64_t ldx, int32_t T, int32_t d_in, co
         nch += (sl.d_out + 63) / 64;
     }
     if (nch > 0x7fffffff) return LORA_ERR_UNSUPPORTED;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    bool dec = fused_decode_fits(dtype, T, num_adapters, r_max) && dec_offsets_fit((int64_t)T * ldx * 2, d_in, r_max);
+    for (int32_t q = 0; q < n_slices; ++q)
+        dec = dec && dec_offsets_fit((int64_t)T * slices[q].ldy * 2, slices[q].d_out, r_max);
+    if (dec) return fused_decode_run(x, ldx, T, d_in, slices, n_slices, num_adapters, r_max, seg, st);
     p.x = x;
     p.ldx = ldx;
     p.K = d_in;
@@ -78,7 +137,6 @@ int fused_run(int dtype, const void* x, int64_t ldx, int32_t T, int32_t d_in, co
     const int64_t max_tiles = SchedLayout::max_tiles64(T, num_adapters);
     p.nsplit = (int32_t)std::max<int64_t>(1, std::min<int64_t>(kNumCus / max_tiles, std::max<int64_t>(1, nch / 8)));
     const unsigned grid = grid_for(max_tiles * p.nsplit, 1, kFusedMaxGrid);
-    hipStream_t st = static_cast<hipStream_t>(stream);
     // 16-rank blocks of phase 1: 1 (r_max <= 16), 2, 4 or 8
     const int nmb = r_max <= 16 ? 1 : (r_max <= 32 ? 2 : (r_max <= 64 ? 4 : 8));
     if (dtype == LORA_BF16)

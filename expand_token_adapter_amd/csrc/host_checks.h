@@ -47,4 +47,24 @@ inline unsigned grid_for(int64_t units, int per_wg, int64_t cap) {
 
 inline int rank_groups(int32_t r_max) { return (r_max + 63) / 64; }
 
+// Batches with at most this many rows per adapter (T <= this * num_adapters)
+// take the 16-row-tile kernels (decode.h, fused_decode.h); others the
+// 64-row-tile kernels.
+#ifndef LORA_DECODE_ROWS_PER_ADAPTER
+#define LORA_DECODE_ROWS_PER_ADAPTER 32
+#endif
+
+inline bool use_decode_path(int dtype, int32_t T, int32_t num_adapters) {
+    return dtype == LORA_BF16 && (int64_t)T <= (int64_t)LORA_DECODE_ROWS_PER_ADAPTER * num_adapters;
+}
+
+// The 16-row-tile kernels address x, A_a and B_a (or y and B_a) through
+// buffer resources with 32-bit byte offsets, and use offsets from 2^31 up as
+// "past the buffer": every buffer they address must hold fewer than 2^31
+// bytes.
+inline bool dec_offsets_fit(int64_t rows_bytes, int64_t d, int32_t r_max) {
+    const int64_t lim = ((int64_t)1 << 31) - 65536;
+    return rows_bytes < lim && d * r_max * 2 < lim;
+}
+
 }  // namespace lora

@@ -239,19 +239,20 @@ int lora_expand_add(int dtype, const float* v, int64_t ldv, int32_t T, int32_t d
  * Fused forward: y_t += s_{a(t)} B_{a(t)} (A_{a(t)} x_t) in one launch, the
  * whole h(x) = W x + B A x delta of MOLT section 2.1 for every row with an
  * adapter, without v passing through HBM and without a workspace.  One
- * workgroup carries each 64-row tile from x to y (v = A x over all of d_in
- * into LDS, then a range of d_out's columns).
- * Where it wins (measured on one MI355X, GPU time per call): only where
- * launch latency dominates and each tile's weights are small -- a few rows
- * per adapter, ranks <= 16, d_in and d_out <= 4096 (256 decode rows over 64
- * rank-16 adapters, 4096 -> 4096: 17.3 us against 18.5 us for lora_shrink +
- * lora_expand_add) -- and for projections that share x (lora_forward_multi,
- * against three split calls).  Everywhere else the split calls are faster
- * (1.7x on 4096 fine-tuning rows at 5120 -> 5120, 2.4x on the mixed
+ * workgroup carries a tile from x to y (v = A x over all of d_in, kept in
+ * LDS, then a range of d_out's columns): 16-row tiles with every load of the
+ * tile in flight at once for bf16 decode batches (at most 32 rows per adapter
+ * on average) with r_max <= 16, 64-row tiles otherwise.
+ * Where it wins (measured on one MI355X, GPU time per call): on decode
+ * batches with r_max <= 16, where the split calls are chains of dependent
+ * round trips (256 decode rows over 64 rank-16 adapters, 4096 -> 4096: 12.3 us
+ * against 18.3 us for lora_shrink + lora_expand_add), and for projections
+ * that share x (lora_forward_multi).  Everywhere else the split calls are
+ * faster (1.6x on 4096 fine-tuning rows at 5120 -> 5120, 2.2x on the mixed
  * prefill / decode / fine-tuning batch at 4096 -> 14336, 2.8x on 2048 decode
  * rows over 320 adapters of ranks 8..128 at 8192 -> 8192): their 16-row-tile
  * decode kernels and split-K shrink spread every adapter's weights over the
- * whole chip, while here each tile's workgroup walks all of d_in.  Callers
+ * whole chip, while the 64-row-tile workgroup walks all of d_in.  Callers
  * pick per batch shape, e.g. by timing both once.  Results equal lora_shrink +
  * lora_expand_add up to the order of the fp32 sum over d_in (a fixed order:
  * bit-reproducible).
@@ -282,7 +283,8 @@ int lora_forward(int dtype, const void* x, int64_t ldx, int32_t T, int32_t d_in,
  *   r_max: the largest rank over every slice's adapters.
  * Errors as for lora_forward; LORA_ERR_UNSUPPORTED for n_slices > 1 with
  * r_max > 64 (the slices' v rows and fragments would not fit the LDS).
- * Bad table entries are counted in seg.err once per slice and tile, and only
+ * Bad table entries are counted in seg.err once per slice and tile (16-row
+ * tiles on lora_forward's decode route, 64-row tiles otherwise), and only
  * that slice's rows are skipped.
  */
 #define LORA_MAX_SLICES 3
