@@ -782,7 +782,7 @@ def main():
     b.check_errors()
 
     ex = alg["forward_fused"] if fused else alg["expand"]
-    kern_name = "lora_forward (fused_forward_kernel)" if fused else "lora_expand_add (expand_kernel)"
+    kern_name = "lora_forward" if fused else "lora_expand_add (expand_kernel)"
     achieved = ex["bytes"] / (kern_ms * 1e-3) / 1e9
     line = {
         "metric": "LoRA delta tokens/s + achieved HBM GB/s (or MFMA %) vs peak, mixed multi-LoRA batch",
