@@ -337,7 +337,14 @@ int shrink_entry(int dtype, const void* x, int64_t ldx, int32_t T, int32_t d_in,
     if (rc != LORA_OK || T == 0) return rc;
     if (!ws || !aligned16(ws) || ws_bytes < (size_t)shrink_part_floats(dtype, T, d_in, r_max) * sizeof(float))
         return LORA_ERR_WORKSPACE;
-    if (use_decode_path(dtype, T, num_adapters) && dec_offsets_fit((int64_t)T * ldx * 2, d_in, r_max))
+    // 16-row tiles on decode batches, and for rank <= 16 tables at any row
+    // count: with one rank block per tile the full-K task reads each x row
+    // once and needs no partial sums (4096 rows, one rank-16 adapter, 5120
+    // -> 5120: 14.1 us against 18.6 us for the split-K shrink and its
+    // reduce; with four rank blocks per tile, on the mixed batch, it reads x
+    // four times and is slower, 34.0 against 29.9 us)
+    if ((use_decode_path(dtype, T, num_adapters) || (dtype == LORA_BF16 && r_max <= 16)) &&
+        dec_offsets_fit((int64_t)T * ldx * 2, d_in, r_max))
         return run_dec_shrink(dtype, x, ldx, T, d_in, adapters, num_adapters, r_max, seg, v, ldv, 0,
                               static_cast<hipStream_t>(stream));
     const SchedLayout sl = SchedLayout::make(T, num_adapters);

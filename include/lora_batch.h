@@ -193,8 +193,12 @@ int lora_segments_build_batch(const lora_segments_job* jobs, int32_t n_jobs, int
  *   and zeros in columns r_a..round_up(r_a, 8)-1; rows without an adapter
  *   are left unchanged.  ws: lora_shrink_workspace_bytes(dtype, T, d_in, r_max)
  *   bytes of device memory (the sum over d_in is split into slices of 512
- *   (bf16) or 256 (fp32) elements whose partials are added in slice order).
- *   Two kernels.
+ *   (bf16) or 256 (fp32) elements whose partials are added in slice order:
+ *   two kernels).  bf16 batches with at most 32 rows per adapter on average,
+ *   or with r_max <= 16, take one kernel on 16-row tiles that sums all of
+ *   d_in per tile in a fixed order and writes v directly (ws is checked but
+ *   not used).  Either way the sum order is fixed: results are
+ *   bit-reproducible.
  */
 int lora_shrink(int dtype, const void* x, int64_t ldx, int32_t T, int32_t d_in,
                 const lora_adapter* adapters, int32_t num_adapters, int32_t r_max,
