@@ -193,6 +193,26 @@ def test_forward_decode_bad_table_entries_are_skipped_and_counted():
     assert not torch.equal(y[ok], case.y0[ok])
 
 
+def _long_rows_r64(seed=0):
+    """Long row groups (more than 32 rows per adapter) with ranks 5..64
+    (several not a multiple of 8 or 16): the split-K shrink and its reduce,
+    with d_in = 264 (a ragged last slice) and rows without adapters."""
+    rng = np.random.default_rng(400 + seed)
+    parts = [np.full(70, 1), rng.integers(-1, 8, size=41), np.full(130, 4), np.full(33, 7), np.full(96, 2),
+             rng.integers(0, 8, size=37)]
+    ids = np.concatenate(parts).astype(np.int32)
+    ranks = [8, 24, 5, 40, 64, 16, 64, 33]
+    assert len(ids) > 32 * len(ranks)
+    return workloads.custom(ids, ranks, 264, 200, "bf16", seed=seed, name="long-rows-r64",
+                            scales=[2.0, 0.5, 1.0, -1.5, 2.0, 3.0, 0.25, -0.75])
+
+
+@pytest.mark.parametrize("y0_zero", [False, True])
+def test_forward_long_rows_ranks_to_64(y0_zero):
+    case = GpuCase(_long_rows_r64(), y0_zero=y0_zero)
+    _check_forward(case, TOL["bf16"])
+
+
 def _many_decode(seed=0, A=600, T=2000, d_out=2056):
     """Many adapters with few rows each and a Zipf-like head (an adapter with
     hundreds of rows, several with tens): enough 16-row tiles x rank blocks for
