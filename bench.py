@@ -308,7 +308,9 @@ def multi_slice_report(steps: int, warmup: int, n_sets: int):
         def step(st):
             lb.lora_segments_build(st["ids"], wq.num_adapters, out=st["seg"])
             fwd(st)
-        for i in range(warmup):
+        # every rotating set once, then the warm-up steps (no timed step is
+        # the first to touch a buffer)
+        for i in range(n_sets + warmup):
             step(sets[i % n_sets])
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -316,9 +318,33 @@ def multi_slice_report(steps: int, warmup: int, n_sets: int):
             step(sets[i % n_sets])
         torch.cuda.synchronize()
         ms = (time.perf_counter() - t0) * 1e3 / steps
+        # GPU time per step, free of host launch costs: a captured graph of one
+        # step over every set, replayed between events (outside the timed loop)
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream(device=dev)
+        cap.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(cap):
+            for st in sets:
+                step(st)
+        torch.cuda.current_stream(dev).wait_stream(cap)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for st in sets:
+                step(st)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 25
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        gpu_us = e0.elapsed_time(e1) * 1e3 / (reps * n_sets)
+        del g
         print(json.dumps({"multi_slice": name, "workload": "decode-64x-r16-4096 q/k/v (d_out 4096/1024/1024)",
                           "rows": wq.T, "ms_per_step": ms, "rows_per_s": wq.T / (ms * 1e-3),
-                          "forward_algorithmic_bytes": alg, "steps": steps}), flush=True)
+                          "gpu_us_per_step": gpu_us, "forward_algorithmic_bytes": alg, "steps": steps}), flush=True)
 
 
 def cost_model_report(reps: int = 10):
@@ -633,7 +659,7 @@ def workload_block(idx, steps, warmup, forward="auto"):
     b = Bench(wl, n_sets)
     alg = algorithmic(wl)
     choice = b.pick_forward(forward)
-    for i in range(warmup):
+    for i in range(n_sets + warmup):
         b.step(b.sets[i % n_sets])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -723,7 +749,9 @@ def main():
         else:
             b.step(sets[i % len(sets)], ev)
 
-    for i in range(args.warmup):
+    # every rotating set once, then the warm-up steps (no timed step is the
+    # first to touch a buffer)
+    for i in range(len(sets) + args.warmup):
         run(i)
     torch.cuda.synchronize()
 

@@ -8,9 +8,9 @@
 // a workgroup = (16-row tile, one of `nsplit` column ranges of the output
 // chunks) with 16 waves, and every load it needs -- the tile's A_a blocks and
 // x rows for phase 1, the first output chunk's B_a block and y rows for
-// phase 2 -- is issued as soon as the tile record, the adapter entries and
-// the row indices have arrived (three round trips in all, plus the result's
-// store).
+// phase 2 -- is issued as soon as the tile record, then the adapter entries
+// and the row indices (scalar loads, requested together) have arrived: three
+// round trips in all, plus the result's store.
 //   phase 1  v = A_a x: wave w takes the w-th sixteenth of d_in's 32-element
 //            steps and loads its x fragments and every slice's A fragments
 //            straight into registers in MFMA operand layout (lane (lr, lg):
@@ -116,6 +116,14 @@ __global__ __launch_bounds__(kFdThreads) void fused_decode_kernel(FdParams p) {
     const int n16 = *cptr(p.sched);
     asm volatile("" ::"s"(rec.adapter), "s"(rec.pos0), "s"(rec.rows), "s"(n16));
     if (t >= n16) return;
+    const int nrows = rec.rows;
+    // The tile's rows (rows past it repeat its first) through scalar loads,
+    // requested with the adapter entries (the empty asm below reads both
+    // before the entries are tested): they do not queue behind the vector
+    // loads of the other workgroups' weights.
+    int32_t prow[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) prow[k] = *cptr(p.perm + rec.pos0 + (k < nrows ? k : 0));
     // each slice's adapter entry; a bad one is counted and its slice skipped
     bool ok_s[S];
     int r_s[S];
@@ -123,9 +131,16 @@ __global__ __launch_bounds__(kFdThreads) void fused_decode_kernel(FdParams p) {
     const char* A_s[S];
     const char* B_s[S];
     bool any = false;
+    lora_adapter ad_s[S];
+#pragma unroll
+    for (int q = 0; q < S; ++q) ad_s[q] = load_adapter(p.sl[q].adapters, rec.adapter);
+    asm volatile("" ::"s"(prow[0]), "s"(prow[1]), "s"(prow[2]), "s"(prow[3]), "s"(prow[4]), "s"(prow[5]),
+                 "s"(prow[6]), "s"(prow[7]), "s"(prow[8]), "s"(prow[9]), "s"(prow[10]), "s"(prow[11]),
+                 "s"(prow[12]), "s"(prow[13]), "s"(prow[14]), "s"(prow[15]), "s"(ad_s[0].rank),
+                 "s"(ad_s[S - 1].rank));
 #pragma unroll
     for (int q = 0; q < S; ++q) {
-        const lora_adapter ad = load_adapter(p.sl[q].adapters, rec.adapter);
+        const lora_adapter& ad = ad_s[q];
         ok_s[q] = adapter_ok(ad, p.r_max);
         if (!ok_s[q] && c == 0 && threadIdx.x == 0) atomicAdd(p.err, 1);
         r_s[q] = ok_s[q] ? ad.rank : 0;
@@ -135,9 +150,10 @@ __global__ __launch_bounds__(kFdThreads) void fused_decode_kernel(FdParams p) {
         any |= ok_s[q];
     }
     if (!any) return;
-    const int nrows = rec.rows;
-    // row lr of the tile (rows past it repeat its first)
-    int32_t row_lr = p.perm[rec.pos0 + (lr < nrows ? lr : 0)];
+    // lane lr takes row lr
+    int32_t row_lr = prow[0];
+#pragma unroll
+    for (int k = 1; k < 16; ++k) row_lr = lr == k ? prow[k] : row_lr;
 
     // ---- phase 2 addressing (G = 2 rank groups of 16 per MFMA)
     // Chunk columns c0 .. c0 + 63 of slice q; MFMA nb (0, 1) covers columns
@@ -169,7 +185,12 @@ __global__ __launch_bounds__(kFdThreads) void fused_decode_kernel(FdParams p) {
     const int j0 = 8 * (lg & 1);
     const int yr = lane >> 3;
     const int yc = 8 * (lane & 7);
-    int64_t yrow0 = 0, yrow1 = 0;  // set once the row indices are in
+    int64_t yrow0 = prow[0], yrow1 = prow[8];  // rows yr and yr + 8
+#pragma unroll
+    for (int k = 1; k < 8; ++k) {
+        yrow0 = yr == k ? prow[k] : yrow0;
+        yrow1 = yr == k ? prow[k + 8] : yrow1;
+    }
     // this wave's chunks: ch0 + wave, ch0 + wave + 16, ...; -1: none
     auto chunk_of = [&](int k) {
         const int ch = ch0 + wave + kFdWaves * k;
@@ -248,17 +269,13 @@ __global__ __launch_bounds__(kFdThreads) void fused_decode_kernel(FdParams p) {
         }
     };
 
-    // Everything that needs only the adapter entries goes in flight first (the
-    // first chunk's weights, the first round's A fragments); then, once the
-    // row indices are in, the x fragments and y rows.
+    // Every load of the tile in one batch: the first chunk's weights, the
+    // first round's A and x fragments, the first chunk's y rows.
     F wf[2];
     u32x4_t yq[2];
+    const uint32_t xo = lr < nrows ? (uint32_t)((int64_t)row_lr * p.ldx * EB) + 16u * lg : kBufOff;
     load_w(chunk_of(0), wf);
     issue_a(sb0);
-    asm volatile("" : "+v"(row_lr)::"memory");
-    yrow0 = __shfl(row_lr, yr, kWave);
-    yrow1 = __shfl(row_lr, yr + 8, kWave);
-    const uint32_t xo = lr < nrows ? (uint32_t)((int64_t)row_lr * p.ldx * EB) + 16u * lg : kBufOff;
     issue_x(sb0, xo);
     load_y(chunk_of(0), yq);
     asm volatile("" ::: "memory");
