@@ -1,5 +1,5 @@
 """A captured HIP graph of one step (batched segment build, shrink, expand-add,
-backward with saved v) replays to the eager results, bit for bit, on every
+one-launch forward, backward with saved v) replays to the eager results, bit for bit, on every
 replay, with eager work and synchronisations between the replays.  The kernels
 clear their own scratch (no memset nodes are recorded) and every reduction runs
 in a fixed order, so a replay must reproduce the eager step exactly."""
@@ -24,8 +24,18 @@ def _mixed():
                             ft_count=96, name="graph-mixed")
 
 
-def test_graph_replays_match_eager_step():
-    wl = _mixed()
+def _decode16():
+    # at most 32 rows per adapter, ranks <= 16: the 16-row-tile shrink and
+    # expand, the one-launch decode forward and the streaming backward
+    rng = np.random.default_rng(23)
+    ids = np.concatenate([rng.integers(-1, 24, size=120), np.full(40, 3)]).astype(np.int32)
+    return workloads.custom(ids, [16, 8, 5, 16, 12, 1] * 4, 200, 456, "bf16", seed=5, ft_start=len(ids) - 40,
+                            ft_count=40, name="graph-decode16")
+
+
+@pytest.mark.parametrize("kind", ["mixed", "decode16"])
+def test_graph_replays_match_eager_step(kind):
+    wl = _mixed() if kind == "mixed" else _decode16()
     dev = torch.device("cuda:0")
     s, n = wl.ft_start, wl.ft_count
     A = [to_dev(a, "bf16", dev) for a in wl.A]
@@ -37,6 +47,7 @@ def test_graph_replays_match_eager_step():
     ids = torch.from_numpy(wl.ids).to(dev)
     ft_ids = ids[s:s + n].contiguous()
     y = y0.clone()
+    yf = y0.clone()  # the one-launch forward's output
     v = torch.zeros((wl.T, (table.r_max + 7) // 8 * 8), dtype=torch.float32, device=dev)
     dx = torch.zeros((n, wl.d_in), dtype=torch.bfloat16, device=dev)
     dA = [torch.zeros(a.shape, dtype=torch.float32, device=dev) for a in A]
@@ -54,6 +65,7 @@ def test_graph_replays_match_eager_step():
         # without an adapter are left unchanged by design, the rest rewritten
         v.fill_(-1.0)
         y.copy_(y0)
+        yf.copy_(y0)
         dx.zero_()
         for t in dA + dB:
             t.zero_()
@@ -62,12 +74,13 @@ def test_graph_replays_match_eager_step():
         lb.lora_segments_build_batch([(ids, seg), (ft_ids, seg_ft)], wl.num_adapters)
         lb.lora_shrink(x, table, seg, v=v, ws=ws)
         lb.lora_expand_add(v, table, seg, y)
+        lb.lora_forward(x, table, seg, yf)
         lb.lora_backward(x[s:s + n], dy, table, grads, seg_ft, dx=dx, v_saved=v[s:s + n], ws=bws)
 
     reset()
     step()
     torch.cuda.synchronize()
-    want = [t.clone() for t in [y, v, dx] + dA + dB]
+    want = [t.clone() for t in [y, yf, v, dx] + dA + dB]
     assert seg.err.item() == 0 and seg_ft.err.item() == 0
 
     side = torch.cuda.Stream(device=dev)
@@ -86,7 +99,7 @@ def test_graph_replays_match_eager_step():
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        got = [y, v, dx] + dA + dB
+        got = [y, yf, v, dx] + dA + dB
         for i, (a, b) in enumerate(zip(got, want)):
             assert torch.equal(a, b), (k, i)
         assert seg.err.item() == 0 and seg_ft.err.item() == 0

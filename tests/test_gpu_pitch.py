@@ -18,6 +18,17 @@ if torch.cuda.is_available():
 DEV = "cuda:0"
 
 
+def _case_decode16():
+    # a bf16 decode batch of rank <= 16 adapters (at most 32 rows per adapter):
+    # the 16-row-tile shrink and expand and the one-launch decode forward; the
+    # fine-tuning rows (rank 16, d_out >= 2 d_in) take the streaming backward
+    rng = np.random.default_rng(19)
+    ids = np.concatenate([rng.integers(-1, 40, size=150), np.full(48, 7)]).astype(np.int32)
+    ranks = [16, 5, 8, 12, 1, 16, 3, 16] * 5
+    return workloads.custom(ids, ranks, 136, 520, "bf16", seed=21, ft_start=len(ids) - 48, ft_count=48,
+                            name="pitch-decode16")
+
+
 def _case(dtype):
     # rows without an adapter, ragged runs, ranks that are not multiples of 8;
     # the fine-tuning rows (rank 40) close the batch
@@ -96,5 +107,15 @@ def test_pitched_views_match_contiguous_buffers_bit_for_bit(dtype):
     got, buf = _run(wl, dtype, pitched=True)
     assert buf.padding_untouched()
     assert want["dA[1], saved v"].abs().sum().item() > 0  # the fine-tuning adapter received gradients
+    for k in want:
+        assert torch.equal(got[k], want[k]), k
+
+
+def test_pitched_views_on_the_decode_routes_bit_for_bit():
+    wl = _case_decode16()
+    want, _ = _run(wl, "bf16", pitched=False)
+    got, buf = _run(wl, "bf16", pitched=True)
+    assert buf.padding_untouched()
+    assert want["dA[7], saved v"].abs().sum().item() > 0
     for k in want:
         assert torch.equal(got[k], want[k]), k
