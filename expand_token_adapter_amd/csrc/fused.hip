@@ -11,6 +11,13 @@
 
 using namespace lora;
 
+namespace lora {
+// forward.hip: the 16-row-tile shrink (needs no workspace)
+int run_dec_shrink(int dtype, const void* x, int64_t ldx, int32_t T, int32_t d_in, const lora_adapter* adapters,
+                   int32_t num_adapters, int32_t r_max, const lora_segments& seg, float* v, int64_t ldv,
+                   int32_t v_by_pos, hipStream_t st);
+}  // namespace lora
+
 namespace {
 
 constexpr int64_t kFusedMaxGrid = 8192;
@@ -123,6 +130,20 @@ int fused_run(int dtype, const void* x, int64_t ldx, int32_t T, int32_t d_in, co
     for (int32_t q = 0; q < n_slices; ++q)
         dec = dec && dec_offsets_fit((int64_t)T * slices[q].ldy * 2, slices[q].d_out, r_max);
     if (dec) return fused_decode_run(x, ldx, T, d_in, slices, n_slices, num_adapters, r_max, seg, st);
+    // One slice with v given: where the split kernels need no workspace -- the
+    // 16-row-tile shrink on decode batches or at r_max <= 16, then the expand
+    // -- they are faster than the 64-row-tile kernel, which walks all of d_in
+    // per tile; the call runs them (v passes through HBM, results as
+    // lora_shrink + lora_expand_add bit for bit).
+    if (n_slices == 1 && slices[0].v && (use_decode_path(dtype, T, num_adapters) ||
+                                         (dtype == LORA_BF16 && r_max <= 16)) &&
+        dec_offsets_fit((int64_t)T * ldx * 2, d_in, r_max)) {
+        const lora_slice& sl = slices[0];
+        rc = run_dec_shrink(dtype, x, ldx, T, d_in, sl.adapters, num_adapters, r_max, seg, sl.v, sl.ldv, 0, st);
+        if (rc != LORA_OK) return rc;
+        return lora_expand_add(dtype, sl.v, sl.ldv, T, sl.d_out, sl.adapters, num_adapters, r_max, seg, sl.y,
+                               sl.ldy, stream);
+    }
     p.x = x;
     p.ldx = ldx;
     p.K = d_in;

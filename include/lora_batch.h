@@ -240,31 +240,34 @@ int lora_expand_add(int dtype, const float* v, int64_t ldv, int32_t T, int32_t d
                     lora_segments seg, void* y, int64_t ldy, void* stream);
 
 /*
- * Fused forward: y_t += s_{a(t)} B_{a(t)} (A_{a(t)} x_t) in one launch, the
- * whole h(x) = W x + B A x delta of MOLT section 2.1 for every row with an
- * adapter, without v passing through HBM and without a workspace.  One
- * workgroup carries a tile from x to y (v = A x over all of d_in, kept in
- * LDS, then a range of d_out's columns): 16-row tiles with every load of the
- * tile in flight at once for bf16 decode batches (at most 32 rows per adapter
- * on average) with r_max <= 16, 64-row tiles otherwise.
- * Where it wins (measured on one MI355X, GPU time per call): on decode
- * batches with r_max <= 16, where the split calls are chains of dependent
- * round trips (256 decode rows over 64 rank-16 adapters, 4096 -> 4096: 12.3 us
- * against 18.3 us for lora_shrink + lora_expand_add), and for projections
- * that share x (lora_forward_multi).  Everywhere else the split calls are
- * faster (1.6x on 4096 fine-tuning rows at 5120 -> 5120, 2.2x on the mixed
- * prefill / decode / fine-tuning batch at 4096 -> 14336, 2.8x on 2048 decode
- * rows over 320 adapters of ranks 8..128 at 8192 -> 8192): their 16-row-tile
- * decode kernels and split-K shrink spread every adapter's weights over the
- * whole chip, while the 64-row-tile workgroup walks all of d_in.  Callers
- * pick per batch shape, e.g. by timing both once.  Results equal lora_shrink +
- * lora_expand_add up to the order of the fp32 sum over d_in (a fixed order:
- * bit-reproducible).
+ * Forward in one call: y_t += s_{a(t)} B_{a(t)} (A_{a(t)} x_t), the whole
+ * h(x) = W x + B A x delta of MOLT section 2.1 for every row with an adapter,
+ * without a workspace.  The call takes the fastest kernel sequence its
+ * arguments allow (decode batch: bf16 with at most 32 rows per adapter on
+ * average):
+ *   - decode batch, r_max <= 16: one launch, 16-row tiles, one workgroup per
+ *     (tile, column range) with every load of the tile in flight at once, v
+ *     kept in LDS (256 decode rows over 64 rank-16 adapters, 4096 -> 4096:
+ *     12.7 us against 18.4 us for lora_shrink + lora_expand_add);
+ *   - otherwise, with v given, on a decode batch or at r_max <= 16 (bf16):
+ *     the split calls' kernels that need no workspace, the 16-row-tile shrink
+ *     into v, then the expand; results equal lora_shrink + lora_expand_add
+ *     bit for bit;
+ *   - otherwise: one launch, 64-row tiles (v = A x over all of d_in in LDS,
+ *     then a range of d_out's columns).  On long row groups with r_max > 16
+ *     this is slower than the split calls (2.2x on the mixed prefill / decode
+ *     / fine-tuning batch at 4096 -> 14336, whose split-K shrink spreads x
+ *     over the whole chip), as it is wherever the other routes apply and v
+ *     is not given (1.6x on 4096 fine-tuning rows at rank 16, 2.8x on 2048
+ *     decode rows over 320 adapters of ranks 8..128).
+ * The one-launch routes equal lora_shrink + lora_expand_add up to the order
+ * of the fp32 sum over d_in (a fixed order: bit-reproducible).
  *   x [T, ldx], y [T, ldy] in/out (dtype); adapters, seg as for lora_shrink.
  *   v: optional [T, ldv] fp32 output (ldv >= r_max, multiple of 8), written as
  *   lora_shrink writes it (columns r_a..round_up(r_a, 8)-1 zero; rows without
  *   an adapter unchanged), e.g. for a later lora_backward; NULL skips it.
- * Errors and device-side data checks as for lora_shrink / lora_expand_add.
+ * Errors and device-side data checks as for lora_shrink / lora_expand_add
+ * (a bad table entry is counted once per tile by each kernel that meets it).
  */
 int lora_forward(int dtype, const void* x, int64_t ldx, int32_t T, int32_t d_in, int32_t d_out,
                  const lora_adapter* adapters, int32_t num_adapters, int32_t r_max, lora_segments seg,
@@ -278,7 +281,8 @@ int lora_forward(int dtype, const void* x, int64_t ldx, int32_t T, int32_t d_in,
  * all of them and v = A x of every slice stays in LDS.  For each slice q and
  * each row t with adapter a = a(t) (the same adapter index in every slice):
  *     y_q[t] += s_{q,a} B_{q,a} (A_{q,a} x_t),
- * exactly what lora_forward computes for that slice alone.
+ * exactly what lora_forward computes for that slice alone without v (bit
+ * for bit: the same one-launch kernel family and sum order).
  *   slices: HOST array of n_slices (1..LORA_MAX_SLICES) entries:
  *     adapters  device table [num_adapters] of the slice (A [r, d_in],
  *               B [d_out, r]; ranks may differ between slices);

@@ -43,13 +43,14 @@ class GpuCase:
         self.y0 = torch.zeros_like(to_dev(wl.y0, dt, self.dev)) if y0_zero else to_dev(wl.y0, dt, self.dev)
         self.y0_zero = y0_zero
 
-    def forward(self, fused: bool = False):
-        """Split path (lora_shrink + lora_expand_add) or the one-launch lora_forward."""
+    def forward(self, fused: bool = False, with_v: bool = True):
+        """Split path (lora_shrink + lora_expand_add) or lora_forward (with_v=False:
+        no v output, so lora_forward runs one of its one-launch kernels)."""
         y = self.y0.clone()
         seg = lb.lora_segments_build(self.ids, self.wl.num_adapters)
         if fused:
             v = torch.zeros((self.wl.T, (self.table.r_max + 7) // 8 * 8), dtype=torch.float32, device=self.dev)
-            lb.lora_forward(self.x, self.table, seg, y, v=v)
+            lb.lora_forward(self.x, self.table, seg, y, v=v if with_v else None)
         else:
             v = lb.lora_shrink(self.x, self.table, seg)
             lb.lora_expand_add(v, self.table, seg, y)

@@ -1,6 +1,9 @@
-"""GPU parity of lora_forward's decode route (bf16, r_max <= 16, at most 32
-rows per adapter): one 16-wave workgroup per (16-row tile, column range),
-v = A x over d_in in registers, then y += s B v.
+"""GPU parity of lora_forward's routes.  Its decode route (bf16, r_max <= 16,
+at most 32 rows per adapter): one 16-wave workgroup per (16-row tile, column
+range), v = A x over d_in in registers, then y += s B v.  With v given and a
+decode batch or r_max <= 16 otherwise, the call runs the split calls' kernels
+(bit-equal to lora_shrink + lora_expand_add); without v, the 64-row-tile
+kernel.
 
 Each case is compared with the fp64 oracle at the usual bar (max|err| <=
 2e-2 * max|ref| for y and v): ragged ranks (1, 3, 5, 8, 12, 16), rows without
@@ -13,6 +16,8 @@ B = 0.
 import numpy as np
 import pytest
 import torch
+
+import functools
 
 import workloads
 
@@ -113,3 +118,57 @@ def test_fused_decode_one_tile_many_ranges():
     ids = np.array([0] * 16 + [1], dtype=np.int32)
     wl = workloads.custom(ids, [16, 7], 96, 2560, "bf16", seed=4, name="dec16-ranges", scales=[1.5, -2.0])
     _check(GpuCase(wl))
+
+
+_config = functools.lru_cache(maxsize=None)(workloads.config)
+
+
+def _zipf64(seed=5):
+    """Decode batch with ranks up to 64 (at most 32 rows per adapter)."""
+    rng = np.random.default_rng(500 + seed)
+    k = np.arange(1, 81, dtype=np.float64)
+    ids = rng.choice(80, size=600, p=(k ** -1.1) / (k ** -1.1).sum()).astype(np.int32)
+    ids[rng.random(600) < 0.05] = -1
+    ranks = rng.choice(np.array([8, 12, 16, 32, 40, 64]), size=80).astype(np.int32)
+    return workloads.custom(ids, ranks, 264, 520, "bf16", seed=seed, name="zipf64")
+
+
+def _long16(seed=6):
+    """Long row groups (more than 32 rows per adapter) at ranks <= 16."""
+    rng = np.random.default_rng(600 + seed)
+    ids = np.concatenate([np.full(300, 0), rng.integers(-1, 3, size=50), np.full(200, 2)]).astype(np.int32)
+    return workloads.custom(ids, [16, 5, 12], 200, 328, "bf16", seed=seed, name="long16")
+
+
+@pytest.mark.parametrize("make", [_zipf64, _long16])
+def test_forward_with_v_runs_the_split_kernels_bit_for_bit(make):
+    wl = make()
+    case = GpuCase(wl, y0_zero=False)
+    yf, vf, seg = case.forward(fused=True)
+    ys, vs, _ = case.forward()
+    assert int(seg.err.item()) == 0
+    assert torch.equal(yf, ys) and torch.equal(vf[:, :vs.shape[1]], vs)
+    y_ref, _ = case.oracle_forward()
+    assert rel_err(yf, y_ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("make", [_zipf64, _long16])
+def test_forward_without_v_runs_one_launch_and_matches_oracle(make):
+    case = GpuCase(make(), y0_zero=True)
+    y, _, seg = case.forward(fused=True, with_v=False)
+    y_ref, _ = case.oracle_forward()
+    assert int(seg.err.item()) == 0
+    assert rel_err(y, y_ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("idx", [4, 5])
+def test_forward_without_v_configs_full_size(idx):
+    """The 64-row-tile one-launch kernel on the fine-tuning and many-adapter
+    workloads (with v given, lora_forward runs the split kernels there)."""
+    wl = _config(idx)
+    print(f"lora_forward without v {wl.name} T={wl.T}", flush=True)
+    case = GpuCase(wl, y0_zero=True)
+    y, _, seg = case.forward(fused=True, with_v=False)
+    y_ref, _ = case.oracle_forward()
+    assert int(seg.err.item()) == 0
+    assert rel_err(y, y_ref) <= TOL["bf16"]

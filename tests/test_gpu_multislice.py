@@ -3,7 +3,9 @@
 Several projections read one x, each with its own adapter table (same ids).
 Every slice's y must match the fp64 oracle of that slice alone (the bf16 /
 fp32 bars of the forward), and equal bit for bit what lora_forward computes
-for the slice alone: the per-slice arithmetic and its order do not change.
+for the slice alone without a v output (always a one-launch kernel): the
+per-slice arithmetic and its order do not change.  Each slice's v matches
+the oracle.
 """
 import numpy as np
 import pytest
@@ -50,8 +52,10 @@ def _run(wls, dtype, with_v, multi=True, bad=None):
     if multi:
         lb.lora_forward_multi(x, [(tables[q], ys[q], vs[q]) for q in range(len(wls))], seg, r_max=r_max)
     else:
+        # without v: lora_forward's one-launch kernels (with v it may run the
+        # split kernels instead)
         for q in range(len(wls)):
-            lb.lora_forward(x, tables[q], seg, ys[q], v=vs[q], r_max=r_max)
+            lb.lora_forward(x, tables[q], seg, ys[q], r_max=r_max)
     torch.cuda.synchronize()
     return ys, vs, seg
 
@@ -97,10 +101,9 @@ def test_multi_slice_matches_oracle_and_single_slices(case, dtype):
             r = int(wl.ranks[ids[t]])
             np.testing.assert_allclose(vs[q][t, :r].double().cpu().numpy(), v_ref[t, :r], rtol=1e-4,
                                        atol=1e-4 * max(np.max(np.abs(v_ref)), 1e-30))
-    ys1, vs1, _ = _run(wls, dtype, with_v=True, multi=False)
+    ys1, _, _ = _run(wls, dtype, with_v=False, multi=False)
     for q in range(len(wls)):
         assert torch.equal(ys[q], ys1[q]), (case, q)
-        assert torch.equal(vs[q], vs1[q]), (case, q)
 
 
 def test_multi_slice_bad_entry_skips_only_its_slice():
