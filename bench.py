@@ -507,6 +507,11 @@ class Bench:
     def forward_fused(self, st):
         self.lb.lora_forward(st["x"], st["table"], st["seg"], st["y"], v=st["v"])
 
+    def forward_one_launch(self, st):
+        # without v: always one launch (with v, decode batches and r_max <= 16
+        # run the split kernels)
+        self.lb.lora_forward(st["x"], st["table"], st["seg"], st["y"])
+
     def backward(self, st, v_saved=True):
         s, n = self.wl.ft_start, self.wl.ft_count
         vs = st["v"][s:s + n] if v_saved else None
@@ -586,7 +591,8 @@ class Bench:
         call over every rotating copy (segments built first), replayed between events."""
         torch = self.torch
         ops = {"segments": self.seg_build, "shrink": self.shrink, "expand": self.expand,
-               "forward_fused": self.forward_fused, "backward": self.backward}
+               "forward_fused": self.forward_fused, "forward_one_launch": self.forward_one_launch,
+               "backward": self.backward}
         out = {}
         for st in self.sets:
             self.seg_build(st)
@@ -642,7 +648,7 @@ def call_report(wl, times, alg):
     """Per-call GPU time with its algorithmic bytes and HBM fraction."""
     out = {}
     keymap = {"segments": "segments", "shrink": "shrink", "expand": "expand", "forward_fused": "forward_fused",
-              "backward": "backward"}
+              "forward_one_launch": "forward_fused", "backward": "backward"}
     for name, us in times.items():
         b = alg[keymap[name]]["bytes"]
         out[name] = {"us_per_call": us, "algorithmic_bytes": b, "GBps": b / (us * 1e-6) / 1e9,
@@ -668,7 +674,7 @@ def workload_block(idx, steps, warmup, forward="auto"):
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
     dist = b.distribution(steps, warmup + steps)
-    names = ["segments", "shrink", "expand", "forward_fused"] + (["backward"] if b.has_ft else [])
+    names = ["segments", "shrink", "expand", "forward_fused", "forward_one_launch"] + (["backward"] if b.has_ft else [])
     calls = call_report(wl, b.call_times(names), alg)
     b.check_errors()
     fwd_us = calls["shrink"]["us_per_call"] + calls["expand"]["us_per_call"]
