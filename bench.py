@@ -405,7 +405,7 @@ def cost_model_report(reps: int = 10):
             torch.cuda.synchronize()
             meas = e0.elapsed_time(e1) * 1e-3 / reps
             pred = model.predict(op, op_ids, wl.ranks, wl.d_in, wl.d_out,
-                                 r_max=r_ft if op == "backward" else 0)
+                                 r_max=r_ft if op == "backward" else 0, with_v=True)
             print(json.dumps({"workload": workloads.CONFIG_NAMES[w], "op": op, "measured_us": meas * 1e6,
                               "predicted_us": pred * 1e6, "rel_err": pred / meas - 1.0}), flush=True)
 

@@ -21,6 +21,14 @@ them; sum_t ceil(r / 16) (d_in + d_out) = row elements once per 16-rank group,
 as the backward's token contraction reads them), with non-negative coefficients fitted by bounded least squares on
 relative residuals, so that a 10 us and a 1 ms call weigh alike.
 
+Each entry point has one model per kernel route the library takes: the
+backward's streaming route is ``backward_stream``; ``forward_fused`` is
+``lora_forward`` without v, whose one-launch kernels are the 16-row-tile
+decode kernel (``forward_fused_decode``: bf16 decode batches, at most 32 rows
+per adapter, with r_max <= 16) or the 64-row-tile kernel
+(``forward_fused``); with v, ``lora_forward`` runs the split kernels of
+``forward`` on decode batches and at r_max <= 16 (``route``).
+
 ``features`` and ``fit`` / ``predict`` run on the host; ``calibrate`` times the
 library's calls on synthetic batches on the GPU (random ids, ranks and
 weights; no dataset).  ``python -m expand_token_adapter_amd.cost_model``
@@ -44,20 +52,36 @@ _OP_FEATURES = {
     "segments": ("const", "rows", "adapters", "tiles16"),
     "forward": ("const", "row_elems", "weight_elems", "rank_rows", "adapters", "tiles16"),
     "forward_fused": ("const", "row_elems", "weight_elems", "rank_rows", "adapters", "tiles16"),
+    "forward_fused_decode": ("const", "row_elems", "weight_elems", "tiles16"),
     "backward": ("const", "row_elems", "weight_elems", "rank_rows", "adapters", "tiles16", "group_elems"),
     "backward_stream": ("const", "row_elems", "weight_elems", "rank_rows", "adapters", "tiles16"),
 }
 
 
-def route(op: str, ranks: Sequence[int], d_in: int, d_out: int, r_max: int = 0) -> str:
-    """The model entry of a bf16 call: the backward takes its streaming route
-    ('backward_stream': one pass over dY) when every adapter has rank <= 16
-    (r_max, default max(ranks)) and d_out >= 2 d_in, as the library does;
-    other entry points have one model each."""
+DECODE_ROWS_PER_ADAPTER = 32  # the library's decode-batch bound: T <= 32 x (adapters in the table)
+
+
+def route(op: str, ranks: Sequence[int], d_in: int, d_out: int, r_max: int = 0, T: int = -1,
+          with_v: bool = False) -> str:
+    """The model entry of a bf16 call, as the library routes it.  r_max
+    defaults to max(ranks); T is the call's row count (-1: not a decode batch).
+    - backward: 'backward_stream' (one pass over dY) when r_max <= 16 and
+      d_out >= 2 d_in, else 'backward';
+    - forward_fused (lora_forward): 'forward_fused_decode' on decode batches
+      (T <= 32 x len(ranks)) with r_max <= 16; else, with v given, 'forward'
+      (the split kernels) on decode batches or at r_max <= 16; else
+      'forward_fused' (the 64-row-tile kernel);
+    - the others: one model each."""
+    r = r_max or (max(ranks) if len(ranks) else 0)
     if op == "backward":
-        r = r_max or (max(ranks) if len(ranks) else 0)
         if r <= 16 and d_out >= 2 * d_in:
             return "backward_stream"
+    if op == "forward_fused":
+        decode = 0 <= T <= DECODE_ROWS_PER_ADAPTER * len(ranks)
+        if decode and r <= 16:
+            return "forward_fused_decode"
+        if with_v and (decode or r <= 16):
+            return "forward"
     return op
 
 
@@ -99,8 +123,8 @@ class CostModel:
     def __init__(self, coef: Dict[str, Sequence[float]]):
         self.coef = {op: np.asarray(c, dtype=np.float64) for op, c in coef.items()}
 
-    def predict(self, op: str, ids, ranks, d_in: int, d_out: int, r_max: int = 0) -> float:
-        key = route(op, ranks, d_in, d_out, r_max)
+    def predict(self, op: str, ids, ranks, d_in: int, d_out: int, r_max: int = 0, with_v: bool = False) -> float:
+        key = route(op, ranks, d_in, d_out, r_max, T=len(ids), with_v=with_v)
         return float(features(ids, ranks, d_in, d_out) @ self.coef[key if key in self.coef else op])
 
     def to_json(self) -> str:
@@ -187,7 +211,7 @@ def calibrate(shapes=None, reps: int = 10, ops: Iterable[str] = OPS, seed: int =
         calls = {
             "segments": lambda: lb.lora_segments_build(ids, len(ranks), out=seg),
             "forward": lambda: (lb.lora_shrink(x, table, seg, v=v, ws=ws), lb.lora_expand_add(v, table, seg, y)),
-            "forward_fused": lambda: lb.lora_forward(x, table, seg, y, v=v),
+            "forward_fused": lambda: lb.lora_forward(x, table, seg, y),  # without v: one launch
             "backward": lambda: lb.lora_backward(x, dy, table, grads, seg, dx=dx, v_saved=v, ws=bws),
         }
         feats = features(ids_np, ranks, d_in, d_out)
@@ -202,7 +226,7 @@ def calibrate(shapes=None, reps: int = 10, ops: Iterable[str] = OPS, seed: int =
             e1.record()
             torch.cuda.synchronize()
             sec = e0.elapsed_time(e1) * 1e-3 / reps
-            samples.append({"op": route(op, ranks, d_in, d_out), "features": feats.tolist(), "seconds": sec,
+            samples.append({"op": route(op, ranks, d_in, d_out, T=T), "features": feats.tolist(), "seconds": sec,
                             "shape": {"T": T, "d_in": d_in, "d_out": d_out, "adapters": len(ranks), "dist": dist}})
         if progress:
             progress(k, T, d_in, d_out, len(ranks), dist)

@@ -67,3 +67,36 @@ def test_model_json_round_trip_and_predict():
     assert m2.predict("forward", ids, ranks, 64, 32) == pytest.approx(m.predict("forward", ids, ranks, 64, 32))
     f = cm.features(ids, ranks, 64, 32)
     assert m.predict("forward", ids, ranks, 64, 32) == pytest.approx(float(f @ m.coef["forward"]))
+
+
+def test_route_follows_the_library_routes():
+    r16, mixed = [16] * 64, [8, 16, 32, 64] * 8
+    # backward: streaming at r_max <= 16 and d_out >= 2 d_in
+    assert cm.route("backward", r16, 4096, 14336) == "backward_stream"
+    assert cm.route("backward", r16, 4096, 4096) == "backward"
+    assert cm.route("backward", mixed, 4096, 14336) == "backward"
+    assert cm.route("backward", mixed, 4096, 14336, r_max=16) == "backward_stream"
+    # lora_forward: decode batches (T <= 32 per adapter of the table) at r_max <= 16
+    # take the 16-row-tile kernel, with or without v
+    for with_v in (False, True):
+        assert cm.route("forward_fused", r16, 4096, 4096, T=2048, with_v=with_v) == "forward_fused_decode"
+        assert cm.route("forward_fused", r16, 4096, 4096, T=2049, with_v=with_v) == \
+            ("forward" if with_v else "forward_fused")
+    # with v: the split kernels on decode batches of any rank and at r_max <= 16
+    assert cm.route("forward_fused", mixed, 4096, 4096, T=1024, with_v=True) == "forward"
+    assert cm.route("forward_fused", mixed, 4096, 4096, T=1024) == "forward_fused"
+    assert cm.route("forward_fused", mixed, 4096, 4096, T=1025, with_v=True) == "forward_fused"
+    assert cm.route("forward_fused", [16], 4096, 4096, T=4096, with_v=True) == "forward"
+    assert cm.route("forward_fused", [16], 4096, 4096, T=4096) == "forward_fused"
+    # other entry points: one model each
+    assert cm.route("forward", mixed, 4096, 4096, T=1) == "forward"
+    assert cm.route("segments", r16, 4096, 4096, T=1) == "segments"
+
+
+def test_predict_uses_the_routed_entry():
+    c = lambda k: [k * 1e-6] + [0.0] * 7
+    m = cm.CostModel({"forward": c(1), "forward_fused": c(2), "forward_fused_decode": c(3)})
+    ids = [0, 1, 1]
+    assert m.predict("forward_fused", ids, [16, 16], 64, 32) == pytest.approx(3e-6)
+    assert m.predict("forward_fused", ids, [64, 64], 64, 32) == pytest.approx(2e-6)
+    assert m.predict("forward_fused", ids, [64, 64], 64, 32, with_v=True) == pytest.approx(1e-6)
