@@ -630,11 +630,19 @@ class Bench:
         if mode != "auto":
             self.fused = mode == "fused"
             return {"mode": mode, "chosen": mode}
+        from expand_token_adapter_amd.cost_model import route
+        wl = self.wl
         t = self.call_times(["shrink", "expand", "forward_fused"], reps=20)
         split_us = t["shrink"] + t["expand"]
-        self.fused = t["forward_fused"] < split_us
-        return {"mode": "auto", "chosen": "fused" if self.fused else "split", "split_us_per_call": split_us,
-                "fused_us_per_call": t["forward_fused"]}
+        # lora_forward given v runs the split calls' kernels on decode batches and
+        # at r_max <= 16 (except the rank-16 decode kernel): then the two are one
+        same = route("forward_fused", wl.ranks, wl.d_in, wl.d_out, T=wl.T, with_v=True) == "forward"
+        self.fused = not same and t["forward_fused"] < split_us
+        out = {"mode": "auto", "chosen": "fused" if self.fused else "split", "split_us_per_call": split_us,
+               "fused_us_per_call": t["forward_fused"]}
+        if same:
+            out["lora_forward_runs_split_kernels"] = True
+        return out
 
     def check_errors(self):
         errs = [int(st["seg"].err.item()) + (int(st["seg_ft"].err.item()) if self.has_ft else 0) for st in self.sets]

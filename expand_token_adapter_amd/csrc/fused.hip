@@ -115,35 +115,50 @@ int fused_run(int dtype, const void* x, int64_t ldx, int32_t T, int32_t d_in, co
     if (n_slices > 1 && r_max > 64) return LORA_ERR_UNSUPPORTED;
     if (T == 0) return LORA_OK;
     if ((rc = check_matrix(x, d_in, ldx)) != LORA_OK) return rc;
-    FusedParams p{};
-    int64_t nch = 0;
     for (int32_t q = 0; q < n_slices; ++q) {
         const lora_slice& sl = slices[q];
         if ((rc = check_matrix(sl.y, sl.d_out, sl.ldy)) != LORA_OK) return rc;
         if (sl.v && (rc = check_f32_rows(sl.v, sl.ldv, r_max)) != LORA_OK) return rc;
-        p.sl[q] = FusedSlice{sl.adapters, sl.y, sl.ldy, sl.v, sl.ldv, sl.d_out, (int32_t)nch};
-        nch += (sl.d_out + 63) / 64;
     }
-    if (nch > 0x7fffffff) return LORA_ERR_UNSUPPORTED;
     hipStream_t st = static_cast<hipStream_t>(stream);
     bool dec = fused_decode_fits(dtype, T, num_adapters, r_max) && dec_offsets_fit((int64_t)T * ldx * 2, d_in, r_max);
     for (int32_t q = 0; q < n_slices; ++q)
         dec = dec && dec_offsets_fit((int64_t)T * slices[q].ldy * 2, slices[q].d_out, r_max);
     if (dec) return fused_decode_run(x, ldx, T, d_in, slices, n_slices, num_adapters, r_max, seg, st);
-    // One slice with v given: where the split kernels need no workspace -- the
+    // Slices with v given: where the split kernels need no workspace -- the
     // 16-row-tile shrink on decode batches or at r_max <= 16, then the expand
     // -- they are faster than the 64-row-tile kernel, which walks all of d_in
-    // per tile; the call runs them (v passes through HBM, results as
-    // lora_shrink + lora_expand_add bit for bit).
-    if (n_slices == 1 && slices[0].v && (use_decode_path(dtype, T, num_adapters) ||
-                                         (dtype == LORA_BF16 && r_max <= 16)) &&
+    // per tile; such a slice runs them (v passes through HBM, results as
+    // lora_shrink + lora_expand_add bit for bit), the others the one-launch
+    // kernel below.
+    lora_slice rest[LORA_MAX_SLICES];
+    if ((use_decode_path(dtype, T, num_adapters) || (dtype == LORA_BF16 && r_max <= 16)) &&
         dec_offsets_fit((int64_t)T * ldx * 2, d_in, r_max)) {
-        const lora_slice& sl = slices[0];
-        rc = run_dec_shrink(dtype, x, ldx, T, d_in, sl.adapters, num_adapters, r_max, seg, sl.v, sl.ldv, 0, st);
-        if (rc != LORA_OK) return rc;
-        return lora_expand_add(dtype, sl.v, sl.ldv, T, sl.d_out, sl.adapters, num_adapters, r_max, seg, sl.y,
-                               sl.ldy, stream);
+        int32_t n_rest = 0;
+        for (int32_t q = 0; q < n_slices; ++q) {
+            const lora_slice& sl = slices[q];
+            if (!sl.v) {
+                rest[n_rest++] = sl;
+                continue;
+            }
+            rc = run_dec_shrink(dtype, x, ldx, T, d_in, sl.adapters, num_adapters, r_max, seg, sl.v, sl.ldv, 0, st);
+            if (rc != LORA_OK) return rc;
+            rc = lora_expand_add(dtype, sl.v, sl.ldv, T, sl.d_out, sl.adapters, num_adapters, r_max, seg, sl.y,
+                                 sl.ldy, stream);
+            if (rc != LORA_OK) return rc;
+        }
+        if (n_rest == 0) return LORA_OK;
+        slices = rest;
+        n_slices = n_rest;
     }
+    FusedParams p{};
+    int64_t nch = 0;
+    for (int32_t q = 0; q < n_slices; ++q) {
+        const lora_slice& sl = slices[q];
+        p.sl[q] = FusedSlice{sl.adapters, sl.y, sl.ldy, sl.v, sl.ldv, sl.d_out, (int32_t)nch};
+        nch += (sl.d_out + 63) / 64;
+    }
+    if (nch > 0x7fffffff) return LORA_ERR_UNSUPPORTED;
     p.x = x;
     p.ldx = ldx;
     p.K = d_in;

@@ -275,14 +275,19 @@ int lora_forward(int dtype, const void* x, int64_t ldx, int32_t T, int32_t d_in,
 
 /*
  * Multi-slice fused forward: several projections that read the same x, each
- * with its own adapters, in one launch.  DeltaServe (section 4.1) adapts all
- * attention projections of a layer; the q, k and v projections (or the gate
- * and up projections of an MLP) read one input, so x is read once per tile for
- * all of them and v = A x of every slice stays in LDS.  For each slice q and
- * each row t with adapter a = a(t) (the same adapter index in every slice):
+ * with its own adapters.  DeltaServe (section 4.1) adapts all attention
+ * projections of a layer; the q, k and v projections (or the gate and up
+ * projections of an MLP) read one input, so the one-launch kernels read x
+ * once per tile for all of them and keep v = A x of every slice in LDS.  For
+ * each slice q and each row t with adapter a = a(t) (the same adapter index
+ * in every slice):
  *     y_q[t] += s_{q,a} B_{q,a} (A_{q,a} x_t),
- * exactly what lora_forward computes for that slice alone without v (bit
- * for bit: the same one-launch kernel family and sum order).
+ * exactly what lora_forward computes for that slice alone with the same
+ * arguments (bit for bit).  The slices take lora_forward's routes: on a
+ * decode batch with r_max <= 16 all of them run in one 16-row-tile launch;
+ * otherwise each slice given v runs the split kernels where lora_forward
+ * would (decode batch or r_max <= 16), and the remaining slices run in one
+ * 64-row-tile launch.
  *   slices: HOST array of n_slices (1..LORA_MAX_SLICES) entries:
  *     adapters  device table [num_adapters] of the slice (A [r, d_in],
  *               B [d_out, r]; ranks may differ between slices);
@@ -291,8 +296,8 @@ int lora_forward(int dtype, const void* x, int64_t ldx, int32_t T, int32_t d_in,
  *   r_max: the largest rank over every slice's adapters.
  * Errors as for lora_forward; LORA_ERR_UNSUPPORTED for n_slices > 1 with
  * r_max > 64 (the slices' v rows and fragments would not fit the LDS).
- * Bad table entries are counted in seg.err once per slice and tile (16-row
- * tiles on lora_forward's decode route, 64-row tiles otherwise), and only
+ * Bad table entries are counted in seg.err as lora_forward counts them for
+ * each slice (once per slice, tile and kernel that meets them), and only
  * that slice's rows are skipped.
  */
 #define LORA_MAX_SLICES 3

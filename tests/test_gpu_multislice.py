@@ -3,9 +3,10 @@
 Several projections read one x, each with its own adapter table (same ids).
 Every slice's y must match the fp64 oracle of that slice alone (the bf16 /
 fp32 bars of the forward), and equal bit for bit what lora_forward computes
-for the slice alone without a v output (always a one-launch kernel): the
-per-slice arithmetic and its order do not change.  Each slice's v matches
-the oracle.
+for the slice alone with the same arguments (v given or not): the per-slice
+routes, arithmetic and sum order do not change.  Each slice's v matches the
+oracle.  Slices given v on a decode batch with r_max > 16 run the split
+kernels while the others share one launch; that mix is a case of its own.
 """
 import numpy as np
 import pytest
@@ -30,6 +31,9 @@ def _slices(ids, d_in, d_outs, rank_sets, dtype, seed):
 
 
 def _run(wls, dtype, with_v, multi=True, bad=None):
+    """with_v: one bool for every slice, or one per slice."""
+    if isinstance(with_v, bool):
+        with_v = [with_v] * len(wls)
     x = to_dev(wls[0].x, dtype, DEV)
     ids = torch.from_numpy(np.ascontiguousarray(wls[0].ids)).to(DEV)
     n_ad = wls[0].num_adapters
@@ -46,16 +50,14 @@ def _run(wls, dtype, with_v, multi=True, bad=None):
         tables.append(t)
         ys.append(to_dev(wl.y0, dtype, DEV))
         rm = max(int(r) for w in wls for r in w.ranks)
-        vs.append(torch.zeros((wl.T, (rm + 7) // 8 * 8), dtype=torch.float32, device=DEV) if with_v else None)
+        vs.append(torch.zeros((wl.T, (rm + 7) // 8 * 8), dtype=torch.float32, device=DEV) if with_v[q] else None)
     seg = lb.lora_segments_build(ids, n_ad)
     r_max = max(t.r_max for t in tables)
     if multi:
         lb.lora_forward_multi(x, [(tables[q], ys[q], vs[q]) for q in range(len(wls))], seg, r_max=r_max)
     else:
-        # without v: lora_forward's one-launch kernels (with v it may run the
-        # split kernels instead)
         for q in range(len(wls)):
-            lb.lora_forward(x, tables[q], seg, ys[q], r_max=r_max)
+            lb.lora_forward(x, tables[q], seg, ys[q], v=vs[q], r_max=r_max)
     torch.cuda.synchronize()
     return ys, vs, seg
 
@@ -101,9 +103,40 @@ def test_multi_slice_matches_oracle_and_single_slices(case, dtype):
             r = int(wl.ranks[ids[t]])
             np.testing.assert_allclose(vs[q][t, :r].double().cpu().numpy(), v_ref[t, :r], rtol=1e-4,
                                        atol=1e-4 * max(np.max(np.abs(v_ref)), 1e-30))
-    ys1, _, _ = _run(wls, dtype, with_v=False, multi=False)
+    ys1, vs1, _ = _run(wls, dtype, with_v=True, multi=False)
     for q in range(len(wls)):
         assert torch.equal(ys[q], ys1[q]), (case, q)
+        assert torch.equal(vs[q], vs1[q]), (case, q)
+    ys0, _, _ = _run(wls, dtype, with_v=False)
+    ys01, _, _ = _run(wls, dtype, with_v=False, multi=False)
+    for q in range(len(wls)):
+        assert torch.equal(ys0[q], ys01[q]), (case, q)
+
+
+@pytest.mark.parametrize("case,with_v", [("gate_up", [True, False]), ("gate_up", [False, True]),
+                                         ("qkv_decode_ragged", [True, False, True]),
+                                         ("qkv_mixed_ranks", [False, True, False])])
+def test_multi_slice_some_slices_with_v(case, with_v):
+    """gate_up is a decode batch (150 rows, 5 adapters) with ranks to 64: the
+    slices given v run the split kernels, the others one 64-row-tile launch;
+    qkv_decode_ragged (ranks <= 16) runs every slice in the 16-row-tile launch
+    and qkv_mixed_ranks (long row groups, ranks to 32) in the 64-row-tile one.
+    Each slice equals lora_forward of that slice alone with the same
+    arguments, bit for bit, and the oracle."""
+    T, A, d_in, d_outs, rank_sets, kind = CASES[case]
+    ids = _ids(kind, T, A, np.random.default_rng(6))
+    wls = _slices(ids, d_in, d_outs, rank_sets, "bf16", seed=11)
+    ys, vs, seg = _run(wls, "bf16", with_v=with_v)
+    ys1, vs1, _ = _run(wls, "bf16", with_v=with_v, multi=False)
+    assert seg.err.item() == 0
+    x0 = oracle.to_f64(wls[0].x, "bf16")
+    for q, wl in enumerate(wls):
+        assert torch.equal(ys[q], ys1[q]), q
+        if with_v[q]:
+            assert torch.equal(vs[q], vs1[q]), q
+        ref = oracle.from_workload(wl)
+        y_ref, _ = oracle.forward(x0, ref["ids"], ref["ranks"], ref["scales"], ref["A"], ref["B"], ref["y0"])
+        assert rel_err(ys[q], y_ref) <= TOL["bf16"], q
 
 
 def test_multi_slice_bad_entry_skips_only_its_slice():
