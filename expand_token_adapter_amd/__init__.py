@@ -323,7 +323,12 @@ def lora_expand_add(v: torch.Tensor, adapters: AdapterTable, seg: Segments, y: t
 
 def lora_forward(x: torch.Tensor, adapters: AdapterTable, seg: Segments, y: torch.Tensor,
                  v: Optional[torch.Tensor] = None, r_max: Optional[int] = None) -> torch.Tensor:
-    """y[t] += s_a B_a A_a x[t] in one launch (for decode-like batches); v, if given, receives A_a x[t]."""
+    """y[t] += s_a B_a A_a x[t] without a workspace; v, if given, receives A_a x[t].
+
+    The library picks the kernels: one launch on rank-16 decode batches; with v
+    given on other decode batches or at r_max <= 16, the split calls' kernels
+    (bit-equal to lora_shrink + lora_expand_add); otherwise one 64-row-tile launch.
+    """
     _on_gpu(x, y, v)
     px, T, d_in, ldx = _rows(x, "x")
     py, Ty, d_out, ldy = _rows(y, "y")
@@ -345,9 +350,11 @@ def lora_forward(x: torch.Tensor, adapters: AdapterTable, seg: Segments, y: torc
 
 
 def lora_forward_multi(x: torch.Tensor, slices, seg: Segments, r_max: Optional[int] = None) -> None:
-    """Several projections of the same x in one launch: slices = [(adapters, y[, v]), ...] (1..3 entries).
+    """Several projections of the same x: slices = [(adapters, y[, v]), ...] (1..3 entries).
 
-    For every slice, y[t] += s_a B_a A_a x[t] with that slice's adapter table (same adapter ids).
+    For every slice, y[t] += s_a B_a A_a x[t] with that slice's adapter table (same adapter ids),
+    bit-equal to lora_forward of that slice alone with the same arguments; the slices that
+    lora_forward would run in one launch share one launch (x read once per tile).
     """
     entries = [tuple(e) + (None,) * (3 - len(e)) for e in slices]
     if not 1 <= len(entries) <= _abi.LORA_MAX_SLICES:
