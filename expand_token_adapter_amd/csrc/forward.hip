@@ -58,11 +58,14 @@ int launch_expand_t(int ks, const ExpandParams& p, unsigned grid, hipStream_t st
 constexpr int64_t kDecShrinkMaxGrid = 1 << 16;
 
 // Balanced mode: at least this many tasks (bound from the row and adapter
-// counts), on a grid of four 4-wave workgroups per CU.  (At most three per CU
-// were found resident at once; a grid of three per CU, or a smaller LDS
-// footprint, measured no faster on the zipf-320 decode batch.)
+// counts), on a grid of two 4-wave workgroups per CU, all resident at once.
+// Measured on the zipf-320 decode batch (2048 rows, 8192 -> 8192): two per CU
+// 65.8 us; four per CU (at most three resident, the rest started late) 71.8;
+// three 72.9; one 73.7; 1.5 or 2.5 per CU (CUs unevenly loaded) 83.8 / 73.7.
+// With more workgroups in flight the memory system serves the same 1 KB row
+// pieces more slowly; with fewer, too few loads are in flight.
 constexpr int64_t kDecShrinkPlanTasks = 2048;
-constexpr unsigned kDecShrinkPlanGrid = 256 * 4;
+constexpr unsigned kDecShrinkPlanGrid = 256 * 2;
 static_assert(kDecShrinkPlanGrid % kNumXcd == 0, "balanced ranges are numbered XCD by XCD");
 
 template <int DT>
