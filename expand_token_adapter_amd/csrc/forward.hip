@@ -18,7 +18,10 @@ using namespace lora;
 namespace {
 
 constexpr int64_t kMaxGrid = 8192;
-constexpr int64_t kShrinkMaxGrid = 1024;
+// Split-K shrink: at most two workgroups per CU, the number the 64-rank
+// variant's LDS keeps resident (mixed batch: 28.6 us at 512 workgroups, 29.8
+// at 1024, 30.4 at 768, 31.8 at 2048).
+constexpr int64_t kShrinkMaxGrid = 512;
 
 template <int DT, int RB>
 void launch_shrink_rb(bool trans_w, const ShrinkParams& p, unsigned grid, hipStream_t st) {
@@ -258,7 +261,7 @@ int launch_shrink_reduce(int32_t r_max, const ReduceParams& rp, int32_t T, int32
 // split-K shrink into partials, then their fixed-order sum.
 int run_shrink(int dtype, bool trans_w, const ShrinkParams& p, const ReduceParams& rp, int32_t T, int32_t num_adapters,
                hipStream_t st) {
-    // at most four workgroups per CU: the later tasks of a workgroup overlap
+    // at most two workgroups per CU: the later tasks of a workgroup overlap
     // their metadata loads with the current task's data
     const int64_t tasks = SchedLayout::max_tiles64(T, num_adapters) * p.rgroups * p.nslices;
     const unsigned grid = grid_for(tasks, 1, kShrinkMaxGrid);
