@@ -1,5 +1,5 @@
 """A captured HIP graph of one step (batched segment build, shrink, expand-add,
-one-launch forward, backward with saved v) replays to the eager results, bit for bit, on every
+lora_forward without and with v, backward with saved v) replays to the eager results, bit for bit, on every
 replay, with eager work and synchronisations between the replays.  The kernels
 clear their own scratch (no memset nodes are recorded) and every reduction runs
 in a fixed order, so a replay must reproduce the eager step exactly."""
@@ -33,9 +33,18 @@ def _decode16():
                             ft_count=40, name="graph-decode16")
 
 
-@pytest.mark.parametrize("kind", ["mixed", "decode16"])
+def _decode64():
+    # at most 32 rows per adapter, ranks to 64: lora_forward without v runs the
+    # 64-row-tile kernel, with v the 16-row-tile shrink and expand
+    rng = np.random.default_rng(29)
+    ids = np.concatenate([rng.integers(-1, 12, size=180), np.full(48, 5)]).astype(np.int32)
+    return workloads.custom(ids, [16, 64, 8, 40, 24, 33] * 2, 264, 328, "bf16", seed=7, ft_start=len(ids) - 48,
+                            ft_count=48, name="graph-decode64")
+
+
+@pytest.mark.parametrize("kind", ["mixed", "decode16", "decode64"])
 def test_graph_replays_match_eager_step(kind):
-    wl = _mixed() if kind == "mixed" else _decode16()
+    wl = {"mixed": _mixed, "decode16": _decode16, "decode64": _decode64}[kind]()
     dev = torch.device("cuda:0")
     s, n = wl.ft_start, wl.ft_count
     A = [to_dev(a, "bf16", dev) for a in wl.A]
@@ -47,8 +56,10 @@ def test_graph_replays_match_eager_step(kind):
     ids = torch.from_numpy(wl.ids).to(dev)
     ft_ids = ids[s:s + n].contiguous()
     y = y0.clone()
-    yf = y0.clone()  # the one-launch forward's output
+    yf = y0.clone()  # lora_forward's output (without v)
+    yfv = y0.clone()  # lora_forward's output with v
     v = torch.zeros((wl.T, (table.r_max + 7) // 8 * 8), dtype=torch.float32, device=dev)
+    vf = torch.zeros_like(v)
     dx = torch.zeros((n, wl.d_in), dtype=torch.bfloat16, device=dev)
     dA = [torch.zeros(a.shape, dtype=torch.float32, device=dev) for a in A]
     dB = [torch.zeros(b.shape, dtype=torch.float32, device=dev) for b in B]
@@ -64,8 +75,10 @@ def test_graph_replays_match_eager_step(kind):
         # stale values everywhere: columns past round_up(r_a, 8) and rows
         # without an adapter are left unchanged by design, the rest rewritten
         v.fill_(-1.0)
+        vf.fill_(-1.0)
         y.copy_(y0)
         yf.copy_(y0)
+        yfv.copy_(y0)
         dx.zero_()
         for t in dA + dB:
             t.zero_()
@@ -75,12 +88,13 @@ def test_graph_replays_match_eager_step(kind):
         lb.lora_shrink(x, table, seg, v=v, ws=ws)
         lb.lora_expand_add(v, table, seg, y)
         lb.lora_forward(x, table, seg, yf)
+        lb.lora_forward(x, table, seg, yfv, v=vf)
         lb.lora_backward(x[s:s + n], dy, table, grads, seg_ft, dx=dx, v_saved=v[s:s + n], ws=bws)
 
     reset()
     step()
     torch.cuda.synchronize()
-    want = [t.clone() for t in [y, yf, v, dx] + dA + dB]
+    want = [t.clone() for t in [y, yf, yfv, v, vf, dx] + dA + dB]
     assert seg.err.item() == 0 and seg_ft.err.item() == 0
 
     side = torch.cuda.Stream(device=dev)
@@ -99,7 +113,7 @@ def test_graph_replays_match_eager_step(kind):
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        got = [y, yf, v, dx] + dA + dB
+        got = [y, yf, yfv, v, vf, dx] + dA + dB
         for i, (a, b) in enumerate(zip(got, want)):
             assert torch.equal(a, b), (k, i)
         assert seg.err.item() == 0 and seg_ft.err.item() == 0
