@@ -248,7 +248,7 @@ int lora_expand_add(int dtype, const float* v, int64_t ldv, int32_t T, int32_t d
  *   - decode batch, r_max <= 16: one launch, 16-row tiles, one workgroup per
  *     (tile, column range) with every load of the tile in flight at once, v
  *     kept in LDS (256 decode rows over 64 rank-16 adapters, 4096 -> 4096:
- *     12.7 us against 18.4 us for lora_shrink + lora_expand_add);
+ *     12.9 us against 18.3 us for lora_shrink + lora_expand_add);
  *   - otherwise, with v given, on a decode batch or at r_max <= 16 (bf16):
  *     the split calls' kernels that need no workspace, the 16-row-tile shrink
  *     into v, then the expand; results equal lora_shrink + lora_expand_add
