@@ -295,12 +295,15 @@ int backward_impl(int dtype, const void* x, int64_t ldx, const void* dy, int64_t
     cp.fix_meta = reinterpret_cast<int32_t*>(wsf + w.fix_meta);
     cp.stop = stop;
     // kContractGrid workgroups (a multiple of the 8 XCDs) split the work evenly
-    if (dtype == LORA_BF16)
-        hipLaunchKernelGGL(contract_kernel<LORA_BF16>, dim3(kContractGrid), dim3(contract_waves<LORA_BF16>() * kWave),
-                           0, st, cp);
+    if (dtype == LORA_BF16 && !one_pass)
+        hipLaunchKernelGGL((contract_kernel<LORA_BF16, true>), dim3(kContractGrid),
+                           dim3(contract_waves<LORA_BF16>() * kWave), 0, st, cp);
+    else if (dtype == LORA_BF16)
+        hipLaunchKernelGGL((contract_kernel<LORA_BF16, false>), dim3(kContractGrid),
+                           dim3(contract_waves<LORA_BF16>() * kWave), 0, st, cp);
     else
-        hipLaunchKernelGGL(contract_kernel<LORA_F32>, dim3(kContractGrid), dim3(contract_waves<LORA_F32>() * kWave), 0,
-                           st, cp);
+        hipLaunchKernelGGL((contract_kernel<LORA_F32, false>), dim3(kContractGrid),
+                           dim3(contract_waves<LORA_F32>() * kWave), 0, st, cp);
     if (hipGetLastError() != hipSuccess) return LORA_ERR_HIP;
 
     // dX += s A^T g and the fix-ups, in one launch.

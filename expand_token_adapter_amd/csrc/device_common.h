@@ -366,6 +366,11 @@ constexpr uint32_t kBufOff = 0x80000000u;
 __device__ __forceinline__ u32x4_t buf_load16(buf_rsrc_t r, uint32_t voff, uint32_t soff) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
 }
+// The same with the nontemporal hint, for data read once (a stream that
+// should not push out of L2 the lines other workgroups still re-read).
+__device__ __forceinline__ u32x4_t buf_load16_nt(buf_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 2);
+}
 
 // s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding:
 // vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
