@@ -22,12 +22,14 @@ as the backward's token contraction reads them), with non-negative coefficients 
 relative residuals, so that a 10 us and a 1 ms call weigh alike.
 
 Each entry point has one model per kernel route the library takes: the
-backward's streaming route is ``backward_stream``; ``forward_fused`` is
+backward's streaming route is ``backward_stream``; the split forward on
+decode batches (at most 32 rows per adapter: the 16-row-tile shrink and
+expand) is ``forward_decode``; ``forward_fused`` is
 ``lora_forward`` without v, whose one-launch kernels are the 16-row-tile
-decode kernel (``forward_fused_decode``: bf16 decode batches, at most 32 rows
-per adapter, with r_max <= 16) or the 64-row-tile kernel
-(``forward_fused``); with v, ``lora_forward`` runs the split kernels of
-``forward`` on decode batches and at r_max <= 16 (``route``).
+decode kernel (``forward_fused_decode``: bf16 decode batches with r_max <=
+16) or the 64-row-tile kernel (``forward_fused``); with v, ``lora_forward``
+runs the split kernels on decode batches and at r_max <= 16, priced as the
+split forward of the same batch (``route``).
 
 ``features`` and ``fit`` / ``predict`` run on the host; ``calibrate`` times the
 library's calls on synthetic batches on the GPU (random ids, ranks and
@@ -51,6 +53,7 @@ OPS = ("segments", "forward", "forward_fused", "backward")
 _OP_FEATURES = {
     "segments": ("const", "rows", "adapters", "tiles16"),
     "forward": ("const", "row_elems", "weight_elems", "rank_rows", "adapters", "tiles16"),
+    "forward_decode": ("const", "row_elems", "weight_elems", "rank_rows", "adapters", "tiles16"),
     "forward_fused": ("const", "row_elems", "weight_elems", "rank_rows", "adapters", "tiles16"),
     "forward_fused_decode": ("const", "row_elems", "weight_elems", "tiles16"),
     "backward": ("const", "row_elems", "weight_elems", "rank_rows", "adapters", "tiles16", "group_elems"),
@@ -67,21 +70,25 @@ def route(op: str, ranks: Sequence[int], d_in: int, d_out: int, r_max: int = 0, 
     defaults to max(ranks); T is the call's row count (-1: not a decode batch).
     - backward: 'backward_stream' (one pass over dY) when r_max <= 16 and
       d_out >= 2 d_in, else 'backward';
+    - forward (lora_shrink + lora_expand_add): 'forward_decode' on decode
+      batches (T <= 32 x len(ranks): the 16-row-tile kernels), else 'forward';
     - forward_fused (lora_forward): 'forward_fused_decode' on decode batches
-      (T <= 32 x len(ranks)) with r_max <= 16; else, with v given, 'forward'
-      (the split kernels) on decode batches or at r_max <= 16; else
+      with r_max <= 16; else, with v given, the split kernels on decode
+      batches or at r_max <= 16 (priced as the split forward); else
       'forward_fused' (the 64-row-tile kernel);
     - the others: one model each."""
     r = r_max or (max(ranks) if len(ranks) else 0)
+    decode = 0 <= T <= DECODE_ROWS_PER_ADAPTER * len(ranks)
     if op == "backward":
         if r <= 16 and d_out >= 2 * d_in:
             return "backward_stream"
     if op == "forward_fused":
-        decode = 0 <= T <= DECODE_ROWS_PER_ADAPTER * len(ranks)
         if decode and r <= 16:
             return "forward_fused_decode"
         if with_v and (decode or r <= 16):
-            return "forward"
+            op = "forward"
+    if op == "forward" and decode:
+        return "forward_decode"
     return op
 
 

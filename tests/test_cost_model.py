@@ -83,20 +83,25 @@ def test_route_follows_the_library_routes():
         assert cm.route("forward_fused", r16, 4096, 4096, T=2049, with_v=with_v) == \
             ("forward" if with_v else "forward_fused")
     # with v: the split kernels on decode batches of any rank and at r_max <= 16
-    assert cm.route("forward_fused", mixed, 4096, 4096, T=1024, with_v=True) == "forward"
+    assert cm.route("forward_fused", mixed, 4096, 4096, T=1024, with_v=True) == "forward_decode"
     assert cm.route("forward_fused", mixed, 4096, 4096, T=1024) == "forward_fused"
     assert cm.route("forward_fused", mixed, 4096, 4096, T=1025, with_v=True) == "forward_fused"
     assert cm.route("forward_fused", [16], 4096, 4096, T=4096, with_v=True) == "forward"
     assert cm.route("forward_fused", [16], 4096, 4096, T=4096) == "forward_fused"
-    # other entry points: one model each
-    assert cm.route("forward", mixed, 4096, 4096, T=1) == "forward"
+    # the split forward: its decode route (16-row tiles) has its own entry
+    assert cm.route("forward", mixed, 4096, 4096, T=1) == "forward_decode"
+    assert cm.route("forward", mixed, 4096, 4096, T=1024) == "forward_decode"
+    assert cm.route("forward", mixed, 4096, 4096, T=1025) == "forward"
+    assert cm.route("forward", mixed, 4096, 4096) == "forward"  # T unknown: not a decode batch
     assert cm.route("segments", r16, 4096, 4096, T=1) == "segments"
 
 
 def test_predict_uses_the_routed_entry():
     c = lambda k: [k * 1e-6] + [0.0] * 7
-    m = cm.CostModel({"forward": c(1), "forward_fused": c(2), "forward_fused_decode": c(3)})
+    m = cm.CostModel({"forward": c(1), "forward_fused": c(2), "forward_fused_decode": c(3), "forward_decode": c(4)})
     ids = [0, 1, 1]
     assert m.predict("forward_fused", ids, [16, 16], 64, 32) == pytest.approx(3e-6)
     assert m.predict("forward_fused", ids, [64, 64], 64, 32) == pytest.approx(2e-6)
-    assert m.predict("forward_fused", ids, [64, 64], 64, 32, with_v=True) == pytest.approx(1e-6)
+    assert m.predict("forward_fused", ids, [64, 64], 64, 32, with_v=True) == pytest.approx(4e-6)
+    assert m.predict("forward", ids, [64, 64], 64, 32) == pytest.approx(4e-6)
+    assert m.predict("forward", list(range(2)) * 40, [64, 64], 64, 32) == pytest.approx(1e-6)

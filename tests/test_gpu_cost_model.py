@@ -8,8 +8,8 @@ not monotone in the row count on these shapes (e.g. 16 adapters of ranks
 no model over these features follows more closely.
 
 The shapes cover the routes of each entry point: decode-sized batches
-(at most 32 rows per adapter) take the 16-row-tile forward, larger ones the
-64-row one; rank-16 tables with d_out >= 2 d_in take the streaming backward
+(at most 32 rows per adapter) take the 16-row-tile split forward (its own
+model entry, 'forward_decode'), larger ones the 64-row one ('forward'); rank-16 tables with d_out >= 2 d_in take the streaming backward
 (its own model entry, 'backward_stream'), the others the two-pass one;
 lora_forward without v runs the 16-row-tile decode kernel on rank-16 decode
 batches ('forward_fused_decode') and the 64-row-tile kernel elsewhere
@@ -30,7 +30,7 @@ TRAIN = [(T, d_in, d_out, ranks, dist) for d_in, d_out in ((2048, 2048), (1024, 
          for T in (128, 1024, 4096) for ranks, dist in _FAMILIES]
 HELD = [(T, d_in, d_out, ranks, dist) for d_in, d_out in ((2048, 4096), (4096, 8192))
         for T in (512, 2048) for ranks, dist in _FAMILIES]
-BOUND = {"forward": 0.15, "backward_stream": 0.15, "backward": 0.20}
+BOUND = {"forward": 0.15, "forward_decode": 0.20, "backward_stream": 0.15, "backward": 0.20}
 
 
 def _key(s):
@@ -46,13 +46,13 @@ def test_calibrate_fit_and_held_out_accuracy():
     train = [s for s in samples if _key(s) not in held_keys]
     held = [s for s in samples if _key(s) in held_keys]
     model = cm.fit_samples(train)
-    assert set(model.coef) >= {"segments", "forward", "forward_fused", "forward_fused_decode", "backward",
-                               "backward_stream"}
+    assert set(model.coef) >= {"segments", "forward", "forward_decode", "forward_fused", "forward_fused_decode",
+                               "backward", "backward_stream"}
     for op in model.coef:
         assert np.all(model.coef[op] >= 0)
     errs = cm.relative_errors(model, held)
     med = {op: float(np.median(np.abs(e))) for op, e in errs.items()}
     print({op: (round(med[op], 3), round(float(np.max(np.abs(errs[op]))), 3)) for op in errs}, flush=True)
-    assert set(errs) >= {"forward", "backward", "backward_stream"}
+    assert set(errs) >= {"forward", "forward_decode", "backward", "backward_stream"}
     for op, bound in BOUND.items():
         assert med[op] <= bound, (op, med[op], errs[op].round(3).tolist())
