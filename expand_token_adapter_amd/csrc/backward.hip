@@ -11,11 +11,19 @@
 // (rank-major), the shrinks' split-K partials and the contraction's partial
 // tiles of tiles cut between workgroups.
 //
+// Launches: the g shrink and its reduce (which also lays out a saved v
+// rank-major), then one launch in which the contraction and the dX expand
+// run side by side on their own workgroups (both read only g, v and the
+// inputs), then the contraction's fix-up of its cut tiles.  Run one after the
+// other, the two middle kernels each paid their own ramp-up and tail: 4096
+// fine-tuning rows, rank 16, 5120 -> 5120: backward 59.4 against 64.4 us;
+// the mixed batch's 2048 rows, 4096 -> 14336: 49.8 against 51.8 us.
+//
 // For bf16 calls with r_max <= 16 and dY the wider stream (d_out >= 2 d_in)
 // the two products that read dY run in one pass over it (dy_pass_kernel: g
 // partials and dB); g's partials are summed by the shrink's reduce kernel,
 // the contraction computes dA only, and the dB tiles cut between workgroups
-// are added in the launch of the dX expand.
+// are added in the x-side launch.
 #include <algorithm>
 
 #include "host_checks.h"
@@ -34,6 +42,13 @@ int64_t shrink_part_floats(int dtype, int32_t T, int32_t K, int32_t r_max);
 int expand_plan(const ExpandParams& p, int32_t T, int32_t num_adapters, int32_t r_max, ExpandParams* q,
                 unsigned* grid);
 int launch_shrink_reduce(int32_t r_max, const ReduceParams& rp, int32_t T, int32_t num_adapters, hipStream_t st);
+
+// Contraction workgroups (4 waves each) of the x-side launch: one per CU.
+#ifndef LORA_XSIDE_CTR
+#define LORA_XSIDE_CTR 256
+#endif
+constexpr int kXsideCtrGrid = LORA_XSIDE_CTR;
+static_assert(kXsideCtrGrid % kNumXcd == 0, "whole rounds of the 8 XCDs");
 
 // Workspace layout of lora_backward (fp32 elements): g by sorted position
 // (row-major and rank-major), v rank-major (two-pass path) or by sorted
@@ -57,8 +72,8 @@ struct BwdWs {
                               shrink_part_floats(dtype, (int32_t)T, (int32_t)d_out, (int32_t)r_max));
         np = std::max(np, (int64_t)dy_slices(d_out) * (T > 0 ? T : 1) * 16);
         w.fix = round_up(w.part + np, 64);
-        w.fix_meta = w.fix + (int64_t)kContractGrid * 2 * kFixFloats;
-        w.dyfix = round_up(w.fix_meta + (int64_t)kContractGrid * 2 * kFixMeta, 64);
+        w.fix_meta = w.fix + (int64_t)kXsideCtrGrid * 2 * kFixFloats;
+        w.dyfix = round_up(w.fix_meta + (int64_t)kXsideCtrGrid * 2 * kFixMeta, 64);
         w.dymeta = w.dyfix + (int64_t)kStGrid * 2 * kDyFixFloats;
         w.total = round_up(w.dymeta + (int64_t)kStGrid * 2 * kStFixMeta, 64);
         return w;
@@ -67,34 +82,39 @@ struct BwdWs {
 }  // namespace lora
 
 namespace {
-// dX += s A^T g on the first n_expand workgroups, the contraction's fix-up of
-// cut tiles on the kContractGrid after them and (streaming path) the fix-up
-// of the dB tiles cut by dy_pass_kernel on n_dy more: one launch for
-// independent steps (the fix-ups' few, latency-bound workgroups run beside
-// the expand's).
-template <int DT, int KS>
-__global__ __launch_bounds__(kExpandWaves * kWave) __attribute__((amdgpu_waves_per_eu(KS == 4 ? 2 : 3)))
-void dx_fixup_kernel(ExpandParams ep, ContractParams cp, DyParams dp, int n_expand) {
-    static_assert(kExpandWaves == 4, "the fix-ups run on 4-wave workgroups");
+// The x side of the backward in one launch: the contraction (dA; on the
+// two-pass route dA and dB) on the first n_ctr workgroups, dX += s A^T g on
+// the next n_expand and (streaming route) the fix-up of the dB tiles cut by
+// dy_pass_kernel on the rest.  Each reads only what earlier launches wrote
+// (g, v, the dY pass's partial tiles), so the three run side by side instead
+// of one after the other; the contraction's own cut tiles are added by
+// contract_fixup_kernel in the next launch.  The contraction and the expand
+// use one LDS buffer (a workgroup runs one of them).
+// (fp32: one workgroup per CU by its LDS, so no register limit for more)
+template <int DT, int KS, bool NT>
+__global__ __launch_bounds__(4 * kWave) __attribute__((amdgpu_waves_per_eu(DT == LORA_F32 ? 1 : (KS == 4 ? 2 : 3))))
+void xside_kernel(ContractParams cp, int n_ctr, ExpandParams ep, int n_expand, DyParams dp) {
+    constexpr int kC = ContractLds<DT, 4>::kBytes, kE = ExpandLds<KS>::kBytes;
+    __shared__ __attribute__((aligned(16))) char s_lds[kC > kE ? kC : kE];
     const int b = (int)blockIdx.x;
-    if (b < n_expand)
-        expand_body<DT, true, KS>(ep, b, n_expand);
-    else if (b < n_expand + kContractGrid)
-        contract_fixup_body(cp, kContractGrid, b - n_expand);
+    if (b < n_ctr)
+        contract_body<DT, NT, 4>(cp, b, n_ctr, s_lds);
+    else if (b < n_ctr + n_expand)
+        expand_body<DT, true, KS>(ep, b - n_ctr, n_expand, s_lds);
     else
-        dy_fixup_body(dp, b - n_expand - kContractGrid);
+        dy_fixup_body(dp, b - n_ctr - n_expand);
 }
 
-template <int DT>
-void launch_dx_fixup(int ks, const ExpandParams& ep, const ContractParams& cp, const DyParams& dp, unsigned n_expand,
-                     unsigned n_dy, hipStream_t st) {
-    const dim3 grid(n_expand + kContractGrid + n_dy), block(kExpandWaves * kWave);
+template <int DT, bool NT>
+void launch_xside(int ks, const ContractParams& cp, const ExpandParams& ep, const DyParams& dp, unsigned n_expand,
+                  unsigned n_dy, hipStream_t st) {
+    const dim3 grid(kXsideCtrGrid + n_expand + n_dy), block(4 * kWave);
     if (ks == 1)
-        hipLaunchKernelGGL((dx_fixup_kernel<DT, 1>), grid, block, 0, st, ep, cp, dp, (int)n_expand);
+        hipLaunchKernelGGL((xside_kernel<DT, 1, NT>), grid, block, 0, st, cp, kXsideCtrGrid, ep, (int)n_expand, dp);
     else if (ks == 2)
-        hipLaunchKernelGGL((dx_fixup_kernel<DT, 2>), grid, block, 0, st, ep, cp, dp, (int)n_expand);
+        hipLaunchKernelGGL((xside_kernel<DT, 2, NT>), grid, block, 0, st, cp, kXsideCtrGrid, ep, (int)n_expand, dp);
     else
-        hipLaunchKernelGGL((dx_fixup_kernel<DT, 4>), grid, block, 0, st, ep, cp, dp, (int)n_expand);
+        hipLaunchKernelGGL((xside_kernel<DT, 4, NT>), grid, block, 0, st, cp, kXsideCtrGrid, ep, (int)n_expand, dp);
 }
 }  // namespace
 
@@ -294,19 +314,8 @@ int backward_impl(int dtype, const void* x, int64_t ldx, const void* dy, int64_t
     cp.fix = wsf + w.fix;
     cp.fix_meta = reinterpret_cast<int32_t*>(wsf + w.fix_meta);
     cp.stop = stop;
-    // kContractGrid workgroups (a multiple of the 8 XCDs) split the work evenly
-    if (dtype == LORA_BF16 && !one_pass)
-        hipLaunchKernelGGL((contract_kernel<LORA_BF16, true>), dim3(kContractGrid),
-                           dim3(contract_waves<LORA_BF16>() * kWave), 0, st, cp);
-    else if (dtype == LORA_BF16)
-        hipLaunchKernelGGL((contract_kernel<LORA_BF16, false>), dim3(kContractGrid),
-                           dim3(contract_waves<LORA_BF16>() * kWave), 0, st, cp);
-    else
-        hipLaunchKernelGGL((contract_kernel<LORA_F32, false>), dim3(kContractGrid),
-                           dim3(contract_waves<LORA_F32>() * kWave), 0, st, cp);
-    if (hipGetLastError() != hipSuccess) return LORA_ERR_HIP;
-
-    // dX += s A^T g and the fix-ups, in one launch.
+    // dX += s A^T g, the contraction and the dB fix-up in one launch, then the
+    // contraction's fix-up.
     const unsigned n_dy = one_pass ? kStGrid * kDyFixParts : 0;
     ExpandParams q{};
     unsigned n_expand = 0;
@@ -327,13 +336,14 @@ int backward_impl(int dtype, const void* x, int64_t ldx, const void* dy, int64_t
         ep.stop = stop;
         ks = expand_plan(ep, T_ft, num_adapters, r_max, &q, &n_expand);
     }
-    if (!dx && !one_pass) {
-        hipLaunchKernelGGL(contract_fixup_kernel, dim3(kContractGrid), dim3(4 * kWave), 0, st, cp, (int)kContractGrid);
-    } else if (dtype == LORA_BF16) {
-        launch_dx_fixup<LORA_BF16>(ks, q, cp, dp, n_expand, n_dy, st);
-    } else {
-        launch_dx_fixup<LORA_F32>(ks, q, cp, dp, n_expand, n_dy, st);
-    }
+    if (dtype == LORA_BF16 && !one_pass)
+        launch_xside<LORA_BF16, true>(ks, cp, q, dp, n_expand, n_dy, st);
+    else if (dtype == LORA_BF16)
+        launch_xside<LORA_BF16, false>(ks, cp, q, dp, n_expand, n_dy, st);
+    else
+        launch_xside<LORA_F32, false>(ks, cp, q, dp, n_expand, n_dy, st);
+    if (hipGetLastError() != hipSuccess) return LORA_ERR_HIP;
+    hipLaunchKernelGGL(contract_fixup_kernel, dim3(kXsideCtrGrid), dim3(4 * kWave), 0, st, cp, (int)kXsideCtrGrid);
     return hipGetLastError() == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 

@@ -575,10 +575,21 @@ __device__ __forceinline__ void st_fixup(const float* fix, const int32_t* fix_me
             uint64_t take = __ballot(match);
             if (stops) take &= (stops & (0 - stops)) - 1;  // lanes before the first stop
             take = (uint64_t)uniform64((int64_t)take);
-            while (take) {
-                const int l = __ffsll((long long)take) - 1;
-                take &= take - 1;
-                sum += *gptr(reinterpret_cast<const f32x4_t*>(fix + (int64_t)(gb + l) * 2 * tile_floats) + q0);
+            while (take) {  // eight partial tiles in flight at a time, added in workgroup order
+                int ls[8];
+                f32x4_t pv[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    ls[j] = take ? __ffsll((long long)take) - 1 : -1;
+                    take &= take - 1;
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    pv[j] = *gptr(reinterpret_cast<const f32x4_t*>(fix + (int64_t)(gb + max(ls[j], 0)) * 2 * tile_floats) +
+                                  q0);
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if (ls[j] >= 0) sum += pv[j];
             }
             if (stops) break;
         }

@@ -34,10 +34,10 @@ __device__ __forceinline__ int rotated(int kc0, int n, int rot, int i) {
 //
 // Work split ("stream-K"): the work is the list of (tile, 32-row window)
 // units, ordered by active adapter, rank group, column block, window; the
-// grid's workgroups (one per CU) take equal contiguous ranges of it, so no
-// CU waits on another's second tile.  Inside a workgroup the waves (eight
-// for bf16, four for fp32) split the windows of each tile they meet into
-// contiguous ranges.  Each wave runs two interleaved streams of windows:
+// contraction's workgroups (one per CU, four waves each, in the backward's
+// x-side launch beside the dX expand) take equal contiguous ranges of it, so
+// no CU waits on another's second tile.  Inside a workgroup the waves split
+// the windows of each tile they meet into contiguous ranges.  Each wave runs two interleaved streams of windows:
 // while one window is multiplied, the next window of the other stream is in
 // flight, and the row indices (perm) of each stream are fetched one window
 // ahead of its data.  The waves' partial tiles are summed in wave order
@@ -46,8 +46,6 @@ __device__ __forceinline__ int rotated(int kc0, int n, int rot, int i) {
 // per workgroup, and contract_fixup_kernel adds those in workgroup order.
 // Every sum therefore runs in an order fixed by the shapes alone.
 
-template <int DT>
-__host__ __device__ constexpr int contract_waves() { return DT == LORA_BF16 ? 8 : 4; }
 constexpr int kContractMB = 1;    // 16-rank blocks per task
 constexpr int kCtPitch = 32 + 8;  // fp32 path: LDS pitch (elements) of a transposed column
 constexpr int kQPitch = 64 + 8;   // bf16 path: LDS pitch (elements) of a staged row
@@ -79,7 +77,6 @@ struct ContractParams {
     const int32_t* stop;
 };
 
-constexpr int kContractGrid = 256;  // one workgroup per CU
 constexpr int kFixFloats = kContractMB * 4 * kWave * 4;
 constexpr int kFixMeta = 8;
 
@@ -116,13 +113,13 @@ __device__ __forceinline__ ContractAct contract_act_uniform(const ContractParams
 }
 
 
-template <int DT>
+template <int DT, int NW>
 struct ContractLds {
     static constexpr int EB = Frag<DT>::kBytes;
     // per wave: two window tiles
     static constexpr int kTileBytes = DT == LORA_BF16 ? 32 * kQPitch * 2 : 64 * kCtPitch * 4;
-    static constexpr int kTransBytes = contract_waves<DT>() * 2 * kTileBytes;
-    static constexpr int kRedBytes = contract_waves<DT>() * kContractMB * 4 * kWave * 16;
+    static constexpr int kTransBytes = NW * 2 * kTileBytes;
+    static constexpr int kRedBytes = NW * kContractMB * 4 * kWave * 16;
     static constexpr int kBytes = kTransBytes > kRedBytes ? kTransBytes : kRedBytes;
 };
 
@@ -220,13 +217,16 @@ __device__ __forceinline__ void contract_compute(const ContractWin<DT>& W, char*
 // NT: nontemporal loads of the x / dY windows.  The two-pass backward (dA and
 // dB tiles) takes it: those streams then leave the g / v windows and the other
 // tiles' rows in L2 (4096 fine-tuning rows, 5120 -> 5120: backward 65.5
-// against 67.6 us); the dA-only contraction after the streaming pass is
-// faster with ordinary loads (52.0 against 53.7 us).
-template <int DT, bool NT>
-__global__ __launch_bounds__(contract_waves<DT>() * kWave) __attribute__((amdgpu_waves_per_eu(DT == LORA_BF16 ? 2 : 1)))
-void contract_kernel(ContractParams p) {
-    constexpr int NW = contract_waves<DT>();
-    __shared__ __attribute__((aligned(16))) char s_mem[ContractLds<DT>::kBytes];
+// against 67.6 us, measured with the contraction in a launch of its own);
+// the dA-only contraction after the streaming pass is faster with ordinary
+// loads (52.0 against 53.7 us).
+//
+// Body of workgroup blk of the G workgroups (NW waves each, G a multiple of
+// the 8 XCDs, workgroup blk placed at a launch index congruent to blk modulo
+// 8) that share the contraction; s_mem holds ContractLds<DT, NW>::kBytes.
+template <int DT, bool NT, int NW>
+__device__ __forceinline__ void contract_body(const ContractParams& p, int blk, int G, char* s_mem) {
+    static_assert(NW >= 4, "waves 0..3 finish the four 16-column blocks of a tile");
     if (p.stop && *p.stop) return;
 
     const int wave = wave_id();
@@ -236,8 +236,7 @@ void contract_kernel(ContractParams p) {
     const int ncb = p.ncb_in + p.ncb_out;
     const int n_act = p.sched[2];
     // Workgroups of one XCD take neighbouring ranges (workgroup b runs on XCD b % 8).
-    const int G = gridDim.x;
-    const int vg = (int)(blockIdx.x % kNumXcd) * (G / kNumXcd) + (int)(blockIdx.x / kNumXcd);
+    const int vg = (blk % kNumXcd) * (G / kNumXcd) + blk / kNumXcd;
     int32_t* meta = p.fix_meta + (int64_t)vg * 2 * kFixMeta;
     if (threadIdx.x == 0) {
         meta[0] = -1;
@@ -251,7 +250,7 @@ void contract_kernel(ContractParams p) {
         ContractAct c{};
         if (i < n_act) c = contract_act(p, i, ncb);
         U += uniform64(wave_sum64(c.units));
-        if (blockIdx.x == 0 && wave == 0 && i < n_act && c.rgroups == 0) atomicAdd(p.err, 1);
+        if (blk == 0 && wave == 0 && i < n_act && c.rgroups == 0) atomicAdd(p.err, 1);
     }
     const int64_t begin = U * vg / G;
     const int64_t end = U * (vg + 1) / G;
@@ -281,8 +280,8 @@ void contract_kernel(ContractParams p) {
         abase += uniform64(__shfl(incl, kWave - 1, kWave));
     }
 
-    char* tileA = s_mem + (2 * wave) * ContractLds<DT>::kTileBytes;
-    char* tileB = s_mem + (2 * wave + 1) * ContractLds<DT>::kTileBytes;
+    char* tileA = s_mem + (2 * wave) * ContractLds<DT, NW>::kTileBytes;
+    char* tileB = s_mem + (2 * wave + 1) * ContractLds<DT, NW>::kTileBytes;
     // Loader role: lane covers window rows 4*(lane/8)+j (j < 4), columns 8*(lane%8)+e (e < 8).
     const int lrow = 4 * (lane >> 3);
     const int lcol = 8 * (lane & 7);
@@ -440,22 +439,30 @@ __device__ __forceinline__ void contract_fixup_body(const ContractParams& p, int
         if (m[0] < 0 || !m[5]) continue;
         const int32_t id0 = m[0], id1 = m[1];
         const int a = m[2], rg = m[3], cb_all = m[4];
+        // Requested together: the adapter's entries, this workgroup's partial
+        // tile and the records of the 64 workgroups after g0 (lane j reads
+        // workgroup g0 + 1 + j's first slot).
+        const lora_adapter ad = load_adapter(p.adapters, a);
+        const lora_adapter_grad gr = load_grad(p.grads, a);
         f32x4_t sum[kContractMB];
 #pragma unroll
         for (int mb = 0; mb < kContractMB; ++mb)
             sum[mb] = *gptr(reinterpret_cast<const f32x4_t*>(p.fix + ((int64_t)g0 * 2 + sl) * kFixFloats) +
                             (mb * 4 + nb) * kWave + lane);
-        for (int g = g0 + 1; g < G; ++g) {
-            const int32_t* mg = p.fix_meta + (int64_t)g * 2 * kFixMeta;  // its first tile
-            if (mg[0] == -2) continue;  // no units
-            if (mg[0] != id0 || mg[1] != id1) break;
-#pragma unroll
-            for (int mb = 0; mb < kContractMB; ++mb)
-                sum[mb] += *gptr(reinterpret_cast<const f32x4_t*>(p.fix + (int64_t)g * 2 * kFixFloats) +
-                                 (mb * 4 + nb) * kWave + lane);
-        }
-        const lora_adapter ad = load_adapter(p.adapters, a);
-        const lora_adapter_grad gr = load_grad(p.grads, a);
+        auto records = [&](int g, int32_t& m0, int32_t& m1) {
+            const int gj = g + lane;
+            m0 = -3;
+            m1 = 0;
+            if (gj < G) {
+                const int32_t* mg = p.fix_meta + (int64_t)gj * 2 * kFixMeta;
+                m0 = mg[0];
+                m1 = mg[1];
+            }
+        };
+        int32_t m0, m1;
+        records(g0 + 1, m0, m1);
+        // The dA / dB entries' old values, requested before the followers'
+        // partial tiles (addresses clamped, stores masked).
         const bool is_dA = cb_all < p.ncb_in;
         const int r = ad.rank;
         const int rank0 = rg * 16 * kContractMB;
@@ -463,8 +470,6 @@ __device__ __forceinline__ void contract_fixup_body(const ContractParams& p, int
         const int c0 = (is_dA ? cb_all : cb_all - p.ncb_in) * 64;
         const int N = is_dA ? p.d_in : p.d_out;
         const int col = c0 + 16 * nb + lr;
-        // read-modify-write of dA / dB: every load issued before any add
-        // (clamped addresses, unconditional), the stores masked
         float old[kContractMB][4];
         float* dst[kContractMB][4];
         bool ok[kContractMB][4];
@@ -478,6 +483,34 @@ __device__ __forceinline__ void contract_fixup_body(const ContractParams& p, int
                 dst[mb][i] = is_dA ? gr.dA + (int64_t)rk_ * p.d_in + col_ : gr.dB + (int64_t)col_ * r + rk_;
                 old[mb][i] = *gptr(dst[mb][i]);
             }
+        // The later workgroups holding the tile (their first slot) form a run
+        // after g0, workgroups without units skipped: a run of up to 64 costs
+        // one round trip for the records; the partial tiles are then loaded
+        // eight at a time and added in workgroup order.
+        for (int g = g0 + 1; g < G; g += kWave) {
+            if (g > g0 + 1) records(g, m0, m1);
+            const bool same = m0 == id0 && m1 == id1;
+            const uint64_t same_mask = __ballot(same);
+            const uint64_t end_mask = __ballot(!same && m0 != -2);  // another tile, or past the grid
+            const int n = end_mask ? __ffsll((long long)end_mask) - 1 : kWave;
+            for (int j0 = 0; j0 < n; j0 += 8) {
+                f32x4_t pv[8][kContractMB];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int gg = min(g + j0 + j, G - 1);
+#pragma unroll
+                    for (int mb = 0; mb < kContractMB; ++mb)
+                        pv[j][mb] = *gptr(reinterpret_cast<const f32x4_t*>(p.fix + (int64_t)gg * 2 * kFixFloats) +
+                                          (mb * 4 + nb) * kWave + lane);
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if (j0 + j < n && ((same_mask >> (j0 + j)) & 1))
+#pragma unroll
+                        for (int mb = 0; mb < kContractMB; ++mb) sum[mb] += pv[j][mb];
+            }
+            if (n < kWave) break;
+        }
 #pragma unroll
         for (int mb = 0; mb < kContractMB; ++mb)
 #pragma unroll

@@ -82,8 +82,17 @@ struct GatherElem<LORA_F32> {
 // The kernel's work as workgroup blk of nblk (nblk a multiple of 8, the
 // workgroup at launch index blk), so that another kernel can run it on part
 // of its grid.
+template <int KS>
+struct ExpandLds {
+    static constexpr int kFragBytes = (64 / 16) * KS * kWave * 2 * 16;   // s_frag: STEPS x KS x 64 x 2 quads
+    static constexpr int kTBytes = kExpandWaves * 16 * kTPitch * 4;      // s_t: per-wave transpose buffers
+    static constexpr int kRowBytes = 64 * 4;                             // s_row
+    static constexpr int kBytes = kFragBytes + kTBytes + kRowBytes;
+};
+
+// (s_lds: ExpandLds<KS>::kBytes of LDS, 16-byte aligned)
 template <int DT, bool TRANS_W, int KS>
-__device__ __forceinline__ void expand_body(const ExpandParams& p, int blk, int nblk) {
+__device__ __forceinline__ void expand_body(const ExpandParams& p, int blk, int nblk, char* s_lds) {
     using F = Frag<DT>;
     using E = Elem<DT>;
     using O = F32Operand<DT>;
@@ -95,9 +104,10 @@ __device__ __forceinline__ void expand_body(const ExpandParams& p, int blk, int 
     constexpr int NF = STEPS * KS * kWave / kThreads;  // V fragments converted per thread
     constexpr int kYBuf = DT == LORA_BF16 ? 4 : 2;     // y steps held in registers
     static_assert(sizeof(O) == 32, "fragment pair is two quads");
-    __shared__ u32x4_t s_frag[STEPS * KS * kWave * 2];
-    __shared__ __attribute__((aligned(16))) float s_t[kExpandWaves][16 * kTPitch];
-    __shared__ int32_t s_row[ROWS];
+    static_assert(ExpandLds<KS>::kFragBytes == STEPS * KS * kWave * 2 * 16, "LDS layout");
+    u32x4_t* s_frag = reinterpret_cast<u32x4_t*>(s_lds);
+    float(*s_t)[16 * kTPitch] = reinterpret_cast<float(*)[16 * kTPitch]>(s_lds + ExpandLds<KS>::kFragBytes);
+    int32_t* s_row = reinterpret_cast<int32_t*>(s_lds + ExpandLds<KS>::kFragBytes + ExpandLds<KS>::kTBytes);
 
     const int wave = wave_id();
     const int lane = threadIdx.x & (kWave - 1);
@@ -295,7 +305,8 @@ __device__ __forceinline__ void expand_body(const ExpandParams& p, int blk, int 
 template <int DT, bool TRANS_W, int KS>
 __global__ __launch_bounds__(kExpandWaves * kWave) __attribute__((amdgpu_waves_per_eu(KS == 4 ? 2 : 3)))
 void expand_kernel(ExpandParams p) {
-    expand_body<DT, TRANS_W, KS>(p, blockIdx.x, gridDim.x);
+    __shared__ __attribute__((aligned(16))) char s_lds[ExpandLds<KS>::kBytes];
+    expand_body<DT, TRANS_W, KS>(p, blockIdx.x, gridDim.x, s_lds);
 }
 
 }  // namespace lora
