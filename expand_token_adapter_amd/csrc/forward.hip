@@ -303,16 +303,12 @@ int expand_plan(const ExpandParams& p, int32_t T, int32_t num_adapters, int32_t 
     return r_max <= 32 ? 1 : (r_max <= 64 ? 2 : 4);
 }
 
-int run_expand(int dtype, bool trans_w, const ExpandParams& p, int32_t T, int32_t num_adapters, int32_t r_max,
-               hipStream_t st) {
+int run_expand(int dtype, const ExpandParams& p, int32_t T, int32_t num_adapters, int32_t r_max, hipStream_t st) {
     ExpandParams q;
     unsigned grid;
     const int ks = expand_plan(p, T, num_adapters, r_max, &q, &grid);
-    if (dtype == LORA_BF16)
-        return trans_w ? launch_expand_t<LORA_BF16, true>(ks, q, grid, st)
-                       : launch_expand_t<LORA_BF16, false>(ks, q, grid, st);
-    return trans_w ? launch_expand_t<LORA_F32, true>(ks, q, grid, st)
-                   : launch_expand_t<LORA_F32, false>(ks, q, grid, st);
+    return dtype == LORA_BF16 ? launch_expand_t<LORA_BF16, false>(ks, q, grid, st)
+                              : launch_expand_t<LORA_F32, false>(ks, q, grid, st);
 }
 
 }  // namespace lora
@@ -418,6 +414,6 @@ extern "C" int lora_expand_add(int dtype, const float* v, int64_t ldv, int32_t T
     if (use_decode_path(dtype, T, num_adapters) && dec_offsets_fit((int64_t)T * ldy * 2, d_out, r_max))
         return run_dec_expand(dtype, v, ldv, 0, T, d_out, adapters, num_adapters, r_max, seg, y, ldy,
                               static_cast<hipStream_t>(stream));
-    return run_expand(dtype, false, p, T, num_adapters, r_max, static_cast<hipStream_t>(stream));
+    return run_expand(dtype, p, T, num_adapters, r_max, static_cast<hipStream_t>(stream));
 }
 
