@@ -11,8 +11,9 @@
 // It cuts dY into (adapter, 256-column slice, 32-row window) units and gives
 // the grid's workgroups (one per CU) equal contiguous ranges of them
 // (stream-K), so a workgroup holds a run of windows of one or two (adapter,
-// slice) pairs.  A pair's B_a block stays in registers and its dB tile (256
-// columns x 16 ranks) accumulates in registers over the workgroup's windows:
+// slice) pairs.  A pair's B_a block is loaded once per workgroup into LDS
+// and each wave keeps it in registers as its MFMA operand; the pair's dB tile
+// (256 columns x 16 ranks) accumulates in registers over the workgroup's windows:
 // a pair whose windows all fall in one workgroup is added to dB there, a pair
 // cut by workgroup boundaries leaves one partial tile per workgroup, added in
 // workgroup order by the fix-up (dy_fixup_body).  Every sum runs in an order
@@ -45,7 +46,9 @@ constexpr int kStSmallBytes = 2048;   // a window's rank-16 fp32 rows
 constexpr int kStRingBytes = 4 * 256; // row indices of four windows
 constexpr int kStFixMeta = 8;
 constexpr int kStFixChunk = 1024;     // floats per fix-up workgroup
-static_assert(kStWaves * (2 * (kStTileBytes + kStSmallBytes) + kStRingBytes) <= 160 * 1024, "fits the LDS of a CU");
+constexpr int kStBBytes = 256 * 16 * 2;  // a pair's B_a block
+static_assert(kStWaves * (2 * (kStTileBytes + kStSmallBytes) + kStRingBytes) + kStBBytes <= 160 * 1024,
+              "fits the LDS of a CU");
 
 constexpr int kDyCols = 256;                  // d_out columns per slice
 constexpr int kDyFixFloats = kDyCols * 16;    // a cut pair's partial dB tile
@@ -256,6 +259,7 @@ struct StLds {
     char* tile;   // [2][kStWaves] window tiles
     char* small;  // [2][kStWaves] small tiles
     char* ring;   // [kStWaves]
+    uint16_t* bblk;  // the pair's B_a block, [kDyCols columns][16 ranks] bf16 (workgroup-wide)
 };
 __device__ __forceinline__ char* st_tile(const StLds& l, int b, int wave) {
     return l.tile + (b * kStWaves + wave) * kStTileBytes;
@@ -310,32 +314,10 @@ __device__ __forceinline__ void dy_pair(const DyParams& p, const StAct& c, int c
     constexpr int KS = kDyCols / 32;  // 32-column steps of g (8)
     const int lr = lane & 15;
     const int lg = lane >> 4;
-    const lora_adapter ad = load_adapter(p.walk.adapters, c.a);
-    const lora_adapter_grad gr = load_grad(p.grads, c.a);
-    const int r = ad.rank;
     const int c0 = cs * kDyCols;
     const int lo = c.lo, hi = c.hi;
     const int wbase = lo & ~31;
 
-    // g's B operand, held for the pair: rank lr, columns c0 + 32 ks + 8 lg + 0..7
-    // of B_a ([d_out][r], row-major); ranks past r and columns past d_out are zero
-    // (unconditional buffer loads: outside B_a they read zeros, so no load
-    // waits behind a branch).
-    F bf[KS];
-    {
-        const buf_rsrc_t brs = make_rsrc(ad.B, (uint32_t)((int64_t)p.d_out * r * 2));
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            uint32_t h[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int col = c0 + 32 * ks + 8 * lg + i;
-                const bool ok = lr < r && col < p.d_out;
-                h[i] = __builtin_amdgcn_raw_buffer_load_b16(brs, ok ? (uint32_t)((col * r + lr) * 2) : kBufOff, 0, 0);
-            }
-            bf[ks].q = u32x4_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-        }
-    }
     f32x4_t accB[CT];
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) accB[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -388,13 +370,50 @@ __device__ __forceinline__ void dy_pair(const DyParams& p, const StAct& c, int c
             dma_lds(vr, ok ? vrow * ldv4 + 16u * vu : kBufOff, 0u, small + j * 1024, 16);
         }
     };
+    // The first windows' row indices go out before anything that needs the
+    // adapter's entry; then the B_a block (16 two-byte loads per thread for
+    // the whole workgroup) and the first two windows' data are in flight
+    // together.  (With the block gathered by every wave in operand layout,
+    // 64 loads per lane behind the entry and ahead of the row indices, a
+    // pair took 5.5 us from its start to its first window's data.)
     issue_perm(0);
     issue_perm(1);
     issue_perm(2);
-    wait_vmcnt_le<2>();
+    const lora_adapter ad = load_adapter(p.walk.adapters, c.a);
+    const lora_adapter_grad gr = load_grad(p.grads, c.a);
+    const int r = ad.rank;
+    uint32_t hb[kStBBytes / 2 / (kStWaves * kWave)];
+    {
+        const buf_rsrc_t brs = make_rsrc(ad.B, (uint32_t)((int64_t)p.d_out * r * 2));
+        // element e = column e / 16, rank e % 16 of the block; ranks past r and
+        // columns past d_out read zeros (offset past the buffer, no fetch)
+#pragma unroll
+        for (int j = 0; j < kStBBytes / 2 / (kStWaves * kWave); ++j) {
+            const int e = (int)threadIdx.x + kStWaves * kWave * j;
+            const int col = c0 + (e >> 4), rk = e & 15;
+            const bool ok = rk < r && col < p.d_out;
+            hb[j] = __builtin_amdgcn_raw_buffer_load_b16(brs, ok ? (uint32_t)((col * r + rk) * 2) : kBufOff, 0, 0);
+        }
+    }
+    constexpr int kB = kStBBytes / 2 / (kStWaves * kWave);  // B loads issued after the row indices
+    wait_vmcnt_le<2 + kB>();                                  // perm(0)
     issue(0, 0, read_perm(0));
-    wait_vmcnt_le<19>();
+    wait_vmcnt_le<1 + kB + 18>();                             // perm(1)
     issue(1, 1, read_perm(1));
+    // The block to LDS (the compiler waits for its loads, and with them for
+    // the windows' loads issued before them), then every wave's B operand:
+    // rank lr, columns c0 + 32 ks + 8 lg + 0..7, read transposed.
+#pragma unroll
+    for (int j = 0; j < kB; ++j) L.bblk[threadIdx.x + kStWaves * kWave * j] = (uint16_t)hb[j];
+    __syncthreads();
+    F bf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const uint16_t* base = L.bblk + (32 * ks + 8 * lg + (lr >> 2)) * 16 + 4 * (lane & 3);
+        const uint2 x0 = lds_read_tr16(base);
+        const uint2 x1 = lds_read_tr16(base + 4 * 16);
+        bf[ks].q = u32x4_t{x0.x, x0.y, x1.x, x1.y};
+    }
 
     // per-lane LDS offsets of the operand reads
     const int e = lr >> 2;
@@ -515,7 +534,8 @@ __device__ __forceinline__ int st_place() {
     __shared__ __attribute__((aligned(16))) char s_t[2 * kStWaves * kStTileBytes];    \
     __shared__ __attribute__((aligned(16))) char s_s[2 * kStWaves * kStSmallBytes];   \
     __shared__ __attribute__((aligned(16))) char s_r[kStWaves * kStRingBytes];        \
-    const StLds L{s_t, s_s, s_r};
+    __shared__ __attribute__((aligned(16))) uint16_t s_b[kStBBytes / 2];              \
+    const StLds L{s_t, s_s, s_r, s_b};
 
 __global__ __launch_bounds__(kStWaves * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void dy_pass_kernel(DyParams p) {
