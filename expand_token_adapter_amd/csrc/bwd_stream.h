@@ -37,6 +37,16 @@
 namespace lora {
 
 constexpr int kStWaves = 4;
+// Units a pair costs before its first window in the stream-K split: starting
+// a pair (its B_a block, row indices and first windows) takes a workgroup
+// about as long as a few windows do, so a workgroup whose range crosses into
+// a second pair gets that many windows fewer.  Mixed batch (2048 rows, 56
+// slices of 64 windows): backward 48.8 / 48.5 / 47.6 / 46.7 / 46.7 / 48.2 us
+// with 0 / 2 / 4 / 6 / 8 / 10 set-up units (14 and 20: 48.2 us).
+#ifndef LORA_ST_SETUP
+#define LORA_ST_SETUP 6
+#endif
+constexpr int kStSetupUnits = LORA_ST_SETUP;
 constexpr int kStGrid = 256;          // one workgroup per CU
 constexpr int kStMaxRank = 16;
 constexpr int kStChunk = 1056;        // one load's 1 KB (8 rows x 128 bytes) plus 32 bytes of bank offset
@@ -111,7 +121,7 @@ __device__ __forceinline__ StAct st_act(const StWalk& w, int i) {
     c.lo = w.offsets[c.a];
     c.hi = w.offsets[c.a + 1];
     c.nwin = (c.hi - (c.lo & ~31) + 31) / 32;
-    c.units = adapter_ok(ad, w.r_max) ? (int64_t)w.nslices * c.nwin : 0;
+    c.units = adapter_ok(ad, w.r_max) ? (int64_t)w.nslices * (c.nwin + kStSetupUnits) : 0;
     return c;
 }
 
@@ -212,13 +222,18 @@ __device__ __forceinline__ void walk_pairs(const StWalk& w, int vg, int G, PairF
             c = act_at(++act);
             continue;
         }
+        // a pair is kStSetupUnits set-up units, then its windows
         const int64_t local = u - abase;
-        const int cs = (int)(local / c.nwin);
-        const int w0 = (int)(local - (int64_t)cs * c.nwin);
-        const int w1 = (int)min((int64_t)c.nwin, w0 + (end - u));
-        pair(c, cs, w0, w1, slot, abase + (int64_t)cs * c.nwin);
-        slot = 1;
-        u += w1 - w0;
+        const int per = c.nwin + kStSetupUnits;
+        const int cs = (int)(local / per);
+        const int v0 = (int)(local - (int64_t)cs * per);
+        const int v1 = (int)min((int64_t)per, v0 + (end - u));
+        const int w0 = max(v0 - kStSetupUnits, 0), w1 = max(v1 - kStSetupUnits, 0);
+        if (w1 > w0) {  // (a range that ends inside a pair's set-up units leaves it to the next workgroup)
+            pair(c, cs, w0, w1, slot, abase + (int64_t)cs * per);
+            slot = 1;
+        }
+        u += v1 - v0;
     }
 }
 
