@@ -74,12 +74,22 @@ struct DecShrinkParams {
 // Balanced mode (many tasks): workgroup w of G (numbered XCD by XCD) takes the
 // tasks whose start falls in [w C / G, (w + 1) C / G) of the total cost C, in
 // task order; a task (tile t, rank block b) costs its A rows plus its x rows,
-// min(16, r - 16 b) + rows(t) rows of d_in elements.  Wave 0 builds the
+// min(16, r - 16 b) + rows(t) rows of d_in elements, plus a fixed
+// kShrTaskCost rows.  Wave 0 builds the
 // tiles' cost prefix in LDS as the expand's plan does; each XCD then holds
 // one contiguous eighth of the work, so the tiles of an adapter share A_a
 // through one L2 and the rank blocks of a tile share its x rows.  Direct
 // mode (few tasks): workgroups take tasks by index, XCD by XCD.
 constexpr int kShrPlanMaxTiles = 2048;  // tiles per call in balanced mode (LDS prefix)
+// A task's time is set mostly by its chain of sequential 512-element groups,
+// whatever its live rows, so the plan prices each task at a fixed 512 rows
+// plus its rows: the ranges then hold nearly equal task counts (zipf-320
+// decode batch, forward per call: 135.3 / 133.2 / 130.6 / 128.9 / 129.0 us
+// with a fixed cost of 0 / 32 / 256 / 512 / 1024 rows).
+#ifndef LORA_SHR_TASK_COST
+#define LORA_SHR_TASK_COST 512
+#endif
+constexpr uint32_t kShrTaskCost = LORA_SHR_TASK_COST;  // fixed cost of a task, in rows
 #ifndef LORA_SHR_DEPTH
 #define LORA_SHR_DEPTH 2
 #endif
@@ -132,7 +142,7 @@ __device__ __forceinline__ int4 dec_shrink_plan(const DecShrinkParams& p, int n1
             const bool ok = t < n16 && adapter_ok(ad, p.r_max);
             if (t < n16 && !ok && blockIdx.x == 0) atomicAdd(p.err, 1);
             const uint32_t nrb = ok ? (uint32_t)(ad.rank + 15) / 16 : 0u;
-            const uint32_t c = ok ? (uint32_t)ad.rank + nrb * (uint32_t)rec[i].rows : 0u;
+            const uint32_t c = ok ? (uint32_t)ad.rank + nrb * ((uint32_t)rec[i].rows + kShrTaskCost) : 0u;
             uint32_t incl = c;
 #pragma unroll
             for (int d = 1; d < kWave; d <<= 1) {
@@ -167,7 +177,7 @@ __device__ __forceinline__ int4 dec_shrink_plan(const DecShrinkParams& p, int n1
         }
         const uint64_t st = l > 0 ? s_pre[l - 1] : 0;
         const uint32_t inf = s_inf[l];
-        const uint64_t q = 16 + (inf & 255u);
+        const uint64_t q = 16 + (inf & 255u) + kShrTaskCost;
         const uint64_t b = (x - st + q - 1) / q;
         tt = b < (inf >> 8) ? l : l + 1;
         bb = b < (inf >> 8) ? (int)b : 0;
